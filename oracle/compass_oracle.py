@@ -1,0 +1,353 @@
+"""Plain fp64 CPU oracle for the Compass/Cohere2 parallel decoder layer.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or run
+this module: only the tests, the smoke check and the bench's CPU-baseline leg
+use it. It shares no code with the HIP library.
+
+Every function is the plain definition written out in float64 (integers for
+position ids), following the mlxcel issue "feat(vlm): add Cohere Compass /
+North-Micro-Vision (cohere_compass) VLM" (page 1), section "Text decoder
+forward" and its "Interleaved MRoPE" and "Position ids" paragraphs, plus the
+"Validation" list of the same page. Library primitives used as steps: numpy
+matmul, exp, sqrt, cos, sin. No tiling, fusion or reordering beyond what the
+definitions state; rows of a softmax are independent by definition and may be
+processed in any grouping.
+
+Readings taken where the page is silent (each one is listed with its reason in
+the design notes of the repository):
+  * LayerNorm: mean-centred, biased variance, weight only, eps passed in.
+  * MRoPE axis rule for sections other than [24, 20, 20]: axis h when
+    j % 3 == 1 and j < 3*s_h, axis w when j % 3 == 2 and j < 3*s_w, else t.
+  * Sliding window of W keys including the query: key j visible to query i
+    iff i - W < j <= i.
+  * GQA: query head h reads key/value head h // (Hq / Hkv).
+  * Deepstack rows are added after the layer's residual sum.
+  * Decode: the new token's key/value sit at cache index n = lens[b]; it sees
+    keys n - W < j <= n (sliding) or j <= n (full).
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional, Sequence, Tuple
+
+import numpy as np
+
+F64 = np.float64
+
+# Status codes of the position-id construction (shared meaning with the C ABI,
+# defined independently there).
+POS_OK = 0
+POS_SPAN_MISMATCH = 1      # an image's pad span runs past L or hits a non-pad token
+POS_EXTRA_PADS = 2         # pad tokens left over with no image to consume them
+POS_UNUSED_IMAGES = 3      # images left over after the row's last pad span
+POS_BAD_GRID = 4           # grid entry non-positive or h/w not divisible by the merge size
+
+
+class PositionError(ValueError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(msg)
+        self.code = code
+
+
+# ----------------------------------------------------------------------------------------
+# Position ids. Page 1, "Position ids (get_rope_index)": text tokens advance t/h/w by one;
+# the t*(h/2)*(w/2) pads of an image take (t_idx, h_idx, w_idx) on the merged grid plus the
+# running text offset; the next text token starts at max(previous positions) + 1;
+# rope_delta = max_position + 1 - L.
+# ----------------------------------------------------------------------------------------
+def mrope_positions(tokens: np.ndarray, image_token_id: int, grid_thw: np.ndarray,
+                    img_offset: np.ndarray, spatial_merge: int) -> Tuple[np.ndarray, np.ndarray]:
+    """tokens [B, L] int; grid_thw [n_img, 3] (patch units); img_offset [B+1].
+
+    Returns pos [3, B, L] int64 and rope_delta [B] int64. Raises PositionError.
+    """
+    tokens = np.asarray(tokens)
+    B, L = tokens.shape
+    pos = np.zeros((3, B, L), dtype=np.int64)
+    delta = np.zeros(B, dtype=np.int64)
+    m = int(spatial_merge)
+    for b in range(B):
+        st = 0                      # first position of the next text token
+        k = int(img_offset[b])      # next image of this row
+        k_end = int(img_offset[b + 1])
+        l = 0
+        while l < L:
+            if int(tokens[b, l]) != image_token_id:
+                pos[:, b, l] = st
+                st += 1
+                l += 1
+                continue
+            if k >= k_end:
+                raise PositionError(POS_EXTRA_PADS, f"row {b}: pad token at {l} but no image left")
+            t, h, w = (int(v) for v in grid_thw[k])
+            if t < 1 or h < 1 or w < 1 or h % m or w % m:
+                raise PositionError(POS_BAD_GRID, f"image {k}: bad grid {(t, h, w)} for merge {m}")
+            gh, gw = h // m, w // m
+            n = t * gh * gw
+            if l + n > L or np.any(tokens[b, l:l + n] != image_token_id):
+                raise PositionError(POS_SPAN_MISMATCH, f"row {b}: image {k} needs {n} pads at {l}")
+            for r in range(n):
+                pos[0, b, l + r] = st + r // (gh * gw)
+                pos[1, b, l + r] = st + (r // gw) % gh
+                pos[2, b, l + r] = st + r % gw
+            st += max(t, gh, gw)
+            k += 1
+            l += n
+        if k != k_end:
+            raise PositionError(POS_UNUSED_IMAGES, f"row {b}: {k_end - k} image(s) not consumed")
+        delta[b] = st - L           # == max position + 1 - L
+    return pos, delta
+
+
+def decode_positions(lens: np.ndarray, rope_delta: np.ndarray) -> np.ndarray:
+    """Page 1, "Position ids": each new token sits at offset + rope_delta on all three axes."""
+    p = np.asarray(lens, dtype=np.int64) + np.asarray(rope_delta, dtype=np.int64)
+    return np.stack([p, p, p])
+
+
+# ----------------------------------------------------------------------------------------
+# LayerNorm. Page 1, "Text decoder forward": weight only, no bias, computed in float.
+# ----------------------------------------------------------------------------------------
+def layer_norm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    x = np.asarray(x, dtype=F64)
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps) * np.asarray(w, dtype=F64)
+
+
+# ----------------------------------------------------------------------------------------
+# Interleaved MRoPE. Page 1, "Interleaved MRoPE (sliding layers)": inv_freq[j] =
+# base^(-2j/hd); axis t by default, h when j % 3 == 1 and j < 3*s_h, w when j % 3 == 2 and
+# j < 3*s_w; cos/sin of concat(freqs, freqs); q*cos + rotate_half(q)*sin with
+# rotate_half(x) = concat(-x2, x1).
+# ----------------------------------------------------------------------------------------
+def mrope_axis_map(section: Sequence[int], half: int) -> np.ndarray:
+    s_t, s_h, s_w = (int(s) for s in section)
+    if s_t + s_h + s_w != half:
+        raise ValueError(f"mrope section {tuple(section)} does not sum to {half}")
+    ax = np.zeros(half, dtype=np.int64)
+    for j in range(half):
+        if j % 3 == 1 and j < 3 * s_h:
+            ax[j] = 1
+        elif j % 3 == 2 and j < 3 * s_w:
+            ax[j] = 2
+    counts = (int((ax == 0).sum()), int((ax == 1).sum()), int((ax == 2).sum()))
+    if counts != (s_t, s_h, s_w):
+        raise ValueError(f"section {tuple(section)} is not realisable by the interleave (got {counts})")
+    return ax
+
+
+def inv_freq(theta: float, head_dim: int) -> np.ndarray:
+    j = np.arange(head_dim // 2, dtype=F64)
+    return float(theta) ** (-2.0 * j / head_dim)
+
+
+def mrope_angles(pos3: np.ndarray, section: Sequence[int], theta: float, head_dim: int) -> np.ndarray:
+    """pos3 [3, N] -> angles [N, hd/2]: freqs[n, j] = pos[axis(j), n] * inv_freq[j]."""
+    half = head_dim // 2
+    ax = mrope_axis_map(section, half)
+    f = inv_freq(theta, head_dim)
+    pos3 = np.asarray(pos3, dtype=F64)
+    return pos3[ax, :].T * f[None, :]
+
+
+def rotate_half(x: np.ndarray) -> np.ndarray:
+    half = x.shape[-1] // 2
+    return np.concatenate([-x[..., half:], x[..., :half]], axis=-1)
+
+
+def apply_rope(x: np.ndarray, angles: np.ndarray) -> np.ndarray:
+    """x [..., N, hd], angles [N, hd/2]: x*cos + rotate_half(x)*sin over concat(freqs, freqs)."""
+    full = np.concatenate([angles, angles], axis=-1)
+    return np.asarray(x, dtype=F64) * np.cos(full) + rotate_half(np.asarray(x, dtype=F64)) * np.sin(full)
+
+
+# ----------------------------------------------------------------------------------------
+# Attention. Page 1, "Text decoder forward": sdpa(q, k, v, scale = hd^-1/2) with a causal
+# mask, restricted to the last W keys on sliding layers; plain causal on full layers.
+# ----------------------------------------------------------------------------------------
+def visible(i: int, j: np.ndarray, kind: str, window: int) -> np.ndarray:
+    ok = j <= i
+    if kind == "sliding":
+        ok &= j > i - window
+    return ok
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, kind: str, window: int,
+              q_index: Optional[np.ndarray] = None, k_index: Optional[np.ndarray] = None) -> np.ndarray:
+    """q [Hq, Nq, hd]; k, v [Hkv, Nk, hd]. Returns o [Nq, Hq*hd].
+
+    q_index / k_index give the sequence index of each query / key (default arange).
+    """
+    Hq, Nq, hd = q.shape
+    Hkv, Nk, _ = k.shape
+    g = Hq // Hkv
+    qi = np.arange(Nq) if q_index is None else np.asarray(q_index)
+    kj = np.arange(Nk) if k_index is None else np.asarray(k_index)
+    mask = kj[None, :] <= qi[:, None]
+    if kind == "sliding":
+        mask &= kj[None, :] > qi[:, None] - window
+    out = np.empty((Nq, Hq * hd), dtype=F64)
+    scale = 1.0 / np.sqrt(hd)
+    for h in range(Hq):
+        kh = np.asarray(k[h // g], dtype=F64)
+        vh = np.asarray(v[h // g], dtype=F64)
+        s = (np.asarray(q[h], dtype=F64) @ kh.T) * scale
+        s = np.where(mask, s, -np.inf)
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p /= p.sum(axis=1, keepdims=True)
+        out[:, h * hd:(h + 1) * hd] = p @ vh
+    return out
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    return x / (1.0 + np.exp(-x))
+
+
+# ----------------------------------------------------------------------------------------
+# The parallel block. Page 1, "Text decoder forward": a = LN(h); h = h + Attn(a) + SwiGLU(a);
+# deepstack rows are added after layers 0..2. Weights are nn.Linear [out, in], no biases.
+# ----------------------------------------------------------------------------------------
+def projections(a: np.ndarray, w: Dict[str, np.ndarray]):
+    a = np.asarray(a, dtype=F64)
+    f = lambda name: np.asarray(w[name], dtype=F64)
+    return a @ f("wq").T, a @ f("wk").T, a @ f("wv").T, a @ f("w_gate").T, a @ f("w_up").T
+
+
+def _heads(x: np.ndarray, n_heads: int, hd: int) -> np.ndarray:
+    """[N, H*hd] -> [H, N, hd]"""
+    return x.reshape(x.shape[0], n_heads, hd).transpose(1, 0, 2)
+
+
+def layer_prefill(shape, w: Dict[str, np.ndarray], x: np.ndarray, pos: Optional[np.ndarray] = None,
+                  ds_rows: Optional[np.ndarray] = None, ds: Optional[np.ndarray] = None,
+                  return_stages: bool = False):
+    """x [B, L, D]; pos [3, B, L] (sliding layers). Returns out [B, L, D] (and stages)."""
+    x = np.asarray(x, dtype=F64)
+    B, L, D = x.shape
+    Hq, Hkv, hd = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
+    out = np.empty_like(x)
+    stages = {"q": [], "k": [], "v": [], "act": [], "attn": []}
+    for b in range(B):
+        a = layer_norm(x[b], w["ln_w"], shape.ln_eps)
+        q, k, v, g, u = projections(a, w)
+        qh, kh, vh = _heads(q, Hq, hd), _heads(k, Hkv, hd), _heads(v, Hkv, hd)
+        if shape.kind == "sliding":
+            ang = mrope_angles(pos[:, b, :], shape.mrope_section, shape.rope_theta, hd)
+            qh, kh = apply_rope(qh, ang), apply_rope(kh, ang)
+        o = attention(qh, kh, vh, shape.kind, shape.window)
+        act = silu(g) * u
+        attn_out = o @ np.asarray(w["wo"], dtype=F64).T
+        mlp_out = act @ np.asarray(w["w_down"], dtype=F64).T
+        out[b] = x[b] + attn_out + mlp_out
+        if return_stages:
+            stages["q"].append(qh); stages["k"].append(kh); stages["v"].append(vh)
+            stages["act"].append(act); stages["attn"].append(o)
+    if ds_rows is not None and ds is not None and len(ds_rows):
+        flat = out.reshape(B * L, D)
+        flat[np.asarray(ds_rows)] += np.asarray(ds, dtype=F64)
+    if return_stages:
+        return out, {k2: np.stack(v2) for k2, v2 in stages.items()}
+    return out
+
+
+def layer_prefill_rows(shape, w: Dict[str, np.ndarray], x: np.ndarray, pos: Optional[np.ndarray],
+                       b: int, rows: Sequence[int]) -> np.ndarray:
+    """Outputs of selected rows of batch row b, computed one by one from the definition.
+
+    Only the keys each selected query can see are projected. Returns [len(rows), D]
+    (no deepstack term).
+    """
+    x = np.asarray(x, dtype=F64)
+    Hq, Hkv, hd = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
+    rows = np.asarray(sorted(rows))
+    lo = 0 if shape.kind == "full" else max(0, int(rows.min()) - shape.window + 1)
+    hi = int(rows.max()) + 1
+    span = np.arange(lo, hi)
+    a_span = layer_norm(x[b, lo:hi], w["ln_w"], shape.ln_eps)
+    k = a_span @ np.asarray(w["wk"], dtype=F64).T
+    v = a_span @ np.asarray(w["wv"], dtype=F64).T
+    kh, vh = _heads(k, Hkv, hd), _heads(v, Hkv, hd)
+    a_rows = layer_norm(x[b, rows], w["ln_w"], shape.ln_eps)
+    q = a_rows @ np.asarray(w["wq"], dtype=F64).T
+    qh = _heads(q, Hq, hd)
+    if shape.kind == "sliding":
+        kh = apply_rope(kh, mrope_angles(pos[:, b, lo:hi], shape.mrope_section, shape.rope_theta, hd))
+        qh = apply_rope(qh, mrope_angles(pos[:, b, rows], shape.mrope_section, shape.rope_theta, hd))
+    o = attention(qh, kh, vh, shape.kind, shape.window, q_index=rows, k_index=span)
+    g = a_rows @ np.asarray(w["w_gate"], dtype=F64).T
+    u = a_rows @ np.asarray(w["w_up"], dtype=F64).T
+    act = silu(g) * u
+    return (x[b, rows] + o @ np.asarray(w["wo"], dtype=F64).T
+            + act @ np.asarray(w["w_down"], dtype=F64).T)
+
+
+# ----------------------------------------------------------------------------------------
+# Decode. Page 1, "Text decoder forward" and its correction under "Acceptance criteria"
+# (dense cache with the window applied as a mask): one new token per row, keys/values
+# appended at index lens[b] after rotation, position lens[b] + rope_delta[b].
+# ----------------------------------------------------------------------------------------
+def layer_decode(shape, w: Dict[str, np.ndarray], x: np.ndarray, pos: np.ndarray,
+                 k_cache: np.ndarray, v_cache: np.ndarray, lens: np.ndarray,
+                 rows: Optional[Sequence[int]] = None):
+    """x [B, D]; pos [3, B]; caches [B, Hkv, cap, hd] (read only here).
+
+    Returns (out [nb, D], k_new [nb, Hkv, hd], v_new [nb, Hkv, hd]) for the batch rows
+    `rows` (default all).
+    """
+    x = np.asarray(x, dtype=F64)
+    B, D = x.shape
+    Hq, Hkv, hd = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
+    rows = list(range(B)) if rows is None else list(rows)
+    outs, ks, vs = [], [], []
+    for b in rows:
+        n = int(lens[b])
+        a = layer_norm(x[b:b + 1], w["ln_w"], shape.ln_eps)
+        q, k, v, g, u = projections(a, w)
+        qh, kh, vh = _heads(q, Hq, hd), _heads(k, Hkv, hd), _heads(v, Hkv, hd)
+        if shape.kind == "sliding":
+            ang = mrope_angles(pos[:, b:b + 1], shape.mrope_section, shape.rope_theta, hd)
+            qh, kh = apply_rope(qh, ang), apply_rope(kh, ang)
+        lo = 0 if shape.kind == "full" else max(0, n - shape.window + 1)
+        kc = np.asarray(k_cache[b, :, lo:n, :], dtype=F64)
+        vc = np.asarray(v_cache[b, :, lo:n, :], dtype=F64)
+        kk = np.concatenate([kc, kh], axis=1)
+        vv = np.concatenate([vc, vh], axis=1)
+        o = attention(qh, kk, vv, shape.kind, shape.window, q_index=np.array([n]),
+                      k_index=np.arange(lo, n + 1))
+        act = silu(g) * u
+        out = x[b] + (o @ np.asarray(w["wo"], dtype=F64).T)[0] + (act @ np.asarray(w["w_down"], dtype=F64).T)[0]
+        outs.append(out); ks.append(kh[:, 0, :]); vs.append(vh[:, 0, :])
+    return np.stack(outs), np.stack(ks), np.stack(vs)
+
+
+# ----------------------------------------------------------------------------------------
+# Logits. Page 1, "Text decoder forward": h = LayerNorm(h); logits = embed.as_linear(h) *
+# logit_scale. Page 2 ("Cohere2 Command R"): the scale is an in-place fp32 multiply.
+# ----------------------------------------------------------------------------------------
+def logits(h: np.ndarray, norm_w: np.ndarray, eps: float, embed: np.ndarray, logit_scale: float,
+           rows: Optional[Sequence[int]] = None, cols: Optional[Sequence[int]] = None) -> np.ndarray:
+    h = np.asarray(h, dtype=F64)
+    if rows is not None:
+        h = h[np.asarray(rows)]
+    e = np.asarray(embed if cols is None else embed[np.asarray(cols)], dtype=F64)
+    return (layer_norm(h, norm_w, eps) @ e.T) * float(logit_scale)
+
+
+# ----------------------------------------------------------------------------------------
+# The stack. Page 1, "Text decoder forward" and "Validation": full attention at layers
+# i % 4 == 3, sliding elsewhere; deepstack added after layers 0, 1, 2 only.
+# ----------------------------------------------------------------------------------------
+def layer_kind(i: int) -> str:
+    return "full" if i % 4 == 3 else "sliding"
+
+
+def stack_prefill(shape, layer_weights: Sequence[Dict[str, np.ndarray]], x: np.ndarray,
+                  pos: np.ndarray, ds_rows: Optional[np.ndarray] = None,
+                  ds: Optional[Sequence[np.ndarray]] = None) -> np.ndarray:
+    h = np.asarray(x, dtype=F64)
+    for i, w in enumerate(layer_weights):
+        sh = shape.with_kind(layer_kind(i))
+        use_ds = ds is not None and i < 3 and i < len(ds)
+        h = layer_prefill(sh, w, h, pos, ds_rows if use_ds else None, ds[i] if use_ds else None)
+    return h

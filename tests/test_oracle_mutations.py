@@ -1,0 +1,138 @@
+"""Planted mistakes in the oracle must each fail at least one pin.
+
+Each mutant replaces one oracle function with a plausible wrong variant (a
+dropped term, a flipped sign, an off-by-one index, a transposed operand), then
+runs the pins that should catch it. CPU only; the oracle module is restored
+after every case by monkeypatch.
+"""
+import numpy as np
+import pytest
+
+from oracle import compass_oracle as O
+import tests.test_oracle_pins as P
+
+
+def _rotate_half_wrong_sign(x):
+    half = x.shape[-1] // 2
+    return np.concatenate([x[..., half:], -x[..., :half]], axis=-1)
+
+
+def _rotate_half_pairwise(x):
+    y = np.empty_like(x)
+    y[..., 0::2] = -x[..., 1::2]
+    y[..., 1::2] = x[..., 0::2]
+    return y
+
+
+def _axis_map_shifted(section, half):
+    s_t, s_h, s_w = section
+    ax = np.zeros(half, dtype=np.int64)
+    for j in range(half):
+        if j % 3 == 0 and j < 3 * s_h:
+            ax[j] = 1
+        elif j % 3 == 1 and j < 3 * s_w:
+            ax[j] = 2
+    return ax
+
+
+def _axis_map_contiguous(section, half):
+    s_t, s_h, s_w = section
+    return np.array([0] * s_t + [1] * s_h + [2] * s_w, dtype=np.int64)
+
+
+def _inv_freq_wrong_exponent(theta, hd):
+    j = np.arange(hd // 2, dtype=np.float64)
+    return float(theta) ** (-j / hd)
+
+
+def _layer_norm_rms(x, w, eps):
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt((x ** 2).mean(-1, keepdims=True) + eps) * w
+
+
+def _layer_norm_no_weight(x, w, eps):
+    x = np.asarray(x, dtype=np.float64)
+    mu = x.mean(-1, keepdims=True)
+    return (x - mu) / np.sqrt(((x - mu) ** 2).mean(-1, keepdims=True) + eps)
+
+
+_orig_attention = O.attention
+
+
+def _attention_window_off_by_one(q, k, v, kind, window, q_index=None, k_index=None):
+    return _orig_attention(q, k, v, kind, window + 1 if kind == "sliding" else window, q_index, k_index)
+
+
+def _attention_gqa_modulo(q, k, v, kind, window, q_index=None, k_index=None):
+    Hq, Hkv = q.shape[0], k.shape[0]
+    g = Hq // Hkv
+    kk = np.stack([k[h % Hkv] for h in range(Hq)])
+    vv = np.stack([v[h % Hkv] for h in range(Hq)])
+    if g == 1:
+        kk, vv = kk[::-1].copy(), vv[::-1].copy()
+    return _orig_attention(q, kk, vv, kind, window, q_index, k_index)
+
+
+def _attention_no_scale(q, k, v, kind, window, q_index=None, k_index=None):
+    return _orig_attention(q * np.sqrt(q.shape[-1]), k, v, kind, window, q_index, k_index)
+
+
+def _attention_not_causal(q, k, v, kind, window, q_index=None, k_index=None):
+    Nk = k.shape[1]
+    far = np.full(q.shape[1], 10 ** 9) if q_index is None else np.full(len(q_index), 10 ** 9)
+    if kind == "sliding":
+        return _orig_attention(q, k, v, kind, window, q_index, k_index)
+    return _orig_attention(q, k, v, kind, window, far, k_index)
+
+
+def _silu_sigmoid_only(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+MUTANTS = {
+    "rotate_half sign": ("rotate_half", _rotate_half_wrong_sign),
+    "pairwise rope": ("rotate_half", _rotate_half_pairwise),
+    "axis map shifted": ("mrope_axis_map", _axis_map_shifted),
+    "axis map contiguous": ("mrope_axis_map", _axis_map_contiguous),
+    "inv_freq exponent": ("inv_freq", _inv_freq_wrong_exponent),
+    "rmsnorm instead of layernorm": ("layer_norm", _layer_norm_rms),
+    "layernorm weight dropped": ("layer_norm", _layer_norm_no_weight),
+    "window off by one": ("attention", _attention_window_off_by_one),
+    "gqa head map": ("attention", _attention_gqa_modulo),
+    "attention scale dropped": ("attention", _attention_no_scale),
+    "full layer not causal": ("attention", _attention_not_causal),
+    "silu term dropped": ("silu", _silu_sigmoid_only),
+}
+
+PINS = [
+    P.test_split_rope_layout_page_example,
+    P.test_axis_sets_page_example,
+    lambda: P.test_mrope_equals_1d_rope_when_axes_agree(64, (12, 10, 10)),
+    P.test_single_axis_probe_rotates_only_that_axis,
+    P.test_layer_norm_vs_torch_and_invariants,
+    lambda: P.test_attention_vs_sdpa_and_brute_force("sliding", 3, 9),
+    lambda: P.test_attention_vs_sdpa_and_brute_force("full", 0, 9),
+    lambda: P.test_parallel_block_vs_library_routines("sliding", 3, 5),
+    lambda: P.test_parallel_block_vs_library_routines("full", 0, 5),
+    P.test_logits_vs_library_and_scale,
+]
+
+
+def _some_pin_fails():
+    for pin in PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError):
+            return True
+    return False
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(O, attr, fn)
+    assert _some_pin_fails(), f"no pin caught the planted mistake: {name}"
+
+
+def test_pins_pass_on_unmutated_oracle():
+    assert not _some_pin_fails()

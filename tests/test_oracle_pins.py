@@ -1,0 +1,447 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: values the
+mlxcel Compass issue (page 1) prints (fixtures under tests/golden/), library
+routines (torch.nn.functional layer_norm / linear / scaled_dot_product_attention
+/ silu in float64), textbook RoPE written as complex rotation (RoFormer), closed
+forms and invariants. CPU only.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import compass_oracle as O
+from synth.workloads import LayerShape
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def tiny_shape(kind="sliding", window=3, Hq=4, Hkv=2, hd=8, D=32, I=48, section=(2, 1, 1)):
+    return LayerShape(hidden=D, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=hd, intermediate=I, kind=kind,
+                      window=window, mrope_section=section, dtype="f32", rope_theta=50000.0, ln_eps=1e-5)
+
+
+def rand_weights(shape, seed=0, std=0.3):
+    r = np.random.default_rng(seed)
+    D, Hq, Hkv, hd, I = shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.intermediate
+    return {
+        "ln_w": 1.0 + 0.1 * r.standard_normal(D),
+        "wq": std * r.standard_normal((Hq * hd, D)), "wk": std * r.standard_normal((Hkv * hd, D)),
+        "wv": std * r.standard_normal((Hkv * hd, D)), "wo": std * r.standard_normal((D, Hq * hd)),
+        "w_gate": std * r.standard_normal((I, D)), "w_up": std * r.standard_normal((I, D)),
+        "w_down": std * r.standard_normal((D, I)),
+    }
+
+
+def text_pos(B, L, offset=0):
+    p = np.arange(L, dtype=np.int64)[None, :].repeat(B, 0) + offset
+    return np.stack([p, p, p])
+
+
+def mixed_pos(B, L, seed=1):
+    """Arbitrary distinct-ish (t, h, w) triples, as image rows produce."""
+    r = np.random.default_rng(seed)
+    return r.integers(0, 3 * L, size=(3, B, L))
+
+
+# ------------------------------------------------------------------------------ RoPE layout
+def test_split_rope_layout_page_example():
+    g = golden("split_rope_layout.json")
+    q = np.array(g["q"], dtype=np.float64)
+    # cos = 0 and sin = 1 for every frequency: angle pi/2.
+    ang = np.full((1, 2), math.pi / 2)
+    got = O.apply_rope(q[None, :], ang)[0]
+    np.testing.assert_allclose(got, g["expected_split"], atol=1e-12)
+    assert not np.allclose(got, g["rejected_pairwise"], atol=1e-3)
+
+
+def test_axis_sets_page_example():
+    g = golden("axis_sets_24_20_20.json")
+    ax = O.mrope_axis_map(g["section"], g["n_freq"])
+    h = set(range(g["h_first"], g["h_last"] + 1, g["h_step"]))
+    w = set(range(g["w_first"], g["w_last"] + 1, g["w_step"]))
+    assert set(np.nonzero(ax == 1)[0].tolist()) == h
+    assert set(np.nonzero(ax == 2)[0].tolist()) == w
+    assert set(np.nonzero(ax == 0)[0].tolist()) == set(range(64)) - h - w
+    assert all(ax[j] == 0 for j in g["t_tail"])
+
+
+def test_axis_map_other_sections():
+    ax = O.mrope_axis_map((12, 10, 10), 32)
+    assert "".join("THW"[a] for a in ax) == "THW" * 10 + "TT"
+    ax = O.mrope_axis_map((2, 1, 1), 4)
+    assert "".join("THW"[a] for a in ax) == "THWT"
+    with pytest.raises(ValueError):
+        O.mrope_axis_map((24, 20, 21), 64)
+    with pytest.raises(ValueError):
+        O.mrope_axis_map((4, 30, 30), 64)  # h/w counts not reachable by the interleave
+
+
+def textbook_rope(x, p, theta, hd):
+    """RoFormer rotary embedding, written as complex rotation of (x_j, x_{j+hd/2})."""
+    half = hd // 2
+    xt = torch.as_tensor(x, dtype=torch.float64)
+    z = torch.complex(xt[..., :half], xt[..., half:])
+    inv = 1.0 / (theta ** (torch.arange(0, hd, 2, dtype=torch.float64) / hd))
+    rot = torch.polar(torch.ones(half, dtype=torch.float64), torch.as_tensor(p, dtype=torch.float64)[..., None] * inv)
+    zr = z * rot
+    return torch.cat([zr.real, zr.imag], dim=-1).numpy()
+
+
+@pytest.mark.parametrize("hd,section", [(8, (2, 1, 1)), (64, (12, 10, 10)), (128, (24, 20, 20))])
+def test_mrope_equals_1d_rope_when_axes_agree(hd, section):
+    r = np.random.default_rng(3)
+    N = 37
+    x = r.standard_normal((N, hd))
+    p = r.integers(0, 9000, size=N)
+    got = O.apply_rope(x, O.mrope_angles(np.stack([p, p, p]), section, 50000.0, hd))
+    np.testing.assert_allclose(got, textbook_rope(x, p, 50000.0, hd), rtol=0, atol=1e-9)
+
+
+def test_single_axis_probe_rotates_only_that_axis():
+    hd, section = 128, (24, 20, 20)
+    ax = O.mrope_axis_map(section, hd // 2)
+    x = np.ones((1, hd))
+    for axis in range(3):
+        pos = np.zeros((3, 1), dtype=np.int64)
+        pos[axis, 0] = 777
+        y = O.apply_rope(x, O.mrope_angles(pos, section, 50000.0, hd))[0]
+        moved = {j for j in range(hd // 2) if abs(y[j] - 1.0) > 1e-12 or abs(y[j + 64] - 1.0) > 1e-12}
+        assert moved == set(np.nonzero(ax == axis)[0].tolist())
+
+
+def test_relative_position_property():
+    hd, section = 64, (12, 10, 10)
+    r = np.random.default_rng(4)
+    q, k = r.standard_normal((1, hd)), r.standard_normal((1, hd))
+    pq, pk = r.integers(0, 500, size=(3, 1)), r.integers(0, 500, size=(3, 1))
+    def dot(c):
+        a = O.apply_rope(q, O.mrope_angles(pq + c, section, 50000.0, hd))
+        b = O.apply_rope(k, O.mrope_angles(pk + c, section, 50000.0, hd))
+        return float((a * b).sum())
+    assert abs(dot(0) - dot(1234)) < 1e-9
+
+
+# ------------------------------------------------------------------------------ LayerNorm
+def test_layer_norm_vs_torch_and_invariants():
+    r = np.random.default_rng(5)
+    x = r.standard_normal((7, 96)) * 3 + 1
+    w = 1 + 0.1 * r.standard_normal(96)
+    ref = F.layer_norm(torch.tensor(x), (96,), weight=torch.tensor(w), bias=None, eps=1e-5).numpy()
+    got = O.layer_norm(x, w, 1e-5)
+    np.testing.assert_allclose(got, ref, atol=1e-12)
+    np.testing.assert_allclose(O.layer_norm(x + 5.0, w, 0.0), O.layer_norm(x, w, 0.0), atol=1e-10)
+    np.testing.assert_allclose(O.layer_norm(3.0 * x, w, 0.0), O.layer_norm(x, w, 0.0), atol=1e-10)
+    n = O.layer_norm(x, np.ones(96), 0.0)
+    np.testing.assert_allclose(n.mean(-1), 0, atol=1e-12)
+    np.testing.assert_allclose(n.var(-1), 1, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------ attention
+def torch_attention(q, k, v, kind, window):
+    """scaled_dot_product_attention with an explicit boolean mask; GQA by repeat_interleave."""
+    Hq, L, hd = q.shape
+    g = Hq // k.shape[0]
+    kk = torch.tensor(k).repeat_interleave(g, 0)
+    vv = torch.tensor(v).repeat_interleave(g, 0)
+    i = torch.arange(L)[:, None]
+    j = torch.arange(L)[None, :]
+    mask = j <= i
+    if kind == "sliding":
+        mask &= j > i - window
+    o = F.scaled_dot_product_attention(torch.tensor(q)[None], kk[None], vv[None], attn_mask=mask[None, None])
+    return o[0].transpose(0, 1).reshape(L, Hq * hd).numpy()
+
+
+def brute_attention(q, k, v, kind, window):
+    """Pure-Python loops: explicit scores, -inf mask, textbook softmax."""
+    Hq, L, hd = q.shape
+    g = Hq // k.shape[0]
+    out = np.zeros((L, Hq * hd))
+    for h in range(Hq):
+        for i in range(L):
+            s = []
+            for j in range(L):
+                vis = j <= i and (kind == "full" or j > i - window)
+                s.append(sum(q[h, i, d] * k[h // g, j, d] for d in range(hd)) / math.sqrt(hd) if vis else -math.inf)
+            m = max(s)
+            e = [math.exp(t - m) if t != -math.inf else 0.0 for t in s]
+            z = sum(e)
+            for d in range(hd):
+                out[i, h * hd + d] = sum(e[j] * v[h // g, j, d] for j in range(L)) / z
+    return out
+
+
+@pytest.mark.parametrize("kind,window", [("full", 0), ("sliding", 1), ("sliding", 2), ("sliding", 3), ("sliding", 9), ("sliding", 20)])
+@pytest.mark.parametrize("L", [1, 2, 5, 9, 17])
+def test_attention_vs_sdpa_and_brute_force(kind, window, L):
+    r = np.random.default_rng(L * 31 + window)
+    q, k, v = r.standard_normal((4, L, 8)), r.standard_normal((2, L, 8)), r.standard_normal((2, L, 8))
+    got = O.attention(q, k, v, kind, window)
+    np.testing.assert_allclose(got, torch_attention(q, k, v, kind, window), atol=1e-12)
+    if L <= 9:
+        np.testing.assert_allclose(got, brute_attention(q, k, v, kind, window), atol=1e-12)
+
+
+def test_window_one_returns_own_value():
+    r = np.random.default_rng(7)
+    q, k, v = r.standard_normal((4, 6, 8)), r.standard_normal((2, 6, 8)), r.standard_normal((2, 6, 8))
+    o = O.attention(q, k, v, "sliding", 1)
+    for h in range(4):
+        np.testing.assert_allclose(o[:, h * 8:(h + 1) * 8], v[h // 2], atol=1e-14)
+
+
+def test_gqa_equals_duplicated_heads():
+    r = np.random.default_rng(8)
+    q, k, v = r.standard_normal((4, 9, 8)), r.standard_normal((2, 9, 8)), r.standard_normal((2, 9, 8))
+    a = O.attention(q, k, v, "sliding", 4)
+    b = O.attention(q, np.repeat(k, 2, 0), np.repeat(v, 2, 0), "sliding", 4)
+    np.testing.assert_allclose(a, b, atol=1e-14)
+
+
+# ------------------------------------------------------------------------------ block
+def torch_layer(shape, w, x, p1d=None):
+    """Parallel block from library routines; RoPE (text positions) as complex rotation."""
+    t = lambda a: torch.tensor(np.asarray(a, dtype=np.float64))
+    B, L, D = x.shape
+    Hq, Hkv, hd = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
+    a = F.layer_norm(t(x), (D,), weight=t(w["ln_w"]), bias=None, eps=shape.ln_eps)
+    q = F.linear(a, t(w["wq"])).view(B, L, Hq, hd).transpose(1, 2)
+    k = F.linear(a, t(w["wk"])).view(B, L, Hkv, hd).transpose(1, 2)
+    v = F.linear(a, t(w["wv"])).view(B, L, Hkv, hd).transpose(1, 2)
+    if shape.kind == "sliding":
+        q = torch.tensor(textbook_rope(q.numpy(), p1d[:, None, :], shape.rope_theta, hd))
+        k = torch.tensor(textbook_rope(k.numpy(), p1d[:, None, :], shape.rope_theta, hd))
+    g = Hq // Hkv
+    i = torch.arange(L)[:, None]
+    j = torch.arange(L)[None, :]
+    mask = j <= i
+    if shape.kind == "sliding":
+        mask &= j > i - shape.window
+    o = F.scaled_dot_product_attention(q, k.repeat_interleave(g, 1), v.repeat_interleave(g, 1), attn_mask=mask)
+    o = o.transpose(1, 2).reshape(B, L, Hq * hd)
+    mlp = F.linear(F.silu(F.linear(a, t(w["w_gate"]))) * F.linear(a, t(w["w_up"])), t(w["w_down"]))
+    return (t(x) + F.linear(o, t(w["wo"])) + mlp).numpy()
+
+
+@pytest.mark.parametrize("kind,window", [("sliding", 3), ("sliding", 1), ("sliding", 40), ("full", 0)])
+@pytest.mark.parametrize("L", [1, 5, 17])
+def test_parallel_block_vs_library_routines(kind, window, L):
+    sh = tiny_shape(kind, window)
+    w = rand_weights(sh, seed=L)
+    r = np.random.default_rng(L + 100)
+    x = r.standard_normal((2, L, sh.hidden))
+    p1d = np.arange(L)[None, :].repeat(2, 0) + np.array([[0], [17]])
+    got = O.layer_prefill(sh, w, x, np.stack([p1d, p1d, p1d]))
+    np.testing.assert_allclose(got, torch_layer(sh, w, x, p1d), atol=1e-10)
+
+
+def test_parallel_block_identity_no_post_norm():
+    sh = tiny_shape("sliding", 4)
+    w = rand_weights(sh, seed=11)
+    x = np.random.default_rng(12).standard_normal((1, 9, sh.hidden))
+    pos = mixed_pos(1, 9)
+    out, st = O.layer_prefill(sh, w, x, pos, return_stages=True)
+    attn = st["attn"][0] @ w["wo"].T
+    mlp = st["act"][0] @ w["w_down"].T
+    np.testing.assert_allclose(out[0], x[0] + attn + mlp, atol=1e-12)
+    # Zeroing the MLP weights leaves x + attn; zeroing attention output leaves x + mlp.
+    w2 = dict(w, w_down=np.zeros_like(w["w_down"]))
+    np.testing.assert_allclose(O.layer_prefill(sh, w2, x, pos)[0], x[0] + attn, atol=1e-12)
+    w3 = dict(w, wo=np.zeros_like(w["wo"]))
+    np.testing.assert_allclose(O.layer_prefill(sh, w3, x, pos)[0], x[0] + mlp, atol=1e-12)
+
+
+def test_window_at_least_L_equals_causal():
+    sh = tiny_shape("sliding", 9)
+    w = rand_weights(sh, seed=13)
+    x = np.random.default_rng(14).standard_normal((2, 9, sh.hidden))
+    pos = mixed_pos(2, 9)
+    a = O.layer_prefill(sh, w, x, pos)
+    for W in (9, 12, 1000):
+        b = O.layer_prefill(dataclass_replace(sh, window=W), w, x, pos)
+        assert np.array_equal(a, b)
+
+
+def dataclass_replace(sh, **kw):
+    import dataclasses
+    return dataclasses.replace(sh, **kw)
+
+
+def test_full_layer_ignores_positions():
+    sh = tiny_shape("full", 0)
+    w = rand_weights(sh, seed=15)
+    x = np.random.default_rng(16).standard_normal((2, 9, sh.hidden))
+    a = O.layer_prefill(sh, w, x, text_pos(2, 9))
+    b = O.layer_prefill(sh, w, x, mixed_pos(2, 9, seed=99))
+    assert np.array_equal(a, b)
+
+
+def test_deepstack_adds_at_rows_only():
+    sh = tiny_shape("sliding", 3)
+    w = rand_weights(sh, seed=17)
+    x = np.random.default_rng(18).standard_normal((2, 6, sh.hidden))
+    pos = mixed_pos(2, 6)
+    rows = np.array([1, 2, 7])
+    ds = np.random.default_rng(19).standard_normal((3, sh.hidden))
+    a = O.layer_prefill(sh, w, x, pos).reshape(12, -1)
+    b = O.layer_prefill(sh, w, x, pos, rows, ds).reshape(12, -1)
+    d = b - a
+    np.testing.assert_allclose(d[rows], ds, atol=1e-12)
+    assert np.all(np.delete(d, rows, axis=0) == 0)
+
+
+def test_stack_deepstack_first_three_layers_only():
+    sh = tiny_shape("sliding", 3)
+    ws = [rand_weights(sh, seed=20 + i) for i in range(5)]
+    x = np.random.default_rng(30).standard_normal((1, 6, sh.hidden))
+    pos = mixed_pos(1, 6)
+    rows = np.array([2, 3])
+    zeros = [np.zeros((2, sh.hidden))] * 5
+    base = O.stack_prefill(sh, ws, x, pos)
+    assert np.array_equal(O.stack_prefill(sh, ws, x, pos, rows, zeros), base)
+    # A deepstack tensor at index >= 3 is never used.
+    ds = [np.zeros((2, sh.hidden))] * 3 + [np.ones((2, sh.hidden))] * 2
+    assert np.array_equal(O.stack_prefill(sh, ws, x, pos, rows, ds), base)
+    ds = [np.zeros((2, sh.hidden))] * 2 + [np.ones((2, sh.hidden))]
+    assert not np.array_equal(O.stack_prefill(sh, ws, x, pos, rows, ds), base)
+
+
+def test_layer_pattern_page_example():
+    g = golden("layer_pattern_28.json")
+    full = [i for i in range(g["n_layers"]) if O.layer_kind(i) == "full"]
+    assert full == g["full_attention_layers"]
+
+
+def test_causal_prefix_page_case():
+    g = golden("causal_prefix.json")
+    sh = tiny_shape("sliding", 8)
+    ws = [rand_weights(sh, seed=40 + i, std=0.15) for i in range(len(g["layers"]))]
+    assert [O.layer_kind(i) for i in range(len(ws))] == g["layers"]
+    Ll, Ls = g["long_prefill"], g["short_prefill"]
+    x = np.random.default_rng(41).standard_normal((1, Ll, sh.hidden))
+    pos = text_pos(1, Ll)
+    nw = 1 + 0.1 * np.random.default_rng(42).standard_normal(sh.hidden)
+    emb = 0.2 * np.random.default_rng(43).standard_normal((50, sh.hidden))
+    hl = O.stack_prefill(sh, ws, x, pos)
+    hs = O.stack_prefill(sh, ws, x[:, :Ls], pos[:, :, :Ls])
+    ll = O.logits(hl[0, :Ls], nw, 1e-5, emb, 0.25)
+    ls = O.logits(hs[0], nw, 1e-5, emb, 0.25)
+    assert np.max(np.abs(ll - ls)) <= g["tolerance"] * 1e-6  # fp64: far inside the page's 1e-4
+
+
+def test_prefill_decode_consistency():
+    for kind, W in (("sliding", 4), ("full", 0)):
+        sh = tiny_shape(kind, W)
+        w = rand_weights(sh, seed=50)
+        B, L = 2, 7
+        x = np.random.default_rng(51).standard_normal((B, L, sh.hidden))
+        pos = mixed_pos(B, L)
+        full_out = O.layer_prefill(sh, w, x, pos)
+        _, st = O.layer_prefill(sh, w, x[:, :L - 1], pos[:, :, :L - 1], return_stages=True)
+        cap = L + 2
+        kc = np.zeros((B, sh.n_kv_heads, cap, sh.head_dim))
+        vc = np.zeros_like(kc)
+        kc[:, :, :L - 1] = st["k"]
+        vc[:, :, :L - 1] = st["v"]
+        lens = np.full(B, L - 1)
+        out, knew, vnew = O.layer_decode(sh, w, x[:, L - 1], pos[:, :, L - 1], kc, vc, lens)
+        np.testing.assert_allclose(out, full_out[:, L - 1], atol=1e-11)
+
+
+# ------------------------------------------------------------------------------ logits
+def test_logits_vs_library_and_scale():
+    r = np.random.default_rng(60)
+    h, nw, emb = r.standard_normal((5, 32)), 1 + 0.1 * r.standard_normal(32), r.standard_normal((40, 32))
+    g = golden("logit_scale.json")
+    ref = F.linear(F.layer_norm(torch.tensor(h), (32,), weight=torch.tensor(nw), bias=None, eps=1e-5),
+                   torch.tensor(emb)).numpy() * g["logit_scale"]
+    got = O.logits(h, nw, 1e-5, emb, g["logit_scale"])
+    np.testing.assert_allclose(got, ref, atol=1e-12)
+    one = O.logits(h, nw, 1e-5, emb, 1.0)
+    for s in (0.25, 0.0625, 2.0 ** -10):
+        assert np.array_equal(O.logits(h, nw, 1e-5, emb, s), one * s)
+
+
+# ------------------------------------------------------------------------------ positions
+def test_positions_text_only():
+    tok = np.arange(1, 41).reshape(2, 20)
+    pos, d = O.mrope_positions(tok, 255031, np.zeros((0, 3), np.int32), np.array([0, 0, 0]), 2)
+    assert np.array_equal(pos, text_pos(2, 20))
+    assert np.array_equal(d, [0, 0])
+
+
+def test_positions_image_448_page_example():
+    g = golden("image_pad_448.json")
+    # One still image: its two temporal frames merge into t = 1; h, w in patches.
+    grid = [1, g["image_px"][0] // g["patch_size"], g["image_px"][1] // g["patch_size"]]
+    assert grid == g["grid_thw"]
+    n = grid[0] * (grid[1] // g["spatial_merge"]) * (grid[2] // g["spatial_merge"])
+    assert n == g["n_image_tokens"]
+    tok = np.array([[5, 255028] + [255031] * n + [255029, 7]])
+    pos, d = O.mrope_positions(tok, 255031, np.array([grid]), np.array([0, 1]), g["spatial_merge"])
+    img = pos[:, 0, 2:2 + n]
+    assert np.all(img[0] == 2)
+    assert img[1].min() == 2 and img[1].max() == 2 + 13
+    assert img[2].min() == 2 and img[2].max() == 2 + 13
+    assert pos[0, 0, 2 + n] == 2 + 14  # next text starts at max + 1
+    assert d[0] == (2 + 14 + 2) - tok.shape[1]
+
+
+def test_positions_c1_layout_hand_derived():
+    """64 text, one 1x64x64 (patch) image = 32x32 merged tokens, 3008 text."""
+    from synth.workloads import c1_tokens
+    tok, grid, off = c1_tokens(seed=1)
+    pos, d = O.mrope_positions(tok, 255031, grid, off, 2)
+    assert np.array_equal(pos[:, 0, :64], np.stack([np.arange(64)] * 3))
+    r = np.arange(1024)
+    assert np.array_equal(pos[0, 0, 64:1088], np.full(1024, 64))
+    assert np.array_equal(pos[1, 0, 64:1088], 64 + r // 32)
+    assert np.array_equal(pos[2, 0, 64:1088], 64 + r % 32)
+    assert np.array_equal(pos[:, 0, 1088:], np.stack([np.arange(1088, 4096) - 992] * 3))
+    assert pos[0, 0, 1088] == 96 and pos[0, 0, 4095] == 3103
+    assert d[0] == -992
+    assert O.decode_positions([4096], d)[:, 0].tolist() == [3104] * 3
+
+
+def test_positions_video_like_and_multi_image():
+    # t = 2 frames of a 4x6 patch grid -> 2 * 2 * 3 = 12 pads; then a 2x2 image (1 pad).
+    tok = np.array([[9, 9] + [255031] * 12 + [9] + [255031] + [9]])
+    grid = np.array([[2, 4, 6], [1, 2, 2]])
+    pos, d = O.mrope_positions(tok, 255031, grid, np.array([0, 2]), 2)
+    t, h, w = pos[:, 0, 2:14]
+    assert t.tolist() == [2] * 6 + [3] * 6
+    assert h.tolist() == [2, 2, 2, 3, 3, 3] * 2
+    assert w.tolist() == [2, 3, 4] * 4
+    assert pos[:, 0, 14].tolist() == [5, 5, 5]   # 2 + max(2, 2, 3)
+    assert pos[:, 0, 15].tolist() == [6, 6, 6]   # 1x1 merged grid
+    assert pos[:, 0, 16].tolist() == [7, 7, 7]
+    assert d[0] == 8 - 17
+
+
+@pytest.mark.parametrize("case,code", [
+    ("short_span", O.POS_SPAN_MISMATCH), ("extra_pads", O.POS_EXTRA_PADS),
+    ("unused_image", O.POS_UNUSED_IMAGES), ("bad_grid", O.POS_BAD_GRID)])
+def test_positions_errors(case, code):
+    n = 4
+    if case == "short_span":
+        tok, grid = [[1] + [255031] * (n - 1) + [2]], [[1, 4, 4]]
+    elif case == "extra_pads":
+        tok, grid = [[1] + [255031] * (n + 1) + [2]], [[1, 4, 4]]
+    elif case == "unused_image":
+        tok, grid = [[1] + [255031] * n + [2]], [[1, 4, 4], [1, 2, 2]]
+    else:
+        tok, grid = [[1] + [255031] * n + [2]], [[1, 3, 4]]
+    with pytest.raises(O.PositionError) as e:
+        O.mrope_positions(np.array(tok), 255031, np.array(grid), np.array([0, len(grid)]), 2)
+    assert e.value.code == code
