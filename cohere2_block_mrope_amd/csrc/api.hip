@@ -1,0 +1,523 @@
+// extern "C" entry points of libcompass: argument validation (pure host code, run
+// before any HIP call), workspace carving, and the launch sequence of each call.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/compass.h"
+#include "launch.h"
+
+using namespace compass;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return COMPASS_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ----------------------------------------------------------------- kernel timing
+struct ProfRec {
+  const char* name;
+  hipEvent_t e0, e1;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;
+std::vector<std::pair<hipEvent_t, hipEvent_t>> g_prof_pool;
+std::vector<std::string> g_prof_names;
+
+struct KScope {
+  int idx = -1;
+  hipEvent_t stop = nullptr;
+  hipStream_t s;
+  KScope(const char* name, hipStream_t st) : s(st) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_on || g_prof.size() >= COMPASS_PROFILE_MAX) return;
+    const size_t i = g_prof.size();
+    if (i >= g_prof_pool.size()) {
+      hipEvent_t a, b;
+      if (hipEventCreate(&a) != hipSuccess) return;
+      if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return; }
+      g_prof_pool.push_back({a, b});
+    }
+    ProfRec r{name, g_prof_pool[i].first, g_prof_pool[i].second};
+    if (hipEventRecord(r.e0, s) != hipSuccess) return;
+    g_prof.push_back(r);
+    idx = (int)i;
+    stop = r.e1;
+    bool seen = false;
+    for (auto& n : g_prof_names) seen |= (n == name);
+    if (!seen) g_prof_names.push_back(name);
+  }
+  ~KScope() {
+    if (idx >= 0) (void)hipEventRecord(stop, s);
+  }
+};
+
+#define LAUNCH(name, stream, call)                                                   \
+  do {                                                                               \
+    hipError_t e_;                                                                   \
+    {                                                                                \
+      KScope ks_(name, stream);                                                      \
+      e_ = (call);                                                                   \
+    }                                                                                \
+    if (e_ != hipSuccess)                                                            \
+      return fail(COMPASS_E_DEVICE, "%s: launch failed: %s", name, hipGetErrorString(e_)); \
+  } while (0)
+
+// ----------------------------------------------------------------- validation
+int check_desc(const compass_layer_desc* d) {
+  if (!d) return fail(COMPASS_E_INVALID, "descriptor is NULL");
+  if (d->hidden <= 0 || d->n_q_heads <= 0 || d->n_kv_heads <= 0 || d->head_dim <= 0 ||
+      d->intermediate <= 0)
+    return fail(COMPASS_E_INVALID, "non-positive width in descriptor");
+  if (d->dtype != COMPASS_F32 && d->dtype != COMPASS_BF16)
+    return fail(COMPASS_E_UNSUPPORTED, "dtype %d not supported", d->dtype);
+  if (d->kind != COMPASS_SLIDING && d->kind != COMPASS_FULL)
+    return fail(COMPASS_E_INVALID, "kind %d is neither SLIDING nor FULL", d->kind);
+  if (d->n_q_heads % d->n_kv_heads)
+    return fail(COMPASS_E_INVALID, "n_q_heads %d not a multiple of n_kv_heads %d", d->n_q_heads,
+                d->n_kv_heads);
+  const int g = d->n_q_heads / d->n_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(COMPASS_E_UNSUPPORTED, "query heads per kv head %d not in {1,2,4,8}", g);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(COMPASS_E_UNSUPPORTED, "head_dim %d not in {64, 128}", d->head_dim);
+  if (d->hidden % 64 || d->hidden > 8192)
+    return fail(COMPASS_E_UNSUPPORTED, "hidden %d must be a multiple of 64 and <= 8192", d->hidden);
+  if (d->intermediate % 64)
+    return fail(COMPASS_E_UNSUPPORTED, "intermediate %d not a multiple of 64", d->intermediate);
+  if (((long long)(d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim) % 128)
+    return fail(COMPASS_E_UNSUPPORTED, "(Hq + 2 Hkv) * head_dim must be a multiple of 128");
+  if ((long long)(d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim + 2LL * d->intermediate > (1LL << 30))
+    return fail(COMPASS_E_UNSUPPORTED, "projection width too large");
+  if (!(d->ln_eps >= 0.f) || !isfinite(d->ln_eps))
+    return fail(COMPASS_E_INVALID, "ln_eps must be finite and >= 0");
+  if (d->kind == COMPASS_SLIDING) {
+    if (d->window < 1) return fail(COMPASS_E_INVALID, "window %d < 1 on a sliding layer", d->window);
+    const int half = d->head_dim / 2;
+    const int st = d->mrope_section[0], sh = d->mrope_section[1], sw = d->mrope_section[2];
+    if (st < 0 || sh < 0 || sw < 0 || st + sh + sw != half)
+      return fail(COMPASS_E_INVALID, "mrope_section {%d,%d,%d} must be >= 0 and sum to %d", st, sh,
+                  sw, half);
+    int ct = 0, ch = 0, cw = 0;
+    for (int j = 0; j < half; ++j) {
+      if (j % 3 == 1 && j < 3 * sh) ++ch;
+      else if (j % 3 == 2 && j < 3 * sw) ++cw;
+      else ++ct;
+    }
+    if (ct != st || ch != sh || cw != sw)
+      return fail(COMPASS_E_INVALID, "mrope_section {%d,%d,%d} not realisable by the interleave", st,
+                  sh, sw);
+    if (!(d->rope_theta > 0.f) || !isfinite(d->rope_theta))
+      return fail(COMPASS_E_INVALID, "rope_theta must be finite and > 0");
+  }
+  return COMPASS_OK;
+}
+
+int check_weights(const compass_layer_weights* w) {
+  if (!w) return fail(COMPASS_E_INVALID, "weights struct is NULL");
+  const void* p[8] = {w->ln_w, w->wq, w->wk, w->wv, w->wo, w->w_gate, w->w_up, w->w_down};
+  const char* n[8] = {"ln_w", "wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"};
+  for (int i = 0; i < 8; ++i) {
+    if (!p[i]) return fail(COMPASS_E_INVALID, "weight %s is NULL", n[i]);
+    if (!aligned16(p[i])) return fail(COMPASS_E_ALIGN, "weight %s not 16-byte aligned", n[i]);
+  }
+  return COMPASS_OK;
+}
+
+RopeTable rope_table(const compass_layer_desc* d) {
+  RopeTable t;
+  t.theta = d->rope_theta;
+  t.sh3 = 3 * d->mrope_section[1];
+  t.sw3 = 3 * d->mrope_section[2];
+  return t;
+}
+
+// ----------------------------------------------------------------- workspace
+constexpr size_t kAlign = 256;
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Dims {
+  long long D, Hq, Hkv, hd, I, qd, Nv, K2;
+  int esz;
+};
+Dims dims(const compass_layer_desc* d) {
+  Dims m;
+  m.D = d->hidden; m.Hq = d->n_q_heads; m.Hkv = d->n_kv_heads; m.hd = d->head_dim;
+  m.I = d->intermediate;
+  m.qd = m.Hq * m.hd;
+  m.Nv = (m.Hq + 2 * m.Hkv) * m.hd + 2 * m.I;
+  m.K2 = m.qd + m.I;
+  m.esz = d->dtype == COMPASS_BF16 ? 2 : 4;
+  return m;
+}
+
+struct PrefillWs {
+  size_t a, q, kc, vc, a2, raw, total;
+};
+PrefillWs prefill_ws(const compass_layer_desc* d, long long B, long long L) {
+  const Dims m = dims(d);
+  const long long T = B * L;
+  PrefillWs w;
+  size_t off = 0;
+  w.a = off; off += up(T * m.D * m.esz);
+  w.q = off; off += up(T * m.qd * m.esz);
+  w.kc = off; off += up(B * m.Hkv * L * m.hd * m.esz);
+  w.vc = off; off += up(B * m.Hkv * L * m.hd * m.esz);
+  w.a2 = off; off += up(T * m.K2 * m.esz);
+  w.raw = off;
+  if (d->dtype == COMPASS_F32) off += up(T * (m.Nv > m.D ? m.Nv : m.D) * 4);
+  w.total = off;
+  return w;
+}
+
+int decode_splits(long long tiles, long long K) {
+  long long s = 512 / (tiles > 0 ? tiles : 1);
+  if (s > K / 256) s = K / 256;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+struct DecodeWs {
+  size_t a, raw1, q, a2, part, raw2, total;
+  int s1, s2, n_chunks;
+};
+DecodeWs decode_ws(const compass_layer_desc* d, long long B, long long cap) {
+  const Dims m = dims(d);
+  DecodeWs w;
+  const long long tiles1 = ((B + 63) / 64) * ((m.Nv + 63) / 64);
+  const long long tiles2 = ((B + 63) / 64) * ((m.D + 63) / 64);
+  w.s1 = decode_splits(tiles1, m.D);
+  w.s2 = decode_splits(tiles2, m.K2);
+  const long long keys = d->kind == COMPASS_SLIDING ? (cap < d->window ? cap : d->window) : cap;
+  const int ck = decode_chunk_keys(d->dtype, d->head_dim);
+  w.n_chunks = (int)((keys + ck - 1) / ck);
+  if (w.n_chunks < 1) w.n_chunks = 1;
+  size_t off = 0;
+  w.a = off; off += up(B * m.D * m.esz);
+  w.raw1 = off; off += up((long long)w.s1 * B * m.Nv * 4);
+  w.q = off; off += up(B * m.qd * m.esz);
+  w.a2 = off; off += up(B * m.K2 * m.esz);
+  w.part = off; off += up(B * m.Hq * (long long)w.n_chunks * (m.hd + 2) * 4);
+  w.raw2 = off; off += up((long long)w.s2 * B * m.D * 4);
+  w.total = off;
+  return w;
+}
+
+BMap proj_bmap(const compass_layer_desc* d, const compass_layer_weights* w) {
+  const Dims m = dims(d);
+  BMap b{};
+  b.kind = 1;
+  b.p[0] = w->wq; b.p[1] = w->wk; b.p[2] = w->wv; b.p[3] = w->w_gate; b.p[4] = w->w_up;
+  b.ld0 = (int)m.D;
+  b.nq64 = (int)(m.qd / 64);
+  b.nk64 = (int)(m.Hkv * m.hd / 64);
+  return b;
+}
+
+BMap out_bmap(const compass_layer_desc* d, const compass_layer_weights* w) {
+  const Dims m = dims(d);
+  BMap b{};
+  b.kind = 2;
+  b.p[0] = w->wo; b.p[1] = w->w_down;
+  b.ld0 = (int)m.qd; b.ld1 = (int)m.I;
+  b.ksplit = (int)m.qd;
+  return b;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* compass_last_error(void) { return g_err.c_str(); }
+
+const char* compass_version(void) { return "compass-mi355x 0.1 (gfx950)"; }
+
+int compass_mrope_positions(const int32_t* token_ids, int32_t B, int32_t L, int32_t image_token_id,
+                            const int32_t* grid_thw, const int32_t* img_offset, int32_t spatial_merge,
+                            int32_t* pos, int32_t* rope_delta, int32_t* status, void* stream) {
+  if (B < 1 || L < 1) return fail(COMPASS_E_INVALID, "B=%d, L=%d must be >= 1", B, L);
+  if ((long long)B * L * 3 > (1LL << 31) - 1) return fail(COMPASS_E_UNSUPPORTED, "B*L too large");
+  if (!token_ids || !img_offset || !pos || !rope_delta || !status)
+    return fail(COMPASS_E_INVALID, "NULL pointer argument");
+  if (spatial_merge < 1) return fail(COMPASS_E_INVALID, "spatial_merge %d < 1", spatial_merge);
+  const hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  LAUNCH("positions", s, launch_positions(token_ids, B, L, image_token_id, grid_thw, img_offset,
+                                          spatial_merge, pos, rope_delta, status, s));
+  return ok();
+}
+
+size_t compass_workspace_size(const compass_layer_desc* d, int32_t B, int32_t L, int32_t capacity,
+                              int32_t decode) {
+  const std::string saved = g_err;
+  if (check_desc(d) != COMPASS_OK || B < 1) { g_err = saved; return 0; }
+  if (decode) {
+    if (capacity < 1) return 0;
+    return decode_ws(d, B, capacity).total;
+  }
+  if (L < 1) return 0;
+  return prefill_ws(d, B, L).total;
+}
+
+int compass_layer_prefill(const compass_layer_desc* d, const compass_layer_weights* w, int32_t B,
+                          int32_t L, const void* x, const int32_t* pos, const compass_kv* kv,
+                          const int32_t* ds_rows, const void* ds, int32_t n_ds, void* out,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if ((rc = check_weights(w))) return rc;
+  if (B < 1 || L < 1) return fail(COMPASS_E_INVALID, "B=%d, L=%d must be >= 1", B, L);
+  const Dims m = dims(d);
+  const long long T = (long long)B * L;
+  if (T * (m.K2 > m.Nv ? m.K2 : m.Nv) > (1LL << 31) - 1 || T > (1LL << 31) - 1)
+    return fail(COMPASS_E_UNSUPPORTED, "B*L too large for 32-bit row indexing");
+  if (!x || !out) return fail(COMPASS_E_INVALID, "x or out is NULL");
+  if (!aligned16(x) || !aligned16(out)) return fail(COMPASS_E_ALIGN, "x/out not 16-byte aligned");
+  const size_t xbytes = (size_t)T * m.D * m.esz;
+  if (x != out && overlap(x, xbytes, out, xbytes))
+    return fail(COMPASS_E_INVALID, "out partially overlaps x (only exact aliasing is allowed)");
+  const bool sliding = d->kind == COMPASS_SLIDING;
+  if (sliding && !pos) return fail(COMPASS_E_INVALID, "pos is NULL on a sliding layer");
+  if (kv) {
+    if (!kv->k || !kv->v) return fail(COMPASS_E_INVALID, "kv->k or kv->v is NULL");
+    if (!aligned16(kv->k) || !aligned16(kv->v)) return fail(COMPASS_E_ALIGN, "kv not 16-byte aligned");
+    if (kv->capacity < L) return fail(COMPASS_E_INVALID, "kv capacity %d < L=%d", kv->capacity, L);
+  }
+  if (n_ds < 0) return fail(COMPASS_E_INVALID, "n_ds < 0");
+  if (n_ds > 0) {
+    if (!ds_rows || !ds) return fail(COMPASS_E_INVALID, "deepstack pointers NULL with n_ds > 0");
+    if (!aligned16(ds)) return fail(COMPASS_E_ALIGN, "ds not 16-byte aligned");
+  }
+  const PrefillWs ws = prefill_ws(d, B, L);
+  if (!workspace || ws_bytes < ws.total)
+    return fail(COMPASS_E_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, ws.total);
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0)
+    return fail(COMPASS_E_ALIGN, "workspace not 256-byte aligned");
+
+  char* wsb = (char*)workspace;
+  void* a = wsb + ws.a;
+  void* q = wsb + ws.q;
+  void* kc = kv ? kv->k : (void*)(wsb + ws.kc);
+  void* vc = kv ? kv->v : (void*)(wsb + ws.vc);
+  const int cap = kv ? kv->capacity : L;
+  void* a2 = wsb + ws.a2;
+  float* raw = (float*)(wsb + ws.raw);
+  const hipStream_t s = (hipStream_t)stream;
+  const int dt = d->dtype;
+
+  ProjEpi ep{};
+  ep.decode = 0;
+  ep.L = L;
+  ep.pos = pos;
+  ep.pos_stride = (int)T;
+  ep.rope = sliding ? 1 : 0;
+  ep.Hq = (int)m.Hq; ep.Hkv = (int)m.Hkv; ep.hd = (int)m.hd;
+  ep.q = q; ep.Lq = L;
+  ep.kc = kc; ep.vc = vc; ep.cap = cap;
+  ep.lens = nullptr;
+  ep.act = a2; ep.ldact = (int)m.K2; ep.act_col0 = (int)m.qd;
+  ep.nq64 = (int)(m.qd / 64); ep.nk64 = (int)(m.Hkv * m.hd / 64);
+  ep.I = (int)m.I;
+  const RopeTable rt = rope_table(d);
+  const BMap pb = proj_bmap(d, w), ob = out_bmap(d, w);
+
+  (void)hipGetLastError();
+  LAUNCH("layernorm", s, launch_layernorm(dt, x, w->ln_w, d->ln_eps, a, (int)T, (int)m.D, s));
+  if (dt == COMPASS_BF16) {
+    LAUNCH("gemm_proj", s, launch_gemm_bf16_proj(a, (int)m.D, (int)T, (int)m.D, pb, (int)m.Nv, ep, rt, s));
+  } else {
+    LAUNCH("gemm_proj_f32", s, launch_gemm_f32_raw(a, (int)m.D, (int)T, (int)m.D, pb, (int)m.Nv, 1, raw, 1.f, s));
+    LAUNCH("proj_epilogue", s, launch_proj_epilogue(dt, raw, 1, (int)T, (int)m.Nv, ep, rt, s));
+  }
+  LAUNCH("attn_prefill", s, launch_attention_prefill(dt, q, kc, vc, B, (int)m.Hq, (int)m.Hkv, L, cap,
+                                                     (int)m.hd, sliding, d->window, a2, (int)m.K2, s));
+  if (dt == COMPASS_BF16) {
+    LAUNCH("gemm_out", s, launch_gemm_bf16_resid(a2, (int)m.K2, (int)T, (int)m.K2, ob, (int)m.D, x, out,
+                                                 (int)m.D, s));
+  } else {
+    LAUNCH("gemm_out_f32", s, launch_gemm_f32_raw(a2, (int)m.K2, (int)T, (int)m.K2, ob, (int)m.D, 1, raw, 1.f, s));
+    LAUNCH("splitk_resid", s, launch_splitk_resid(dt, raw, 1, (int)T, (int)m.D, x, out, nullptr, 0, s));
+  }
+  if (n_ds > 0)
+    LAUNCH("deepstack", s, launch_deepstack(dt, ds_rows, ds, n_ds, (int)m.D, (int)T, out, s));
+  return ok();
+}
+
+int compass_layer_decode(const compass_layer_desc* d, const compass_layer_weights* w, int32_t B,
+                         const void* x, const int32_t* pos, const compass_kv* kv, void* out,
+                         void* workspace, size_t ws_bytes, void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if ((rc = check_weights(w))) return rc;
+  if (B < 1) return fail(COMPASS_E_INVALID, "B=%d must be >= 1", B);
+  const Dims m = dims(d);
+  if ((long long)B * (m.K2 > m.Nv ? m.K2 : m.Nv) > (1LL << 31) - 1)
+    return fail(COMPASS_E_UNSUPPORTED, "B too large");
+  if (!x || !out) return fail(COMPASS_E_INVALID, "x or out is NULL");
+  if (!aligned16(x) || !aligned16(out)) return fail(COMPASS_E_ALIGN, "x/out not 16-byte aligned");
+  const size_t xbytes = (size_t)B * m.D * m.esz;
+  if (x != out && overlap(x, xbytes, out, xbytes))
+    return fail(COMPASS_E_INVALID, "out partially overlaps x (only exact aliasing is allowed)");
+  const bool sliding = d->kind == COMPASS_SLIDING;
+  if (sliding && !pos) return fail(COMPASS_E_INVALID, "pos is NULL on a sliding layer");
+  if (!kv || !kv->k || !kv->v || !kv->lens) return fail(COMPASS_E_INVALID, "decode needs kv with k, v, lens");
+  if (!aligned16(kv->k) || !aligned16(kv->v)) return fail(COMPASS_E_ALIGN, "kv not 16-byte aligned");
+  if (kv->capacity < 1) return fail(COMPASS_E_INVALID, "kv capacity %d < 1", kv->capacity);
+  if ((long long)B * m.Hkv * kv->capacity * m.hd > (1LL << 40))
+    return fail(COMPASS_E_UNSUPPORTED, "kv cache too large");
+  const DecodeWs ws = decode_ws(d, B, kv->capacity);
+  if (!workspace || ws_bytes < ws.total)
+    return fail(COMPASS_E_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, ws.total);
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0)
+    return fail(COMPASS_E_ALIGN, "workspace not 256-byte aligned");
+
+  char* wsb = (char*)workspace;
+  void* a = wsb + ws.a;
+  float* raw1 = (float*)(wsb + ws.raw1);
+  void* q = wsb + ws.q;
+  void* a2 = wsb + ws.a2;
+  float* part = (float*)(wsb + ws.part);
+  float* raw2 = (float*)(wsb + ws.raw2);
+  const hipStream_t s = (hipStream_t)stream;
+  const int dt = d->dtype;
+
+  ProjEpi ep{};
+  ep.decode = 1;
+  ep.L = 1;
+  ep.pos = pos;
+  ep.pos_stride = B;
+  ep.rope = sliding ? 1 : 0;
+  ep.Hq = (int)m.Hq; ep.Hkv = (int)m.Hkv; ep.hd = (int)m.hd;
+  ep.q = q; ep.Lq = 1;
+  ep.kc = kv->k; ep.vc = kv->v; ep.cap = kv->capacity;
+  ep.lens = kv->lens;
+  ep.act = a2; ep.ldact = (int)m.K2; ep.act_col0 = (int)m.qd;
+  ep.nq64 = (int)(m.qd / 64); ep.nk64 = (int)(m.Hkv * m.hd / 64);
+  ep.I = (int)m.I;
+  const RopeTable rt = rope_table(d);
+  const BMap pb = proj_bmap(d, w), ob = out_bmap(d, w);
+
+  (void)hipGetLastError();
+  LAUNCH("layernorm", s, launch_layernorm(dt, x, w->ln_w, d->ln_eps, a, B, (int)m.D, s));
+  if (dt == COMPASS_BF16)
+    LAUNCH("gemm_proj_decode", s, launch_gemm_bf16_raw(a, (int)m.D, B, (int)m.D, pb, (int)m.Nv, ws.s1, raw1, s));
+  else
+    LAUNCH("gemm_proj_decode", s, launch_gemm_f32_raw(a, (int)m.D, B, (int)m.D, pb, (int)m.Nv, ws.s1, raw1, 1.f, s));
+  LAUNCH("proj_epilogue", s, launch_proj_epilogue(dt, raw1, ws.s1, B, (int)m.Nv, ep, rt, s));
+  LAUNCH("decode_attn", s, launch_decode_attention(dt, q, kv->k, kv->v, kv->lens, B, (int)m.Hq, (int)m.Hkv,
+                                                   kv->capacity, (int)m.hd, sliding, d->window,
+                                                   ws.n_chunks, part, s));
+  LAUNCH("decode_combine", s, launch_decode_combine(dt, part, kv->lens, B, (int)m.Hq, kv->capacity,
+                                                    (int)m.hd, ws.n_chunks, a2, (int)m.K2, s));
+  if (dt == COMPASS_BF16)
+    LAUNCH("gemm_out_decode", s, launch_gemm_bf16_raw(a2, (int)m.K2, B, (int)m.K2, ob, (int)m.D, ws.s2, raw2, s));
+  else
+    LAUNCH("gemm_out_decode", s, launch_gemm_f32_raw(a2, (int)m.K2, B, (int)m.K2, ob, (int)m.D, ws.s2, raw2, 1.f, s));
+  LAUNCH("splitk_resid", s, launch_splitk_resid(dt, raw2, ws.s2, B, (int)m.D, x, out, kv->lens,
+                                                kv->capacity, s));
+  return ok();
+}
+
+size_t compass_logits_workspace_size(int32_t R, int32_t D, int32_t dtype) {
+  if (R < 1 || D < 1 || (dtype != COMPASS_F32 && dtype != COMPASS_BF16)) return 0;
+  return up((size_t)R * D * (dtype == COMPASS_BF16 ? 2 : 4));
+}
+
+int compass_logits(int32_t R, int32_t D, int32_t V, int32_t dtype, const void* h, const void* norm_w,
+                   float ln_eps, const void* embed, float logit_scale, float* logits, void* workspace,
+                   size_t ws_bytes, void* stream) {
+  if (R < 1 || D < 1 || V < 1) return fail(COMPASS_E_INVALID, "R=%d D=%d V=%d must be >= 1", R, D, V);
+  if (dtype != COMPASS_F32 && dtype != COMPASS_BF16)
+    return fail(COMPASS_E_UNSUPPORTED, "dtype %d not supported", dtype);
+  if (D % 64 || D > 8192) return fail(COMPASS_E_UNSUPPORTED, "D=%d must be a multiple of 64, <= 8192", D);
+  if ((long long)R * D > (1LL << 31) - 1 || (long long)V * D > (1LL << 31) - 1)
+    return fail(COMPASS_E_UNSUPPORTED, "R*D or V*D too large");
+  if (!h || !norm_w || !embed || !logits) return fail(COMPASS_E_INVALID, "NULL pointer argument");
+  if (!aligned16(h) || !aligned16(norm_w) || !aligned16(embed) || !aligned16(logits))
+    return fail(COMPASS_E_ALIGN, "tensor not 16-byte aligned");
+  if (!(ln_eps >= 0.f) || !isfinite(ln_eps)) return fail(COMPASS_E_INVALID, "ln_eps must be finite and >= 0");
+  const size_t need = compass_logits_workspace_size(R, D, dtype);
+  if (!workspace || ws_bytes < need)
+    return fail(COMPASS_E_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return fail(COMPASS_E_ALIGN, "workspace not 256-byte aligned");
+  const hipStream_t s = (hipStream_t)stream;
+  BMap eb{};
+  eb.kind = 0;
+  eb.p[0] = embed;
+  eb.ld0 = D;
+  (void)hipGetLastError();
+  LAUNCH("logits_layernorm", s, launch_layernorm(dtype, h, norm_w, ln_eps, workspace, R, D, s));
+  if (dtype == COMPASS_BF16)
+    LAUNCH("gemm_logits", s, launch_gemm_bf16_scaled_f32(workspace, D, R, D, eb, V, logit_scale, logits,
+                                                          (long long)V, s));
+  else
+    LAUNCH("gemm_logits", s, launch_gemm_f32_raw(workspace, D, R, D, eb, V, 1, logits, logit_scale, s));
+  return ok();
+}
+
+int compass_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+  return COMPASS_OK;
+}
+
+int compass_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof.clear();
+  g_prof_names.clear();
+  return COMPASS_OK;
+}
+
+int compass_profile_read(const char* kernel, int64_t* count, double* total_ms) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  int64_t c = 0;
+  double t = 0.0;
+  for (const ProfRec& r : g_prof) {
+    if (kernel && strcmp(kernel, r.name) != 0) continue;
+    hipError_t e = hipEventSynchronize(r.e1);
+    if (e != hipSuccess) return fail(COMPASS_E_DEVICE, "event sync failed: %s", hipGetErrorString(e));
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, r.e0, r.e1);
+    if (e != hipSuccess) return fail(COMPASS_E_DEVICE, "event time failed: %s", hipGetErrorString(e));
+    ++c;
+    t += ms;
+  }
+  if (count) *count = c;
+  if (total_ms) *total_ms = t;
+  return COMPASS_OK;
+}
+
+const char* compass_profile_kernel_name(int32_t i) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (i < 0 || (size_t)i >= g_prof_names.size()) return nullptr;
+  return g_prof_names[i].c_str();
+}
+
+}  // extern "C"

@@ -1,0 +1,287 @@
+// Causal GQA attention for prefill: o = softmax(q k^T / sqrt(hd)) v over the keys the
+// layer type allows ("Text decoder forward" of the mlxcel Compass issue: sliding
+// layers see the last `window` keys, full layers everything up to the query).
+// Query head h reads key/value head h / (Hq / Hkv).
+//
+// bf16 kernel (gfx950 MFMA). A 256-thread workgroup takes 128 queries of one head;
+// each wave owns 32 queries. Scores are computed transposed, S^T = K Q^T, with
+// v_mfma_f32_32x32x16_bf16: the result lane l then holds one query (l % 32) and 16 of
+// the tile's keys per 32-key block, so the online-softmax max and sum are in-lane
+// reductions plus one exchange with lane l ^ 32. The probabilities are already in
+// the B-operand layout of O^T = V^T P^T (the key order inside a 16-key step is
+// permuted identically on both operands), and the V^T operand is read from the
+// row-major V tile with ds_read_b64_tr_b16, the gfx950 LDS transpose read.
+// K/V tiles of 64 keys are double-buffered in LDS (rows padded against bank
+// conflicts); tiles outside the causal/window range are skipped, and only tiles that
+// straddle the diagonal or the window edge are masked.
+//
+// fp32 kernel: one wave per query, keys in 64-lane chunks with an online softmax.
+#include "common.h"
+#include "launch.h"
+
+namespace compass {
+namespace {
+
+struct AttnParams {
+  const bf16_t* q;
+  const bf16_t* k;
+  const bf16_t* v;
+  int B, Hq, Hkv, L, cap;
+  int sliding, window;
+  bf16_t* o;
+  int ldo;
+  float scale_log2;  // log2(e) / sqrt(hd)
+  int nqb;
+};
+
+constexpr int QB = 128, KB = 64;
+
+template <int HD>
+__global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
+  constexpr int KS = HD + 8;    // K row stride (elements): 8 consecutive rows -> distinct banks
+  constexpr int VS = HD + 16;   // V row stride: 4 rows x 32 B of a tr16 read -> distinct banks
+  constexpr int DB = HD / 32;   // 32-wide d blocks of O^T
+  constexpr int QK = HD / 16;   // 16-deep k-steps of S^T
+  constexpr int CH = HD / 8;    // 16-byte chunks per key row
+  constexpr int LD_PER_T = KB * CH / 256;
+  __shared__ __align__(16) bf16_t Ks[2][KB * KS];
+  __shared__ __align__(16) bf16_t Vs[2][KB * VS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qb = P.nqb - 1 - blockIdx.x;  // heaviest (latest) query blocks first
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int g = P.Hq / P.Hkv, kvh = h / g;
+  const int q0 = qb * QB;
+  const int L = P.L;
+  const int qw = q0 + 32 * wave + (lane & 31);  // this lane's query
+  const int half = lane >> 5;
+
+  // Q fragments (B operand of S^T): lane holds query qw, d = 16 ks + 8 half .. + 8.
+  bf16x8_t qf[QK];
+  {
+    const bf16_t* qp = P.q + (((size_t)b * P.Hq + h) * L + min(qw, L - 1)) * HD + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < QK; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * ks);
+  }
+
+  const int q_hi = min(q0 + QB - 1, L - 1);
+  const int k_lo = P.sliding ? max(0, q0 - P.window + 1) : 0;
+  const int kt0 = k_lo / KB, kt1 = q_hi / KB;
+
+  const bf16_t* kbase = P.k + ((size_t)b * P.Hkv + kvh) * P.cap * HD;
+  const bf16_t* vbase = P.v + ((size_t)b * P.Hkv + kvh) * P.cap * HD;
+  u32x4_t rk[LD_PER_T], rv[LD_PER_T];
+  auto gload = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LD_PER_T; ++i) {
+      const int c = tid + 256 * i;
+      const int key = min(kt * KB + c / CH, L - 1);
+      const size_t off = (size_t)key * HD + 8 * (c % CH);
+      rk[i] = *reinterpret_cast<const u32x4_t*>(kbase + off);
+      rv[i] = *reinterpret_cast<const u32x4_t*>(vbase + off);
+    }
+  };
+  auto sstore = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LD_PER_T; ++i) {
+      const int c = tid + 256 * i;
+      const int key = c / CH, ch = c % CH;
+      *reinterpret_cast<u32x4_t*>(&Ks[buf][key * KS + 8 * ch]) = rk[i];
+      *reinterpret_cast<u32x4_t*>(&Vs[buf][key * VS + 8 * ch]) = rv[i];
+    }
+  };
+
+  f32x16_t O[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) O[i][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  gload(kt0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = kt0; kt <= kt1; ++kt) {
+    const int cur = (kt - kt0) & 1;
+    if (kt < kt1) gload(kt + 1);
+    const bf16_t* ks_ = Ks[cur];
+    const bf16_t* vs_ = Vs[cur];
+    const int k0 = kt * KB;
+
+    // S^T for 64 keys x 32 queries: two 32-key blocks.
+    f32x16_t S[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[kb][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < QK; ++ks) {
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
+            ks_ + (32 * kb + (lane & 31)) * KS + 16 * ks + 8 * half);
+        S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], S[kb], 0, 0, 0);
+      }
+    }
+    // Mask only tiles that are not entirely visible to every query of the workgroup.
+    const bool full_vis = (k0 + KB - 1 <= q0) && (!P.sliding || k0 >= q0 + QB - P.window);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float s = S[kb][r] * P.scale_log2;
+        if (!full_vis) {
+          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+          const bool vis = key <= qw && (!P.sliding || key > qw - P.window);
+          s = vis ? s : -INFINITY;
+        }
+        S[kb][r] = s;
+        mx = fmaxf(mx, s);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    float rs = 0.f;
+    bf16x8_t pf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float p = exp2f(S[kb][8 * st + t] - m_use);
+          rs += p;
+          pf[kb][st][t] = (__bf16)p;
+        }
+    rs += __shfl_xor(rs, 32, 64);
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) O[i][r] *= alpha;
+
+    // O^T[d, q] += sum_key V[key, d] P[q, key]. The V^T operand comes from two
+    // transpose reads: lane m of each 16-lane group addresses row key0 + m / 4,
+    // columns d0 + 4 (m % 4) .. + 4, and receives V[key0 + j][d0 + lane % 16], j < 4.
+    const int grp = lane >> 4, m16 = lane & 15;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int d0 = 32 * db + 16 * (grp & 1);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int key0 = 32 * kb + 16 * st + 4 * half;
+          const bf16_t* a0 = vs_ + (key0 + (m16 >> 2)) * VS + d0 + 4 * (m16 & 3);
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4_t))a0);
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4_t))(a0 + 8 * VS));
+          const bf16x8_t vf = __builtin_bit_cast(
+              bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][st], O[db], 0, 0, 0);
+        }
+    }
+    if (kt < kt1) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  if (qw >= L) return;
+  const float inv = 1.0f / l_run;
+  bf16_t* op = P.o + ((size_t)b * L + qw) * P.ldo + (size_t)h * HD;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d = 32 * db + 8 * r4 + 4 * half;
+      u32x2_t v;
+      v.x = pack_bf2(O[db][4 * r4 + 0] * inv, O[db][4 * r4 + 1] * inv);
+      v.y = pack_bf2(O[db][4 * r4 + 2] * inv, O[db][4 * r4 + 3] * inv);
+      *reinterpret_cast<u32x2_t*>(op + d) = v;
+    }
+}
+
+// ---------------------------------------------------------------- fp32
+template <int HD>
+__global__ __launch_bounds__(64) void attn_prefill_f32(const float* __restrict__ q,
+                                                       const float* __restrict__ k,
+                                                       const float* __restrict__ v, int Hq, int Hkv,
+                                                       int L, int cap, int sliding, int window,
+                                                       float scale, float* __restrict__ o, int ldo) {
+  constexpr int DPL = (HD + 63) / 64;  // d values per lane in the PV accumulation
+  __shared__ float qs[HD];
+  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+  const int kvh = h / (Hq / Hkv);
+  const float* qp = q + (((size_t)b * Hq + h) * L + i) * HD;
+  for (int d = lane; d < HD; d += 64) qs[d] = qp[d];
+  __syncthreads();
+  const float* kb = k + ((size_t)b * Hkv + kvh) * cap * HD;
+  const float* vb = v + ((size_t)b * Hkv + kvh) * cap * HD;
+  const int lo = sliding ? max(0, i - window + 1) : 0;
+  float m = -INFINITY, l = 0.f, acc[DPL];
+#pragma unroll
+  for (int t = 0; t < DPL; ++t) acc[t] = 0.f;
+  for (int c0 = lo; c0 <= i; c0 += 64) {
+    const int key = c0 + lane;
+    float s = -INFINITY;
+    if (key <= i) {
+      const float* kp = kb + (size_t)key * HD;
+      float dot = 0.f;
+      for (int d = 0; d < HD; ++d) dot = fmaf(qs[d], kp[d], dot);
+      s = dot * scale;
+    }
+    const float m_new = fmaxf(m, wave_max(s));
+    const float alpha = expf(m - m_new);
+    const float p = (key <= i) ? expf(s - m_new) : 0.f;
+    l = l * alpha + wave_sum(p);
+    m = m_new;
+#pragma unroll
+    for (int t = 0; t < DPL; ++t) acc[t] *= alpha;
+    const int n = min(64, i - c0 + 1);
+    for (int j = 0; j < n; ++j) {
+      const float pj = __shfl(p, j, 64);
+      const float* vp = vb + (size_t)(c0 + j) * HD;
+#pragma unroll
+      for (int t = 0; t < DPL; ++t) {
+        const int d = lane + 64 * t;
+        if (d < HD) acc[t] = fmaf(pj, vp[d], acc[t]);
+      }
+    }
+  }
+  float* op = o + ((size_t)b * L + i) * ldo + (size_t)h * HD;
+#pragma unroll
+  for (int t = 0; t < DPL; ++t) {
+    const int d = lane + 64 * t;
+    if (d < HD) op[d] = acc[t] / l;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attention_prefill(int dtype, const void* q, const void* k, const void* v, int B,
+                                    int Hq, int Hkv, int L, int cap, int hd, int sliding, int window,
+                                    void* o, int ldo, hipStream_t s) {
+  if (dtype == 1) {
+    AttnParams P;
+    P.q = (const bf16_t*)q; P.k = (const bf16_t*)k; P.v = (const bf16_t*)v;
+    P.B = B; P.Hq = Hq; P.Hkv = Hkv; P.L = L; P.cap = cap;
+    P.sliding = sliding; P.window = window;
+    P.o = (bf16_t*)o; P.ldo = ldo;
+    P.scale_log2 = kLog2e / sqrtf((float)hd);
+    P.nqb = (L + QB - 1) / QB;
+    const dim3 grid(P.nqb, Hq, B);
+    if (hd == 128) attn_prefill_bf16<128><<<grid, 256, 0, s>>>(P);
+    else attn_prefill_bf16<64><<<grid, 256, 0, s>>>(P);
+  } else {
+    const dim3 grid(L, Hq, B);
+    const float scale = 1.0f / sqrtf((float)hd);
+    if (hd == 128)
+      attn_prefill_f32<128><<<grid, 64, 0, s>>>((const float*)q, (const float*)k, (const float*)v, Hq,
+                                                Hkv, L, cap, sliding, window, scale, (float*)o, ldo);
+    else
+      attn_prefill_f32<64><<<grid, 64, 0, s>>>((const float*)q, (const float*)k, (const float*)v, Hq,
+                                               Hkv, L, cap, sliding, window, scale, (float*)o, ldo);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace compass

@@ -1,0 +1,132 @@
+// Elementwise kernels that finish a GEMM whose sums were written raw (fp32 partial
+// sums over K-slices), used by the decode path and by the fp32 path:
+//   * projection epilogue: interleaved MRoPE on q and k ("Interleaved MRoPE" of the
+//     mlxcel Compass issue: x_j' = x_j cos - x_{j+hd/2} sin, x_{j+hd/2}' = x_{j+hd/2}
+//     cos + x_j sin with angle pos[axis(j)] * inv_freq[j]), q/k/v scatter into the
+//     attention layouts, and act = silu(gate) * up (SwiGLU);
+//   * split-K reduction plus the residual (parallel block: out = x + attn + mlp);
+//   * the deepstack row update h[rows] += ds ("after layers 0, 1, 2").
+// Each thread handles one rotation pair (or one gate/up pair) so that both members
+// of the pair are combined in registers.
+#include "common.h"
+#include "launch.h"
+
+namespace compass {
+namespace {
+
+template <typename T>
+__global__ __launch_bounds__(256) void proj_epilogue_kernel(const float* __restrict__ raw, int splits,
+                                                            int M, int N, ProjEpi E, RopeTable rt) {
+  const int hd = E.hd, half = hd >> 1;
+  const int qkv_units = (E.Hq + 2 * E.Hkv) * half;
+  const int units = qkv_units + E.I;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long long)M * units) return;
+  const int m = (int)(idx / units);
+  const int u = (int)(idx - (long long)m * units);
+  const size_t slab = (size_t)M * N;
+  auto sum = [&](int c) {
+    float s = 0.f;
+    for (int z = 0; z < splits; ++z) s += raw[z * slab + (size_t)m * N + c];
+    return s;
+  };
+  int b, l;
+  if (E.decode) {
+    b = m; l = E.lens[b];
+    if (l < 0 || l >= E.cap) return;
+  } else {
+    b = m / E.L; l = m - b * E.L;
+  }
+  if (u >= qkv_units) {
+    const int c = u - qkv_units;                                   // gate/up column
+    const int vg = (E.nq64 + 2 * E.nk64) * 64 + (c >> 6) * 128 + (c & 63);  // virtual gate col
+    const float g = sum(vg), up = sum(vg + 64);
+    T* act = (T*)E.act;
+    act[(size_t)m * E.ldact + E.act_col0 + c] = Elt<T>::from_f(silu_f(g) * up);
+    return;
+  }
+  const int hh = u / half, f = u - hh * half;
+  const int c1 = hh * hd + f;
+  float x1 = sum(c1), x2 = sum(c1 + half);
+  T* dst;
+  if (hh < E.Hq) {
+    dst = (T*)E.q + (((size_t)b * E.Hq + hh) * E.Lq + (E.decode ? 0 : l)) * hd;
+  } else {
+    const int kv = hh - E.Hq;
+    const bool isk = kv < E.Hkv;
+    const int head = isk ? kv : kv - E.Hkv;
+    dst = (T*)(isk ? E.kc : E.vc) + (((size_t)b * E.Hkv + head) * E.cap + l) * hd;
+  }
+  if (E.rope && hh < E.Hq + E.Hkv) {
+    const float p = (float)E.pos[(size_t)rope_axis(rt, f) * E.pos_stride + m];
+    float sn, cs;
+    sincosf(p * rope_inv_freq(rt, f, hd), &sn, &cs);
+    const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
+    x1 = y1; x2 = y2;
+  }
+  dst[f] = Elt<T>::from_f(x1);
+  dst[f + half] = Elt<T>::from_f(x2);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void splitk_resid_kernel(const float* __restrict__ raw, int splits,
+                                                           int M, int N, const T* x, T* out,
+                                                           const int32_t* __restrict__ lens, int cap) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long long)M * N) return;
+  if (lens) {  // decode: rows whose cache index is out of range are left untouched
+    const int l = lens[idx / N];
+    if (l < 0 || l >= cap) return;
+  }
+  float s = Elt<T>::to_f(x[idx]);
+  for (int z = 0; z < splits; ++z) s += raw[(size_t)z * M * N + idx];
+  out[idx] = Elt<T>::from_f(s);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void deepstack_kernel(const int32_t* __restrict__ rows,
+                                                        const T* __restrict__ ds, int D, int n_rows,
+                                                        T* out) {
+  const int r = blockIdx.x;
+  const int row = rows[r];
+  if (row < 0 || row >= n_rows) return;
+  for (int c = blockIdx.y * 256 + threadIdx.x; c < D; c += gridDim.y * 256) {
+    T* o = out + (size_t)row * D + c;
+    *o = Elt<T>::from_f(Elt<T>::to_f(*o) + Elt<T>::to_f(ds[(size_t)r * D + c]));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_proj_epilogue(int dtype, const float* raw, int splits, int M, int N,
+                                const ProjEpi& ep, const RopeTable& rt, hipStream_t s) {
+  const long long units = (long long)M * ((ep.Hq + 2 * ep.Hkv) * (ep.hd / 2) + ep.I);
+  const dim3 grid((unsigned)((units + 255) / 256));
+  if (dtype == 1) proj_epilogue_kernel<bf16_t><<<grid, 256, 0, s>>>(raw, splits, M, N, ep, rt);
+  else proj_epilogue_kernel<float><<<grid, 256, 0, s>>>(raw, splits, M, N, ep, rt);
+  return hipGetLastError();
+}
+
+hipError_t launch_splitk_resid(int dtype, const float* raw, int splits, int M, int N, const void* x,
+                               void* out, const int32_t* lens, int cap, hipStream_t s) {
+  const long long n = (long long)M * N;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (dtype == 1)
+    splitk_resid_kernel<bf16_t><<<grid, 256, 0, s>>>(raw, splits, M, N, (const bf16_t*)x, (bf16_t*)out, lens, cap);
+  else
+    splitk_resid_kernel<float><<<grid, 256, 0, s>>>(raw, splits, M, N, (const float*)x, (float*)out, lens, cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_deepstack(int dtype, const int32_t* rows, const void* ds, int n_ds, int D,
+                            int n_rows, void* out, hipStream_t s) {
+  if (n_ds <= 0) return hipSuccess;
+  const dim3 grid(n_ds, (D + 255) / 256);
+  if (dtype == 1)
+    deepstack_kernel<bf16_t><<<grid, 256, 0, s>>>(rows, (const bf16_t*)ds, D, n_rows, (bf16_t*)out);
+  else
+    deepstack_kernel<float><<<grid, 256, 0, s>>>(rows, (const float*)ds, D, n_rows, (float*)out);
+  return hipGetLastError();
+}
+
+}  // namespace compass

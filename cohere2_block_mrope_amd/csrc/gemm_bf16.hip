@@ -1,0 +1,415 @@
+// bf16 GEMMs on gfx950 MFMA (v_mfma_f32_32x32x16_bf16, fp32 accumulation):
+//   C[m, n] = sum_k A[m, k] * B[n, k]    (A [M, K] and B [N, K] both K-contiguous)
+//
+// One kernel template serves the four GEMMs of the layer:
+//   PROJ   the fused q/k/v/gate/up projection of "Text decoder forward" (mlxcel
+//          Compass issue). Its epilogue applies interleaved MRoPE to q and k in
+//          registers, scatters q to [B, Hq, L, hd], k/v to the cache [B, Hkv, cap, hd],
+//          and writes act = silu(gate) * up (SwiGLU);
+//   RESID  the output GEMM [o | act] . [Wo | Wd]^T plus the residual x (parallel
+//          block: h + attn + mlp);
+//   SCALED the tied-embedding logits times logit_scale, stored as fp32;
+//   RAW    fp32 partial sums over a K-slice (split-K for skinny decode GEMMs).
+//
+// Tiling: a 256-thread workgroup (4 waves, 2 x 2) computes a BM x BN tile; each wave
+// owns a (BM/2) x (BN/2) sub-tile of 32 x 32 MFMA blocks. K advances in steps of 64
+// through a double-buffered LDS stage (A and B tiles, 16-byte chunks XOR-swizzled by
+// row so that the fragment reads of 8 consecutive rows hit distinct banks); the next
+// step's global loads are in flight while the current step's MFMAs run.
+//
+// MFMA lane layout (checked on gfx950): operand lane l holds row (l % 32) and
+// k = 8 * (l / 32) .. + 8; result register r of lane l holds
+// C[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32].
+//
+// The fused MRoPE epilogue needs the pair (x_j, x_{j + hd/2}) in one lane: with
+// BN = 256 each wave owns 128 consecutive columns aligned to a head (hd = 128) or to
+// two heads (hd = 64), so for hd = 128 block j and block j + 2 hold the two halves of
+// the same rows in the same lane and register. Gate and up come in 64-column chunk
+// pairs (see BMap kind 1), so silu(gate) * up is also a same-lane, same-register op.
+#include "common.h"
+#include "launch.h"
+
+namespace compass {
+namespace {
+
+enum { MODE_PROJ = 0, MODE_RESID = 1, MODE_SCALED = 2, MODE_RAW = 3 };
+
+struct GemmParams {
+  const bf16_t* A;
+  int lda, M, K, N;
+  BMap bm;
+  int kchunk;        // K elements per split (RAW)
+  int tiles_m, tiles_n;
+  float* raw;        // RAW
+  const bf16_t* x;   // RESID
+  bf16_t* out;
+  int ldo;
+  float* outf;       // SCALED
+  long long ldof;
+  float scale;
+  ProjEpi ep;        // PROJ
+  RopeTable rt;
+};
+
+constexpr int BK = 64;
+
+__device__ __forceinline__ int swz(int row, int chunk) { return (row << 6) + ((chunk ^ (row & 7)) << 3); }
+
+// Workgroup id -> (tile_m, tile_n). Consecutive workgroup ids go round-robin over the
+// 8 XCDs; ids are first regrouped so that each XCD gets a contiguous range of logical
+// tiles, and logical tiles are ordered in column groups of GROUP_M row-tiles so that
+// the tiles resident on one XCD at a time share A rows and B rows in its L2.
+template <int GROUP_M>
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int nwg = tiles_m * tiles_n;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, local = bid >> 3;
+  const int per = nwg >> 3, extra = nwg & 7;
+  const int logical = xcd * per + min(xcd, extra) + local;
+  const int group = logical / (GROUP_M * tiles_n);
+  const int first_m = group * GROUP_M;
+  const int gsize = min(tiles_m - first_m, GROUP_M);
+  const int in_group = logical - group * GROUP_M * tiles_n;
+  tm = first_m + in_group % gsize;
+  tn = in_group / gsize;
+}
+
+__device__ __forceinline__ void store_bf16(bf16_t* p, float v) { *p = f2bf(v); }
+
+template <int BM, int BN, int MODE, int BKIND>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams P) {
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int MB = WM / 32, NB = WN / 32;
+  constexpr int A_PER_T = BM / 32, B_PER_T = BN / 32;  // 16-byte chunks per thread per stage
+  extern __shared__ __align__(16) bf16_t smem[];
+  bf16_t* As = smem;                 // [2][BM * 64]
+  bf16_t* Bs = smem + 2 * BM * BK;   // [2][BN * 64]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  int tm, tn;
+  if (MODE == MODE_RAW) { tm = blockIdx.x % P.tiles_m; tn = blockIdx.x / P.tiles_m; }
+  else tile_coords<8>(P.tiles_m, P.tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  int kbeg = 0, kend = P.K;
+  if (MODE == MODE_RAW) {
+    kbeg = blockIdx.z * P.kchunk;
+    kend = min(P.K, kbeg + P.kchunk);
+  }
+
+  // Operand loading: wave w stages rows w * (ROWS / 4) + (lane >> 3) + 8 i of each tile
+  // (16-byte chunk lane & 7 of each row), so one wave's B rows always sit inside one
+  // 64-row chunk of the virtual B operand: a wave-uniform base pointer plus 32-bit row
+  // offsets. Rows beyond M / N are clamped to valid rows and never stored.
+  const int lchunk = lane & 7, lsub = lane >> 3;
+  const int arow0 = wave * (BM / 4) + lsub, brow0 = wave * (BN / 4) + lsub;
+  uint32_t aoff[A_PER_T];
+#pragma unroll
+  for (int i = 0; i < A_PER_T; ++i)
+    aoff[i] = (uint32_t)min(m0 + arow0 + 8 * i, P.M - 1) * (uint32_t)P.lda + lchunk * 8;
+  const bf16_t* bbase0;
+  const bf16_t* bbase1 = nullptr;
+  uint32_t boff[B_PER_T];
+  uint32_t boff1[BKIND == 2 ? B_PER_T : 1];
+  if constexpr (BKIND == 1) {
+    // Virtual projection layout: chunk -> (matrix, first row); all rows have stride ld0.
+    const int nch = P.N >> 6;
+    const int ch = min((n0 + wave * (BN / 4)) >> 6, nch - 1);
+    const int qe = P.bm.nq64, ke = qe + P.bm.nk64, ve = ke + P.bm.nk64;
+    const bf16_t* base;
+    int first;
+    if (ch < qe) { base = (const bf16_t*)P.bm.p[0]; first = ch * 64; }
+    else if (ch < ke) { base = (const bf16_t*)P.bm.p[1]; first = (ch - qe) * 64; }
+    else if (ch < ve) { base = (const bf16_t*)P.bm.p[2]; first = (ch - ke) * 64; }
+    else {
+      const int mm = ch - ve;
+      base = (mm & 1) ? (const bf16_t*)P.bm.p[4] : (const bf16_t*)P.bm.p[3];
+      first = (mm >> 1) * 64;
+    }
+    bbase0 = base;
+    const int r0 = first + ((n0 + wave * (BN / 4)) & 63) + lsub;
+#pragma unroll
+    for (int i = 0; i < B_PER_T; ++i) boff[i] = (uint32_t)(r0 + 8 * i) * (uint32_t)P.bm.ld0 + lchunk * 8;
+  } else {
+    bbase0 = (const bf16_t*)P.bm.p[0];
+#pragma unroll
+    for (int i = 0; i < B_PER_T; ++i)
+      boff[i] = (uint32_t)min(n0 + brow0 + 8 * i, P.N - 1) * (uint32_t)P.bm.ld0 + lchunk * 8;
+    if constexpr (BKIND == 2) {
+      bbase1 = (const bf16_t*)P.bm.p[1] - P.bm.ksplit;
+#pragma unroll
+      for (int i = 0; i < B_PER_T; ++i)
+        boff1[i] = (uint32_t)min(n0 + brow0 + 8 * i, P.N - 1) * (uint32_t)P.bm.ld1 + lchunk * 8;
+    }
+  }
+
+  u32x4_t ra[A_PER_T], rb[B_PER_T];
+  auto gload = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < A_PER_T; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(P.A + aoff[i] + k0);
+    if (BKIND == 2 && k0 >= P.bm.ksplit) {
+#pragma unroll
+      for (int i = 0; i < B_PER_T; ++i) rb[i] = *reinterpret_cast<const u32x4_t*>(bbase1 + boff1[i] + k0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < B_PER_T; ++i) rb[i] = *reinterpret_cast<const u32x4_t*>(bbase0 + boff[i] + k0);
+    }
+  };
+  auto sstore = [&](int buf) __attribute__((always_inline)) {
+    bf16_t* a = As + buf * BM * BK;
+    bf16_t* b = Bs + buf * BN * BK;
+#pragma unroll
+    for (int i = 0; i < A_PER_T; ++i)
+      *reinterpret_cast<u32x4_t*>(a + swz(arow0 + 8 * i, lchunk)) = ra[i];
+#pragma unroll
+    for (int i = 0; i < B_PER_T; ++i)
+      *reinterpret_cast<u32x4_t*>(b + swz(brow0 + 8 * i, lchunk)) = rb[i];
+  };
+
+  f32x16_t acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = (kend - kbeg) / BK;
+  if (nk > 0) {
+    gload(kbeg);
+    sstore(0);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload(kbeg + (kt + 1) * BK);
+    const bf16_t* a = As + cur * BM * BK;
+    const bf16_t* b = Bs + cur * BN * BK;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8_t fa[MB], fb[NB];
+      const int c = 2 * ks + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int r = wm * WM + 32 * i + (lane & 31);
+        fa[i] = *reinterpret_cast<const bf16x8_t*>(a + swz(r, c));
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int r = wn * WN + 32 * j + (lane & 31);
+        fb[j] = *reinterpret_cast<const bf16x8_t*>(b + swz(r, c));
+      }
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ------------------------------------------------------------------ epilogues
+  const int col_l = lane & 31;
+  const int row_l = 4 * (lane >> 5);
+  if constexpr (MODE == MODE_RAW || MODE == MODE_RESID || MODE == MODE_SCALED) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int n = n0 + wn * WN + 32 * j + col_l;
+        if (n >= P.N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm * WM + 32 * i + 8 * (r >> 2) + row_l + (r & 3);
+          if (m >= P.M) continue;
+          const float v = acc[i][j][r];
+          if constexpr (MODE == MODE_RAW) {
+            P.raw[((size_t)blockIdx.z * P.M + m) * P.N + n] = v;
+          } else if constexpr (MODE == MODE_RESID) {
+            const size_t o = (size_t)m * P.ldo + n;
+            P.out[o] = f2bf(bf2f(P.x[o]) + v);
+          } else {
+            P.outf[(size_t)m * P.ldof + n] = v * P.scale;
+          }
+        }
+      }
+  } else {
+    // MODE_PROJ: requires WN == 128 (BN == 256); see the header comment.
+    static_assert(MODE != MODE_PROJ || WN == 128, "fused projection epilogue needs 128-column waves");
+    const ProjEpi& E = P.ep;
+    const int nw0 = n0 + wn * WN;
+    if (nw0 >= P.N) return;
+    const int ch0 = nw0 >> 6;
+    const int qe = E.nq64, ke = qe + E.nk64, ve = ke + E.nk64;
+    const int hd = E.hd;
+    if (ch0 >= ve) {
+      // SwiGLU: chunk ch0 is gate columns, ch0 + 1 the up columns of the same c.
+      const int cbase = ((ch0 - ve) >> 1) * 64;
+      bf16_t* act = (bf16_t*)E.act;
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm * WM + 32 * i + 8 * (r >> 2) + row_l + (r & 3);
+          if (m >= P.M) continue;
+          bf16_t* dst = act + (size_t)m * E.ldact + E.act_col0 + cbase + col_l;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const float g = acc[i][j][r], u = acc[i][j + 2][r];
+            dst[32 * j] = f2bf(silu_f(g) * u);
+          }
+        }
+      return;
+    }
+    // q / k / v heads. For hd == 128 the wave holds one head: halves are blocks {0,1}
+    // and {2,3}. For hd == 64 it holds two heads: blocks {0,1} and {2,3}.
+    // This lane's frequencies: col_l (+ 32 for hd == 128).
+    float invf[2];
+    int axf[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int f = 32 * j + col_l;
+      invf[j] = rope_inv_freq(P.rt, f, hd);
+      axf[j] = rope_axis(P.rt, f);
+    }
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      if (hd == 128 && hf == 1) break;
+      const int ch = ch0 + hf;  // first chunk of this head
+      int kind, head;
+      if (ch < qe) { kind = 0; head = ch * 64 / hd; }
+      else if (ch < ke) { kind = 1; head = (ch - qe) * 64 / hd; }
+      else { kind = 2; head = (ch - ke) * 64 / hd; }
+      const int half = hd >> 1;
+      const bool rot = E.rope && kind < 2;
+      // Blocks of this head: jlo .. jlo + hd/32 - 1; partner of block j is j + half/32.
+      const int jlo = (hd == 128) ? 0 : 2 * hf;
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm * WM + 32 * i + 8 * (r >> 2) + row_l + (r & 3);
+          if (m >= P.M) continue;
+          int b, l;
+          if (E.decode) { b = m; l = E.lens[b]; } else { b = m / E.L; l = m - b * E.L; }
+          bf16_t* dst;
+          if (kind == 0) dst = (bf16_t*)E.q + (((size_t)b * E.Hq + head) * E.Lq + (E.decode ? 0 : l)) * hd;
+          else dst = (bf16_t*)(kind == 1 ? E.kc : E.vc) + (((size_t)b * E.Hkv + head) * E.cap + l) * hd;
+          if (hd == 128) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              float x1 = acc[i][j][r], x2 = acc[i][j + 2][r];
+              const int f = 32 * j + col_l;
+              if (rot) {
+                const float p = (float)E.pos[(size_t)axf[j] * E.pos_stride + m];
+                float sn, cs;
+                sincosf(p * invf[j], &sn, &cs);
+                const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
+                x1 = y1; x2 = y2;
+              }
+              dst[f] = f2bf(x1);
+              dst[f + half] = f2bf(x2);
+            }
+          } else {
+            float x1 = acc[i][jlo][r], x2 = acc[i][jlo + 1][r];
+            const int f = col_l;
+            if (rot) {
+              const float p = (float)E.pos[(size_t)axf[0] * E.pos_stride + m];
+              float sn, cs;
+              sincosf(p * invf[0], &sn, &cs);
+              const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
+              x1 = y1; x2 = y2;
+            }
+            dst[f] = f2bf(x1);
+            dst[f + half] = f2bf(x2);
+          }
+        }
+    }
+  }
+}
+
+template <int BM, int BN, int MODE, int BKIND>
+hipError_t launch(const GemmParams& P, dim3 grid, hipStream_t s) {
+  constexpr size_t lds = (size_t)2 * (BM + BN) * BK * sizeof(bf16_t);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<BM, BN, MODE, BKIND>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  gemm_bf16_kernel<BM, BN, MODE, BKIND><<<grid, 256, lds, s>>>(P);
+  return hipGetLastError();
+}
+
+GemmParams base_params(const void* A, int lda, int M, int K, const BMap& bm, int N) {
+  GemmParams P{};
+  P.A = (const bf16_t*)A;
+  P.lda = lda; P.M = M; P.K = K; P.N = N;
+  P.bm = bm;
+  P.kchunk = K;
+  return P;
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16_proj(const void* A, int lda, int M, int K, const BMap& bm, int N,
+                                 const ProjEpi& ep, const RopeTable& rt, hipStream_t s) {
+  GemmParams P = base_params(A, lda, M, K, bm, N);
+  P.ep = ep;
+  P.rt = rt;
+  P.tiles_m = (M + 255) / 256;
+  P.tiles_n = (N + 255) / 256;
+  return launch<256, 256, MODE_PROJ, 1>(P, dim3(P.tiles_m * P.tiles_n), s);
+}
+
+hipError_t launch_gemm_bf16_resid(const void* A, int lda, int M, int K, const BMap& bm, int N,
+                                  const void* x, void* out, int ldo, hipStream_t s) {
+  GemmParams P = base_params(A, lda, M, K, bm, N);
+  P.x = (const bf16_t*)x;
+  P.out = (bf16_t*)out;
+  P.ldo = ldo;
+  // Pick the tile so the grid covers the 256 CUs: 256 x 256 when that gives at least
+  // 256 tiles, else 128 x 256.
+  const long long t256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
+  if (t256 >= 256) {
+    P.tiles_m = (M + 255) / 256; P.tiles_n = (N + 255) / 256;
+    return bm.kind == 2 ? launch<256, 256, MODE_RESID, 2>(P, dim3(P.tiles_m * P.tiles_n), s)
+                        : launch<256, 256, MODE_RESID, 0>(P, dim3(P.tiles_m * P.tiles_n), s);
+  }
+  P.tiles_m = (M + 127) / 128; P.tiles_n = (N + 255) / 256;
+  return bm.kind == 2 ? launch<128, 256, MODE_RESID, 2>(P, dim3(P.tiles_m * P.tiles_n), s)
+                      : launch<128, 256, MODE_RESID, 0>(P, dim3(P.tiles_m * P.tiles_n), s);
+}
+
+hipError_t launch_gemm_bf16_scaled_f32(const void* A, int lda, int M, int K, const BMap& bm, int N,
+                                       float scale, float* out, long long ldo, hipStream_t s) {
+  GemmParams P = base_params(A, lda, M, K, bm, N);
+  P.outf = out;
+  P.ldof = ldo;
+  P.scale = scale;
+  P.tiles_m = (M + 255) / 256;
+  P.tiles_n = (N + 255) / 256;
+  return launch<256, 256, MODE_SCALED, 0>(P, dim3(P.tiles_m * P.tiles_n), s);
+}
+
+hipError_t launch_gemm_bf16_raw(const void* A, int lda, int M, int K, const BMap& bm, int N,
+                                int splits, float* raw, hipStream_t s) {
+  GemmParams P = base_params(A, lda, M, K, bm, N);
+  P.raw = raw;
+  const int kc = ((K / splits + BK - 1) / BK) * BK;
+  P.kchunk = kc;
+  P.tiles_m = (M + 63) / 64;
+  P.tiles_n = (N + 63) / 64;
+  const dim3 grid(P.tiles_m * P.tiles_n, 1, splits);
+  switch (bm.kind) {
+    case 1: return launch<64, 64, MODE_RAW, 1>(P, grid, s);
+    case 2: return launch<64, 64, MODE_RAW, 2>(P, grid, s);
+    default: return launch<64, 64, MODE_RAW, 0>(P, grid, s);
+  }
+}
+
+}  // namespace compass

@@ -1,0 +1,120 @@
+// Host-side launcher declarations and the small structs passed to kernels by value.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace compass {
+
+// MRoPE parameters. Frequency j < head_dim / 2 has inverse frequency
+// theta^(-2j / head_dim) (evaluated in double, rounded once to fp32) and uses axis
+// h when j % 3 == 1 and j < sh3 (= 3 * s_h), axis w when j % 3 == 2 and j < sw3
+// (= 3 * s_w), axis t otherwise.
+struct RopeTable {
+  float theta;
+  int sh3, sw3;
+};
+
+#ifdef __HIPCC__
+__device__ __forceinline__ float rope_inv_freq(const RopeTable& rt, int f, int hd) {
+  return (float)pow((double)rt.theta, -2.0 * (double)f / (double)hd);
+}
+__device__ __forceinline__ int rope_axis(const RopeTable& rt, int f) {
+  const int r = f % 3;
+  return (r == 1 && f < rt.sh3) ? 1 : (r == 2 && f < rt.sw3) ? 2 : 0;
+}
+#endif
+
+// Where row n of the virtual B operand ([N, K], K contiguous) lives.
+//  kind 0: one matrix p[0] with row stride ld0.
+//  kind 1: the fused projection. N is split in 64-row chunks: nq64 chunks of wq,
+//          nk64 of wk, nk64 of wv, then 2*I/64 chunks alternating w_gate / w_up
+//          (chunk 2c -> gate rows [64c, 64c+64), chunk 2c+1 -> up rows of the same c).
+//          All five matrices have row stride ld0 (= D).
+//  kind 2: concatenation along K: columns k < ksplit come from p[0] (stride ld0),
+//          columns k >= ksplit from p[1] (stride ld1) at k - ksplit.
+struct BMap {
+  int kind;
+  const void* p[5];
+  int ld0, ld1;
+  int ksplit;
+  int nq64, nk64;
+};
+
+// Destinations of the projection epilogue (q/k/v with MRoPE, KV write, SwiGLU).
+struct ProjEpi {
+  int decode;           // 0: row m is (b = m / L, l = m % L); 1: row m is b = m, l = lens[b]
+  int L;
+  const int32_t* pos;   // prefill [3, B, L]; decode [3, B]; NULL when rope == 0
+  int pos_stride;       // distance between the t, h, w planes (B*L or B)
+  int rope;             // 1: rotate q and k
+  int Hq, Hkv, hd;
+  void* q;              // [B, Hq, Lq, hd]
+  int Lq;
+  void* kc;             // [B, Hkv, cap, hd]
+  void* vc;
+  int cap;
+  const int32_t* lens;  // decode: cache index of the new token, per row
+  void* act;            // act[m * ldact + act_col0 + c] = silu(gate) * up
+  int ldact;
+  int act_col0;
+  int nq64, nk64;
+  int I;
+};
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_positions(const int32_t* tok, int B, int L, int image_id, const int32_t* grid,
+                            const int32_t* img_off, int merge, int32_t* pos, int32_t* delta,
+                            int32_t* status, hipStream_t s);
+
+// a = LN(x) over rows [rows, D]; dtype 1 = bf16, 0 = f32 (a has the dtype of x).
+hipError_t launch_layernorm(int dtype, const void* x, const void* w, float eps, void* a, int rows,
+                            int D, hipStream_t s);
+
+// bf16 MFMA GEMMs, C[m, n] = sum_k A[m, k] * B[n, k], A [M, lda] bf16.
+// Fused projection epilogue (MRoPE, q/k/v scatter, SwiGLU); N = virtual projection width.
+hipError_t launch_gemm_bf16_proj(const void* A, int lda, int M, int K, const BMap& bm, int N,
+                                 const ProjEpi& ep, const RopeTable& rt, hipStream_t s);
+// out[m, n] = x[m, n] + C (bf16; out may alias x).
+hipError_t launch_gemm_bf16_resid(const void* A, int lda, int M, int K, const BMap& bm, int N,
+                                  const void* x, void* out, int ldo, hipStream_t s);
+// out[m, n] = C * scale (fp32).
+hipError_t launch_gemm_bf16_scaled_f32(const void* A, int lda, int M, int K, const BMap& bm, int N,
+                                       float scale, float* out, long long ldo, hipStream_t s);
+// raw[z][m][n] = partial C over K-slice z (fp32), splits slices of K.
+hipError_t launch_gemm_bf16_raw(const void* A, int lda, int M, int K, const BMap& bm, int N,
+                                int splits, float* raw, hipStream_t s);
+
+// fp32 GEMM (VALU), same contract as launch_gemm_bf16_raw with fp32 operands; every
+// stored sum is multiplied by `scale` (1 for raw partials).
+hipError_t launch_gemm_f32_raw(const void* A, int lda, int M, int K, const BMap& bm, int N,
+                               int splits, float* raw, float scale, hipStream_t s);
+
+// Projection epilogue over raw fp32 partial sums [splits][M][N].
+hipError_t launch_proj_epilogue(int dtype, const float* raw, int splits, int M, int N,
+                                const ProjEpi& ep, const RopeTable& rt, hipStream_t s);
+// out[m, n] = x[m, n] + sum_z raw[z][m][n]; with lens != NULL (decode), rows m whose
+// lens[m] is outside [0, cap) are skipped.
+hipError_t launch_splitk_resid(int dtype, const float* raw, int splits, int M, int N, const void* x,
+                               void* out, const int32_t* lens, int cap, hipStream_t s);
+
+// Prefill attention: q [B, Hq, L, hd]; k, v [B, Hkv, cap, hd]; o written to
+// o[(b*L + l) * ldo + h*hd + d].
+hipError_t launch_attention_prefill(int dtype, const void* q, const void* k, const void* v, int B,
+                                    int Hq, int Hkv, int L, int cap, int hd, int sliding, int window,
+                                    void* o, int ldo, hipStream_t s);
+
+// Decode attention, split over key chunks, then combine.
+int decode_chunk_keys(int dtype, int hd);
+hipError_t launch_decode_attention(int dtype, const void* q, const void* k, const void* v,
+                                   const int32_t* lens, int B, int Hq, int Hkv, int cap, int hd,
+                                   int sliding, int window, int n_chunks, float* part,
+                                   hipStream_t s);
+hipError_t launch_decode_combine(int dtype, const float* part, const int32_t* lens, int B, int Hq,
+                                 int cap, int hd, int n_chunks, void* o, int ldo, hipStream_t s);
+
+// out[rows[r]] += ds[r], rows outside [0, n_rows) skipped.
+hipError_t launch_deepstack(int dtype, const int32_t* rows, const void* ds, int n_ds, int D,
+                            int n_rows, void* out, hipStream_t s);
+
+}  // namespace compass

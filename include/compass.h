@@ -1,0 +1,200 @@
+/*
+ * compass.h — C ABI of the MI355X (gfx950) Compass/Cohere2 parallel decoder layer.
+ *
+ * The layer is the one the mlxcel issue "feat(vlm): add Cohere Compass /
+ * North-Micro-Vision (cohere_compass) VLM" defines in its section "Text decoder
+ * forward": one weight-only LayerNorm a = LN(h) feeds an attention branch and a
+ * SwiGLU branch, and h + attn(a) + mlp(a) is the output (parallel block, no
+ * post-attention norm). Sliding-window layers rotate q and k with interleaved
+ * three-axis MRoPE (section "Interleaved MRoPE"); full-attention layers use no
+ * positional encoding. The stack alternates them 3:1 and ends with a tied
+ * embedding head times logit_scale.
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless stated otherwise; the caller owns every
+ *     buffer (inputs, outputs, caches, workspace). Nothing here allocates, frees
+ *     or synchronizes device memory (the profiling helpers at the end excepted).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls
+ *     enqueue their kernels on it and return immediately.
+ *   - Return value: COMPASS_OK (0) or a negative compass_status. Argument checks
+ *     happen on the host before anything is enqueued: on an error nothing runs
+ *     and compass_last_error() returns a message (thread-local, valid until the
+ *     next call on that thread). No C++ exception crosses this interface.
+ *   - Tensors are contiguous, row-major, and 16-byte aligned. Dtype is
+ *     COMPASS_BF16 (bf16 storage, fp32 accumulation) or COMPASS_F32 throughout a
+ *     call: x, out, weights, KV cache and deepstack rows share the dtype.
+ *   - Supported widths: head_dim in {64, 128}; hidden, intermediate and
+ *     n_q_heads*head_dim multiples of 64; (n_q_heads + 2*n_kv_heads)*head_dim a
+ *     multiple of 128; n_q_heads a multiple of n_kv_heads. Others return
+ *     COMPASS_E_UNSUPPORTED.
+ */
+#ifndef COMPASS_H
+#define COMPASS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  COMPASS_OK = 0,
+  COMPASS_E_INVALID = -1,      /* null pointer, non-positive size, inconsistent shape */
+  COMPASS_E_UNSUPPORTED = -2,  /* valid but outside the widths/dtypes listed above */
+  COMPASS_E_ALIGN = -3,        /* a tensor pointer is not 16-byte aligned */
+  COMPASS_E_WORKSPACE = -4,    /* workspace missing or smaller than the size query says */
+  COMPASS_E_DEVICE = -5        /* the HIP runtime reported an error at launch */
+} compass_status;
+
+typedef enum { COMPASS_F32 = 0, COMPASS_BF16 = 1 } compass_dtype;
+typedef enum { COMPASS_SLIDING = 0, COMPASS_FULL = 1 } compass_kind;
+
+/* Status words written by compass_mrope_positions (device, one per call). */
+enum {
+  COMPASS_POS_OK = 0,
+  COMPASS_POS_SPAN_MISMATCH = 1,  /* an image's pad span runs past L or meets a non-pad token */
+  COMPASS_POS_EXTRA_PADS = 2,     /* pad tokens remain but the row has no image left */
+  COMPASS_POS_UNUSED_IMAGES = 3,  /* the row ends with images not consumed */
+  COMPASS_POS_BAD_GRID = 4,       /* a grid entry < 1, or h / w not divisible by the merge size */
+  COMPASS_POS_TOO_MANY_IMAGES = 5 /* more than COMPASS_MAX_IMAGES_PER_ROW images in a row */
+};
+#define COMPASS_MAX_IMAGES_PER_ROW 2048
+
+/* One decoder layer's shape (host struct).
+ * kind: COMPASS_SLIDING applies MRoPE and the window; COMPASS_FULL uses no
+ *   positional encoding and a plain causal mask ("Text decoder forward").
+ * window: sliding layers only; key j is visible to query i iff i - window < j <= i
+ *   (the last `window` keys, the query's own key included). Must be >= 1.
+ * mrope_section: {s_t, s_h, s_w} frequency counts, sum == head_dim / 2. Frequency j
+ *   uses axis h when j % 3 == 1 and j < 3*s_h, axis w when j % 3 == 2 and j < 3*s_w,
+ *   axis t otherwise ("Interleaved MRoPE"; [24, 20, 20] on the real model).
+ * rope_theta: MRoPE base (50000 on the real model); inv_freq[j] = theta^(-2j/head_dim).
+ * ln_eps: LayerNorm epsilon (the value is not printed by the page; callers pass it). */
+typedef struct {
+  int32_t hidden;        /* D */
+  int32_t n_q_heads;     /* Hq */
+  int32_t n_kv_heads;    /* Hkv; query head h reads kv head h / (Hq / Hkv) */
+  int32_t head_dim;      /* hd */
+  int32_t intermediate;  /* I, SwiGLU width */
+  int32_t kind;          /* compass_kind */
+  int32_t window;
+  int32_t mrope_section[3];
+  float rope_theta;
+  float ln_eps;
+  int32_t dtype;         /* compass_dtype */
+} compass_layer_desc;
+
+/* Weights of one layer, nn.Linear layout [out, in], no biases (section "Weight keys":
+ * input_layernorm.weight, self_attn.{q,k,v,o}_proj.weight, mlp.{gate,up,down}_proj.weight). */
+typedef struct {
+  const void *ln_w;    /* [D] */
+  const void *wq;      /* [Hq*hd, D] */
+  const void *wk;      /* [Hkv*hd, D] */
+  const void *wv;      /* [Hkv*hd, D] */
+  const void *wo;      /* [D, Hq*hd] */
+  const void *w_gate;  /* [I, D] */
+  const void *w_up;    /* [I, D] */
+  const void *w_down;  /* [D, I] */
+} compass_layer_weights;
+
+/* Dense KV cache of one layer (the page's correction under "Acceptance criteria":
+ * a dense cache with the window applied as a mask). Keys are stored AFTER MRoPE on
+ * sliding layers. The library never advances `lens`; the caller does, once per
+ * decode step, after all layers have run. */
+typedef struct {
+  void *k;              /* [B, Hkv, capacity, hd] */
+  void *v;              /* [B, Hkv, capacity, hd] */
+  int32_t capacity;
+  const int32_t *lens;  /* device [B]: tokens already cached (decode only; prefill ignores it) */
+} compass_kv;
+
+/* Position ids, section "Position ids (get_rope_index)" of the mlxcel issue: text
+ * tokens advance (t, h, w) by one; image k with patch grid (t, h, w) and merge m
+ * takes the next t*(h/m)*(w/m) image-pad tokens, which get start + (t_i, h_i, w_i)
+ * on the merged grid; the next text token starts at max(position) + 1;
+ * rope_delta[b] = max position + 1 - L. Integer arithmetic, bit-exact.
+ *   token_ids  [B, L] int32     grid_thw [n_img, 3] int32 (patch units, images in
+ *   row order)    img_offset [B+1] int32: images of row b are [img_offset[b],
+ *   img_offset[b+1])    pos out [3, B, L] int32    rope_delta out [B] int32
+ *   status out [B] int32: COMPASS_POS_* per row, the first error a left-to-right walk
+ *   over the row's tokens meets (read it after the stream has synchronized); for a
+ *   failing row, pos and rope_delta of that row are left unwritten.
+ * Decode positions are lens[b] + rope_delta[b] on all three axes (caller computes). */
+int compass_mrope_positions(const int32_t *token_ids, int32_t B, int32_t L,
+                            int32_t image_token_id, const int32_t *grid_thw,
+                            const int32_t *img_offset, int32_t spatial_merge,
+                            int32_t *pos, int32_t *rope_delta, int32_t *status,
+                            void *stream);
+
+/* Bytes of device workspace compass_layer_prefill (L > 1, or decode == 0) or
+ * compass_layer_decode (decode != 0, L ignored) needs for this shape; `capacity`
+ * is the KV capacity (decode) and is ignored for prefill. Returns 0 for an
+ * invalid or unsupported descriptor. */
+size_t compass_workspace_size(const compass_layer_desc *d, int32_t B, int32_t L,
+                              int32_t capacity, int32_t decode);
+
+/* Prefill of one layer over B rows of L tokens (the "Text decoder forward" loop body):
+ *   out = x + o_proj(attn(MRoPE(q), MRoPE(k), v)) + down(silu(gate(a)) * up(a)),
+ *   a = LN(x), then out[ds_rows[r]] += ds[r] (deepstack, "after layers 0, 1, 2").
+ *   x    [B, L, D]           pos [3, B, L] int32 (sliding only; may be NULL for FULL)
+ *   kv   optional (NULL = keep K/V in the workspace): K/V of rows [0, L) are written
+ *        to kv->k / kv->v (capacity >= L)
+ *   ds_rows [n_ds] int32 flattened row indices b*L + l, distinct; ds [n_ds, D];
+ *        n_ds == 0 (pointers may be NULL) for no deepstack. Rows outside [0, B*L)
+ *        are skipped.
+ *   out  [B, L, D]; may alias x exactly (in-place residual update).
+ *   workspace: compass_workspace_size(d, B, L, 0, 0) bytes, 256-byte aligned. */
+int compass_layer_prefill(const compass_layer_desc *d, const compass_layer_weights *w,
+                          int32_t B, int32_t L, const void *x, const int32_t *pos,
+                          const compass_kv *kv, const int32_t *ds_rows, const void *ds,
+                          int32_t n_ds, void *out, void *workspace, size_t ws_bytes,
+                          void *stream);
+
+/* One decode step of one layer: one new token per row.
+ *   x [B, D]; pos [3, B] int32 (lens[b] + rope_delta[b] on every axis; unread for FULL)
+ *   kv (required): the new token's K/V are written at index lens[b]; keys
+ *   max(0, lens[b] - window + 1) .. lens[b] (sliding) or 0 .. lens[b] (full) are
+ *   attended. Requires 0 <= lens[b] < capacity (rows violating it are skipped
+ *   and their output left unwritten).
+ *   out [B, D]; may alias x.
+ *   workspace: compass_workspace_size(d, B, 1, kv->capacity, 1) bytes. */
+int compass_layer_decode(const compass_layer_desc *d, const compass_layer_weights *w,
+                         int32_t B, const void *x, const int32_t *pos, const compass_kv *kv,
+                         void *out, void *workspace, size_t ws_bytes, void *stream);
+
+/* Tied-embedding head ("Text decoder forward": h = LayerNorm(h); logits =
+ * embed_tokens.as_linear(h) * logit_scale), with the scale applied as the last fp32
+ * operation on each logit (the in-place fp32 footer of the C-Kernel-Engine page,
+ * section "1. Cohere2 Command R").
+ *   h [R, D] (dtype)   norm_w [D]   embed [V, D] (dtype)   logits out [R, V] fp32
+ *   workspace: compass_logits_workspace_size(R, D, dtype) bytes. */
+size_t compass_logits_workspace_size(int32_t R, int32_t D, int32_t dtype);
+int compass_logits(int32_t R, int32_t D, int32_t V, int32_t dtype, const void *h,
+                   const void *norm_w, float ln_eps, const void *embed, float logit_scale,
+                   float *logits, void *workspace, size_t ws_bytes, void *stream);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char *compass_last_error(void);
+
+/* Library version string (host). */
+const char *compass_version(void);
+
+/* Kernel timing with HIP events (host side; for measurement only).
+ * compass_profile_enable(1) makes every later launch record a start/stop event pair
+ * on its own stream; compass_profile_enable(0) stops recording. compass_profile_read
+ * synchronizes the recorded events and returns, for kernels whose name equals
+ * `kernel` (or all kernels if `kernel` is NULL), the launch count and the summed
+ * duration in milliseconds. compass_profile_reset drops all records. The event pool
+ * holds COMPASS_PROFILE_MAX launches; later launches are not recorded. */
+#define COMPASS_PROFILE_MAX 65536
+int compass_profile_enable(int on);
+int compass_profile_reset(void);
+int compass_profile_read(const char *kernel, int64_t *count, double *total_ms);
+/* Name of the i-th distinct kernel name recorded so far (NULL past the end). */
+const char *compass_profile_kernel_name(int32_t i);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* COMPASS_H */

@@ -1,0 +1,109 @@
+"""Shared plumbing for the GPU parity tests: seeded inputs as torch tensors, calls
+through the C ABI (ctypes binding), and the error metrics the gates use."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from synth import bf16_round
+from synth.workloads import LayerShape
+
+DEV = "cuda"
+
+
+def B():
+    from cohere2_block_mrope_amd import binding
+    return binding
+
+
+def tdtype(shape: LayerShape):
+    return torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+
+
+def cdtype(shape: LayerShape) -> int:
+    return 1 if shape.dtype == "bf16" else 0
+
+
+def desc(shape: LayerShape):
+    b = B()
+    return b.make_desc(shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.intermediate,
+                       b.COMPASS_SLIDING if shape.kind == "sliding" else b.COMPASS_FULL,
+                       shape.window if shape.kind == "sliding" else 0, shape.mrope_section, shape.rope_theta,
+                       shape.ln_eps, cdtype(shape))
+
+
+def to_dev(a: np.ndarray, dtype) -> torch.Tensor:
+    """Exact transfer: bf16 inputs are already bf16-representable fp32 values."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV).to(dtype)
+
+
+def weights_to_dev(shape: LayerShape, w: dict) -> dict:
+    return {k: to_dev(v, tdtype(shape)) for k, v in w.items()}
+
+
+def ints_to_dev(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
+
+
+def workspace(nbytes: int) -> torch.Tensor:
+    # 256-byte aligned (the caching allocator aligns to at least 512 bytes).
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=DEV)
+
+
+def run_prefill(shape: LayerShape, wdev: dict, x: torch.Tensor, pos, kv=None, ds_rows=None, ds=None,
+                out=None, stream=None):
+    b = B()
+    d = desc(shape)
+    Bn, L = x.shape[0], x.shape[1]
+    ws = workspace(b.compass_workspace_size(d, Bn, L, 0, 0))
+    out = torch.empty_like(x) if out is None else out
+    kvs = None if kv is None else b.make_kv(kv[0], kv[1])
+    b.compass_layer_prefill(d, b.make_weights(wdev), x, pos, kvs, ds_rows, ds, out, ws, stream)
+    return out
+
+
+def run_decode(shape: LayerShape, wdev: dict, x: torch.Tensor, pos, kc, vc, lens, out=None, stream=None):
+    b = B()
+    d = desc(shape)
+    Bn = x.shape[0]
+    ws = workspace(b.compass_workspace_size(d, Bn, 1, kc.shape[2], 1))
+    out = torch.empty_like(x) if out is None else out
+    b.compass_layer_decode(d, b.make_weights(wdev), x, pos, b.make_kv(kc, vc, lens), out, ws, stream)
+    return out
+
+
+def run_logits(h: torch.Tensor, norm_w, eps: float, embed, scale: float, dtype: int, logits=None):
+    b = B()
+    R, D = h.shape
+    ws = workspace(b.compass_logits_workspace_size(R, D, dtype))
+    logits = torch.empty(R, embed.shape[0], dtype=torch.float32, device=DEV) if logits is None else logits
+    b.compass_logits(h, norm_w, eps, embed, scale, logits, ws, dtype)
+    return logits
+
+
+def np64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def rel_err(got, ref) -> float:
+    """max |got - ref| / max |ref| over the compared set."""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
+
+
+def tol(shape: LayerShape) -> float:
+    """Gates: 2e-2 for bf16 storage, 1e-4 for fp32."""
+    return 2e-2 if shape.dtype == "bf16" else 1e-4
+
+
+def small_shape(dtype="bf16", kind="sliding", hd=128, Hq=4, Hkv=1, D=256, I=512, window=48, section=None):
+    if section is None:
+        section = (24, 20, 20) if hd == 128 else (12, 10, 10)
+    return LayerShape(hidden=D, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=hd, intermediate=I, kind=kind,
+                      window=window, mrope_section=section, dtype=dtype)
+
+
+def rand_np(seed: int, shape_tuple, std=1.0, mean=0.0, bf16=True) -> np.ndarray:
+    from synth import normal
+    v = normal(seed, int(np.prod(shape_tuple)), std=std, mean=mean).reshape(shape_tuple)
+    return bf16_round(v) if bf16 else v

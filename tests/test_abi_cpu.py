@@ -1,0 +1,163 @@
+"""The C-ABI library loads, exports every symbol include/compass.h declares, and its
+host-side argument checks return the documented codes (no GPU needed: every
+failing call here is rejected before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "compass.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(compass_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def b():
+    from cohere2_block_mrope_amd import binding
+    return binding
+
+
+def test_header_symbols_exported(b):
+    lib = ctypes.CDLL(b.LIB_PATH)
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in compass.h but not exported"
+    assert set(names) == set(b.EXPORTED)
+
+
+def compass_shape(b, **kw):
+    args = dict(hidden=2048, n_q_heads=16, n_kv_heads=4, head_dim=128, intermediate=8192,
+                kind=b.COMPASS_SLIDING, window=1024, mrope_section=(24, 20, 20), rope_theta=50000.0,
+                ln_eps=1e-5, dtype=b.COMPASS_BF16)
+    args.update(kw)
+    return b.make_desc(**args)
+
+
+def test_workspace_sizes(b):
+    d = compass_shape(b)
+    T, D, qd, K2 = 4096, 2048, 2048, 10240
+    need = 2 * (T * D + T * qd + 2 * 4 * 4096 * 128 + T * K2)
+    got = b.compass_workspace_size(d, 1, 4096, 0, 0)
+    assert need <= got <= need + 8 * 256
+    assert b.compass_workspace_size(d, 64, 1, 8200, 1) > 0
+    assert b.compass_workspace_size(compass_shape(b, head_dim=96), 1, 16, 0, 0) == 0
+    assert b._lib.compass_workspace_size(None, 1, 1, 0, 0) == 0
+    assert b.compass_logits_workspace_size(4096, 2048, b.COMPASS_BF16) == 4096 * 2048 * 2
+    assert b.compass_logits_workspace_size(0, 2048, 1) == 0
+
+
+class FakePtr:
+    """Stands in for a tensor: only data_ptr() is read by the binding on these paths."""
+    def __init__(self, p, shape=(1, 16, 2048), n=1 << 40, esz=1):
+        self.p, self.shape, self.n, self.esz = p, shape, n, esz
+
+    def data_ptr(self):
+        return self.p
+
+    def numel(self):
+        return self.n
+
+    def element_size(self):
+        return self.esz
+
+
+def weights(b, p=0x10000):
+    return b.make_weights({k: FakePtr(p + 0x1000 * i) for i, k in enumerate(
+        ["ln_w", "wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"])})
+
+
+CASES = [
+    ("head_dim 96", dict(head_dim=96), "UNSUPPORTED"),
+    ("heads not grouped", dict(n_q_heads=6), "INVALID"),
+    ("group of 16", dict(n_q_heads=64), "UNSUPPORTED"),
+    ("hidden not /64", dict(hidden=2000), "UNSUPPORTED"),
+    ("section sum", dict(mrope_section=(24, 20, 21)), "INVALID"),
+    ("section not interleavable", dict(mrope_section=(4, 30, 30)), "INVALID"),
+    ("window 0", dict(window=0), "INVALID"),
+    ("dtype 7", dict(dtype=7), "UNSUPPORTED"),
+    ("kind 2", dict(kind=2), "INVALID"),
+    ("eps nan", dict(ln_eps=float("nan")), "INVALID"),
+    ("odd head mix", dict(n_q_heads=3, n_kv_heads=1, head_dim=64), "UNSUPPORTED"),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", CASES, ids=[c[0] for c in CASES])
+def test_descriptor_rejected_before_launch(b, name, kw, code):
+    d = compass_shape(b, **kw)
+    x = FakePtr(0x100000)
+    with pytest.raises(b.CompassError) as e:
+        b.compass_layer_prefill(d, weights(b), x, FakePtr(0x200000), None, None, None, FakePtr(0x300000),
+                                FakePtr(0x400000), stream=0)
+    assert e.value.code == getattr(b, "COMPASS_E_" + code)
+    assert b.compass_last_error()
+
+
+def test_argument_errors(b):
+    d = compass_shape(b)
+    x, out, ws = FakePtr(0x100000), FakePtr(0x300000), FakePtr(0x400000)
+    pos = FakePtr(0x200000)
+    call = lambda **k: b.compass_layer_prefill(d, k.get("w", weights(b)), k.get("x", x), k.get("pos", pos),
+                                               k.get("kv"), None, None, k.get("out", out), k.get("ws", ws), stream=0)
+    with pytest.raises(b.CompassError) as e:
+        call(pos=None)
+    assert e.value.code == b.COMPASS_E_INVALID
+    with pytest.raises(b.CompassError) as e:
+        call(x=FakePtr(0x100008))
+    assert e.value.code == b.COMPASS_E_ALIGN
+    with pytest.raises(b.CompassError) as e:
+        call(w=weights(b, 0x10004))
+    assert e.value.code == b.COMPASS_E_ALIGN
+    with pytest.raises(b.CompassError) as e:
+        call(ws=FakePtr(0x400000, n=1024))
+    assert e.value.code == b.COMPASS_E_WORKSPACE
+    with pytest.raises(b.CompassError) as e:
+        call(out=FakePtr(0x100000 + 4096))  # partial overlap with x
+    assert e.value.code == b.COMPASS_E_INVALID
+    kv = b.compass_kv()
+    kv.k, kv.v, kv.capacity = 0x500000, 0x600000, 8
+    with pytest.raises(b.CompassError) as e:
+        call(kv=kv)  # capacity 8 < L = 16
+    assert e.value.code == b.COMPASS_E_INVALID
+
+
+def test_decode_and_logits_argument_errors(b):
+    d = compass_shape(b)
+    x = FakePtr(0x100000, shape=(4, 2048))
+    with pytest.raises(b.CompassError) as e:
+        b.compass_layer_decode(d, weights(b), x, FakePtr(0x200000), b.compass_kv(), FakePtr(0x300000),
+                               FakePtr(0x400000), stream=0)
+    assert e.value.code == b.COMPASS_E_INVALID
+    h = FakePtr(0x100000, shape=(16, 2048))
+    emb = FakePtr(0x800000, shape=(1000, 2048))
+    with pytest.raises(b.CompassError) as e:
+        b.compass_logits(h, FakePtr(0x200000), 1e-5, emb, 0.25, FakePtr(0x300000), FakePtr(0x400000, n=16), 1,
+                         stream=0)
+    assert e.value.code == b.COMPASS_E_WORKSPACE
+    h2 = FakePtr(0x100000, shape=(16, 2000))
+    with pytest.raises(b.CompassError) as e:
+        b.compass_logits(h2, FakePtr(0x200000), 1e-5, emb, 0.25, FakePtr(0x300000), FakePtr(0x400000), 1, stream=0)
+    assert e.value.code == b.COMPASS_E_UNSUPPORTED
+
+
+def test_positions_argument_errors(b):
+    tok = FakePtr(0x100000, shape=(2, 0))
+    with pytest.raises(b.CompassError) as e:
+        b.compass_mrope_positions(tok, 255031, FakePtr(0x1000), FakePtr(0x2000), 2, FakePtr(0x3000),
+                                  FakePtr(0x4000), FakePtr(0x5000), stream=0)
+    assert e.value.code == b.COMPASS_E_INVALID
+    tok = FakePtr(0x100000, shape=(2, 5))
+    with pytest.raises(b.CompassError) as e:
+        b.compass_mrope_positions(tok, 255031, FakePtr(0x1000), FakePtr(0x2000), 0, FakePtr(0x3000),
+                                  FakePtr(0x4000), FakePtr(0x5000), stream=0)
+    assert e.value.code == b.COMPASS_E_INVALID
+
+
+def test_version(b):
+    assert "gfx950" in b.compass_version()

@@ -1,0 +1,290 @@
+"""GPU parity at small sizes: every entry point of the C ABI against the fp64 oracle.
+
+Sizes span several tiles and a ragged tail; inputs are seeded (synth). Gates:
+positions bit-exact; layer outputs, K/V cache rows and logits within 2e-2 (bf16)
+or 1e-4 (fp32) as max|gpu - oracle| / max|oracle|. Layer outputs are also gated on
+the branch sum out - x, allowing for the bf16 rounding of out itself.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import compass_oracle as O
+from synth import workloads as W
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+def mixed_tokens(B, L, seed):
+    """Rows with text, images of a few grids (including back-to-back images) and text."""
+    toks, grids, offs = [], [], [0]
+    layouts = [[(3, (1, 4, 6)), (2, (2, 4, 4)), (0, (1, 2, 2))], [(7, (1, 8, 12))], [], [(0, (1, 6, 2))]]
+    for b in range(B):
+        row = list(W.text_tokens(seed + b, L))
+        p = 0
+        for gap, g in layouts[b % len(layouts)]:
+            p += gap
+            n = g[0] * (g[1] // 2) * (g[2] // 2)
+            if p + n > L:
+                break
+            row[p:p + n] = [W.IMAGE_TOKEN_ID] * n
+            grids.append(g)
+            p += n
+        toks.append(row)
+        offs.append(len(grids))
+    return (np.array(toks, np.int32), np.array(grids, np.int32).reshape(-1, 3), np.array(offs, np.int32))
+
+
+# ------------------------------------------------------------------------------ positions
+def gpu_positions(tok, grid, off, merge=2):
+    b = H.B()
+    Bn, L = tok.shape
+    pos = torch.full((3, Bn, L), -7, dtype=torch.int32, device="cuda")
+    delta = torch.full((Bn,), -7, dtype=torch.int32, device="cuda")
+    status = torch.full((Bn,), -7, dtype=torch.int32, device="cuda")
+    g = H.ints_to_dev(grid if len(grid) else np.zeros((1, 3), np.int32))
+    b.compass_mrope_positions(H.ints_to_dev(tok), W.IMAGE_TOKEN_ID, g, H.ints_to_dev(off), merge, pos, delta, status)
+    torch.cuda.synchronize()
+    return pos.cpu().numpy(), delta.cpu().numpy(), status.cpu().numpy()
+
+
+@pytest.mark.parametrize("B,L", [(1, 1), (2, 37), (4, 300), (3, 2500)])
+def test_positions_bit_exact(B, L):
+    tok, grid, off = mixed_tokens(B, L, seed=L)
+    pos, delta, status = gpu_positions(tok, grid, off)
+    ref_pos, ref_delta = O.mrope_positions(tok, W.IMAGE_TOKEN_ID, grid, off, 2)
+    assert np.all(status == 0)
+    assert np.array_equal(pos, ref_pos)
+    assert np.array_equal(delta, ref_delta)
+
+
+def test_positions_c1_layout_bit_exact():
+    tok, grid, off = W.c1_tokens(seed=5)
+    pos, delta, status = gpu_positions(tok, grid, off)
+    ref_pos, ref_delta = O.mrope_positions(tok, W.IMAGE_TOKEN_ID, grid, off, 2)
+    assert status.tolist() == [0]
+    assert np.array_equal(pos, ref_pos) and np.array_equal(delta, ref_delta)
+    assert delta[0] == -992
+
+
+@pytest.mark.parametrize("case", ["short_span", "extra_pads", "unused_image", "bad_grid", "span_past_end"])
+def test_positions_error_codes(case):
+    n = 4
+    I = W.IMAGE_TOKEN_ID
+    rows = {
+        "short_span": ([[1] + [I] * (n - 1) + [2, 3]], [[1, 4, 4]]),
+        "extra_pads": ([[1] + [I] * (n + 1) + [2]], [[1, 4, 4]]),
+        "unused_image": ([[1] + [I] * n + [2]], [[1, 4, 4], [1, 2, 2]]),
+        "bad_grid": ([[1] + [I] * n + [2]], [[1, 3, 4]]),
+        "span_past_end": ([[1, 2] + [I] * (n - 1)], [[1, 4, 4]]),
+    }
+    tok, grid = rows[case]
+    tok = np.array(tok, np.int32)
+    grid = np.array(grid, np.int32)
+    # Row 1 is a clean text row: its status must stay 0 and its positions exact.
+    tok2 = np.concatenate([tok, np.arange(10, 10 + tok.shape[1], dtype=np.int32)[None]], 0)
+    off = np.array([0, len(grid), len(grid)], np.int32)
+    _, _, status = gpu_positions(tok2, grid, off)
+    with pytest.raises(O.PositionError) as e:
+        O.mrope_positions(tok, I, grid, np.array([0, len(grid)]), 2)
+    assert status.tolist() == [e.value.code, 0]
+
+
+# ------------------------------------------------------------------------------ prefill
+def layer_case(shape, Bn, L, seed, wstd=0.06):
+    w = {}
+    r = np.random.default_rng(seed)
+    base = W.make_layer_weights(shape, 100 + seed % 50, seed)
+    for k, v in base.items():  # rescale the N(0, 0.02) weights so both branches are sizeable
+        w[k] = v if k == "ln_w" else (H.bf16_round(v * (wstd / 0.02)) if shape.dtype == "bf16" else v * (wstd / 0.02))
+    x = H.rand_np(seed + 1, (Bn, L, shape.hidden), bf16=shape.dtype == "bf16")
+    tok, grid, off = mixed_tokens(Bn, L, seed)
+    pos, _ = O.mrope_positions(tok, W.IMAGE_TOKEN_ID, grid, off, 2)
+    return w, x, pos
+
+
+def check_layer_out(shape, out_gpu, x, ref, what=""):
+    g = H.np64(out_gpu)
+    e_out = H.rel_err(g, ref)
+    assert e_out <= H.tol(shape), f"{what} out rel err {e_out:.3e}"
+    d_ref = ref - x
+    d_gpu = g - x
+    rounding = (2.0 ** -8 if shape.dtype == "bf16" else 2.0 ** -23) * np.abs(ref)
+    excess = np.abs(d_gpu - d_ref) - rounding
+    e_delta = float(np.max(excess) / np.max(np.abs(d_ref)))
+    assert e_delta <= H.tol(shape), f"{what} branch-sum rel err {e_delta:.3e}"
+    return e_out, e_delta
+
+
+PREFILL_CASES = [
+    # dtype, kind, hd, Hq, Hkv, D, I, window, B, L
+    ("f32", "sliding", 64, 4, 1, 256, 1024, 32, 1, 128),     # the fp32 parity workload's shape
+    ("f32", "full", 128, 4, 2, 256, 512, 0, 2, 77),
+    ("bf16", "sliding", 128, 4, 1, 256, 512, 48, 2, 200),
+    ("bf16", "full", 128, 4, 1, 256, 512, 0, 2, 200),
+    ("bf16", "sliding", 64, 8, 2, 256, 512, 100, 1, 333),
+    ("bf16", "full", 64, 8, 4, 512, 256, 0, 1, 130),
+    ("bf16", "sliding", 128, 8, 1, 512, 1024, 1, 1, 70),    # window of one key
+    ("bf16", "sliding", 128, 2, 2, 256, 256, 5000, 1, 257),  # window >= L
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_prefill_parity(case):
+    dt, kind, hd, Hq, Hkv, D, I, win, Bn, L = case
+    sh = H.small_shape(dt, kind, hd, Hq, Hkv, D, I, win)
+    w, x, pos = layer_case(sh, Bn, L, seed=hd + Hq + L)
+    ref, st = O.layer_prefill(sh, w, x, pos, return_stages=True)
+    td = H.tdtype(sh)
+    wd = H.weights_to_dev(sh, w)
+    xd = H.to_dev(x, td)
+    posd = H.ints_to_dev(pos)
+    cap = L + 3
+    kc = torch.full((Bn, Hkv, cap, hd), float("nan"), dtype=td, device="cuda")
+    vc = torch.full_like(kc, float("nan"))
+    out = H.run_prefill(sh, wd, xd, posd, kv=(kc, vc))
+    torch.cuda.synchronize()
+    check_layer_out(sh, out, x, ref)
+    assert H.rel_err(H.np64(kc[:, :, :L]), st["k"]) <= H.tol(sh)
+    assert H.rel_err(H.np64(vc[:, :, :L]), st["v"]) <= H.tol(sh)
+    assert torch.isnan(kc[:, :, L:]).all()  # rows past L untouched
+
+
+def test_prefill_in_place_and_deepstack():
+    sh = H.small_shape("bf16", "sliding", 128, 4, 1, 256, 512, 40)
+    Bn, L = 2, 150
+    w, x, pos = layer_case(sh, Bn, L, seed=7)
+    rows = np.array([3, 4, 5, 160, 299], np.int32)
+    ds = H.rand_np(99, (len(rows), sh.hidden))
+    ref = O.layer_prefill(sh, w, x, pos, rows, ds)
+    xd = H.to_dev(x, torch.bfloat16)
+    H.run_prefill(sh, H.weights_to_dev(sh, w), xd, H.ints_to_dev(pos), ds_rows=H.ints_to_dev(rows),
+                  ds=H.to_dev(ds, torch.bfloat16), out=xd)
+    torch.cuda.synchronize()
+    check_layer_out(sh, xd, x, ref)
+
+
+def test_full_layer_position_relabel_bitwise():
+    sh = H.small_shape("bf16", "full", 128, 4, 1, 256, 512, 0)
+    Bn, L = 2, 190
+    w, x, pos = layer_case(sh, Bn, L, seed=11)
+    perm = np.stack([np.stack([np.random.default_rng(3 * b + a).permutation(pos[a, b]) for b in range(Bn)])
+                     for a in range(3)])
+    wd, xd = H.weights_to_dev(sh, w), H.to_dev(x, torch.bfloat16)
+    o1 = H.run_prefill(sh, wd, xd, H.ints_to_dev(pos))
+    o2 = H.run_prefill(sh, wd, xd, H.ints_to_dev(perm))
+    o3 = H.run_prefill(sh, wd, xd, None)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(o1, o3)
+
+
+def test_window_at_least_L_equals_full_causal_without_rope_difference():
+    """W >= L: the sliding layer equals the same layer with a plain causal mask (same rope)."""
+    sh = H.small_shape("bf16", "sliding", 128, 4, 1, 256, 512, 300)
+    Bn, L = 1, 300
+    w, x, pos = layer_case(sh, Bn, L, seed=12)
+    wd, xd, pd = H.weights_to_dev(sh, w), H.to_dev(x, torch.bfloat16), H.ints_to_dev(pos)
+    o1 = H.run_prefill(sh, wd, xd, pd)
+    import dataclasses
+    o2 = H.run_prefill(dataclasses.replace(sh, window=10 ** 6), wd, xd, pd)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+# ------------------------------------------------------------------------------ decode
+DECODE_CASES = [
+    ("bf16", "sliding", 128, 4, 1, 256, 512, 40),
+    ("bf16", "full", 128, 4, 1, 256, 512, 0),
+    ("bf16", "sliding", 64, 8, 2, 256, 512, 300),
+    ("f32", "sliding", 64, 4, 1, 256, 1024, 32),
+    ("f32", "full", 128, 4, 2, 256, 512, 0),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_decode_parity(case):
+    dt, kind, hd, Hq, Hkv, D, I, win = case
+    sh = H.small_shape(dt, kind, hd, Hq, Hkv, D, I, win)
+    bf = dt == "bf16"
+    lens = np.array([0, 1, 37, 255, 256, 257, 600, 1000], np.int32)
+    Bn, cap = len(lens), 1003
+    w, _, _ = layer_case(sh, 1, 8, seed=hd + Hq)
+    x = H.rand_np(5, (Bn, D), bf16=bf)
+    kc = H.rand_np(6, (Bn, Hkv, cap, hd), bf16=bf)
+    vc = H.rand_np(7, (Bn, Hkv, cap, hd), bf16=bf)
+    delta = np.array([0, -3, 5, -992, 0, 17, -200, 1], np.int64)
+    pos = O.decode_positions(lens, delta)
+    ref, knew, vnew = O.layer_decode(sh, w, x, pos, kc, vc, lens)
+    td = H.tdtype(sh)
+    kd, vd = H.to_dev(kc, td), H.to_dev(vc, td)
+    out = H.run_decode(sh, H.weights_to_dev(sh, w), H.to_dev(x, td), H.ints_to_dev(pos), kd, vd,
+                       H.ints_to_dev(lens))
+    torch.cuda.synchronize()
+    e = H.rel_err(H.np64(out), ref)
+    assert e <= H.tol(sh), e
+    kg, vg = H.np64(kd), H.np64(vd)
+    for i, n in enumerate(lens):
+        assert H.rel_err(kg[i, :, n], knew[i]) <= H.tol(sh)
+        assert H.rel_err(vg[i, :, n], vnew[i]) <= H.tol(sh)
+    # Every other cache row is untouched.
+    mask = np.ones((Bn, cap), bool)
+    mask[np.arange(Bn), lens] = False
+    assert np.array_equal(kg.transpose(0, 2, 1, 3)[mask], kc.transpose(0, 2, 1, 3)[mask])
+
+
+def test_decode_skips_rows_with_lens_out_of_range():
+    sh = H.small_shape("bf16", "sliding", 128, 4, 1, 256, 512, 40)
+    lens = np.array([5, 64, 63], np.int32)  # capacity 64: row 1 is out of range
+    Bn, cap = 3, 64
+    w, _, _ = layer_case(sh, 1, 8, seed=3)
+    x = H.rand_np(5, (Bn, sh.hidden))
+    kc = H.rand_np(6, (Bn, 1, cap, 128))
+    vc = H.rand_np(7, (Bn, 1, cap, 128))
+    pos = O.decode_positions(lens, np.zeros(Bn, np.int64))
+    out = torch.full((Bn, sh.hidden), 7.0, dtype=torch.bfloat16, device="cuda")
+    kd, vd = H.to_dev(kc, torch.bfloat16), H.to_dev(vc, torch.bfloat16)
+    H.run_decode(sh, H.weights_to_dev(sh, w), H.to_dev(x, torch.bfloat16), H.ints_to_dev(pos), kd, vd,
+                 H.ints_to_dev(lens), out=out)
+    torch.cuda.synchronize()
+    assert torch.all(out[1] == 7.0)
+    assert np.array_equal(H.np64(kd[1]), kc[1])
+    ref, _, _ = O.layer_decode(sh, w, x, pos, kc, vc, lens, rows=[0, 2])
+    assert H.rel_err(H.np64(out[[0, 2]]), ref) <= 2e-2
+
+
+def test_prefill_then_decode_matches_longer_prefill():
+    """Row L-1 of prefill(L) equals decode of token L-1 over the cache prefill(L-1) wrote."""
+    for kind in ("sliding", "full"):
+        sh = H.small_shape("bf16", kind, 128, 4, 1, 256, 512, 50)
+        Bn, L = 2, 130
+        w, x, pos = layer_case(sh, Bn, L, seed=21)
+        wd = H.weights_to_dev(sh, w)
+        cap = L + 5
+        kc = torch.zeros((Bn, 1, cap, 128), dtype=torch.bfloat16, device="cuda")
+        vc = torch.zeros_like(kc)
+        xd = H.to_dev(x, torch.bfloat16)
+        full = H.run_prefill(sh, wd, xd, H.ints_to_dev(pos))
+        H.run_prefill(sh, wd, xd[:, :L - 1].contiguous(), H.ints_to_dev(pos[:, :, :L - 1]), kv=(kc, vc))
+        lens = torch.full((Bn,), L - 1, dtype=torch.int32, device="cuda")
+        dec = H.run_decode(sh, wd, xd[:, L - 1].contiguous(), H.ints_to_dev(pos[:, :, L - 1]), kc, vc, lens)
+        torch.cuda.synchronize()
+        assert H.rel_err(H.np64(dec), H.np64(full[:, L - 1])) <= 2e-2
+
+
+# ------------------------------------------------------------------------------ logits
+@pytest.mark.parametrize("dt,R,D,V", [("bf16", 37, 256, 1000), ("bf16", 300, 512, 2048), ("f32", 20, 256, 517)])
+def test_logits_parity_and_scale(dt, R, D, V):
+    bf = dt == "bf16"
+    h = H.rand_np(31, (R, D), bf16=bf)
+    nw = H.rand_np(32, (D,), std=0.02, mean=1.0, bf16=bf)
+    E = H.rand_np(33, (V, D), std=0.02, bf16=bf)
+    td = torch.bfloat16 if bf else torch.float32
+    hd_, nd, Ed = H.to_dev(h, td), H.to_dev(nw, td), H.to_dev(E, td)
+    c = 1 if bf else 0
+    lg = H.run_logits(hd_, nd, 1e-5, Ed, 0.0625, c)
+    l1 = H.run_logits(hd_, nd, 1e-5, Ed, 1.0, c)
+    torch.cuda.synchronize()
+    ref = O.logits(h, nw, 1e-5, E, 0.0625)
+    assert H.rel_err(H.np64(lg), ref) <= (2e-2 if bf else 1e-4)
+    assert torch.equal(lg, l1 * 0.0625)
