@@ -1,0 +1,311 @@
+"""Benchmark of the Compass/Cohere2 parallel decoder layer on one MI355X.
+
+Timed step (the headline): the sliding-layer prefill workload — hidden 2048, 16/4
+heads, head_dim 128, SwiGLU 8192, window 1024, MRoPE [24, 20, 20], one row of 4096
+tokens laid out as 64 text + 1024 image (patch grid 1 x 64 x 64, merge 2) + 3008
+text — i.e. compass_mrope_positions followed by compass_layer_prefill on inputs
+already resident in HBM. value = tokens per second per layer.
+
+Also reported (one JSON line, key "extra"): the full-attention prefill (B=2, L=8192),
+batched decode of a 4-layer 3:1 stack (B=64, cache 8192, window 4096) in us/step,
+and the 4-layer stack prefill with deepstack plus tied 256000-vocab logits.
+
+"roofline" describes the dominant kernel of the headline step (the fused projection
+GEMM): algorithmic flops per launch / its mean launch time from HIP events recorded
+around every launch in the timed region. "cpu_baseline" is the fp64 oracle timed on
+this host on one full layer of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-extra", action="store_true", help="headline workload only")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--only", default=None, help="run one workload: c1|c2|c3|c4 (for profiling)")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_stats(b, names):
+    out = {}
+    for n in names:
+        c, ms = b.compass_profile_read(n)
+        if c:
+            out[n] = {"launches": c, "mean_us": 1e3 * ms / c}
+    return out
+
+
+def timed(fn, steps, warmup, b, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    b.compass_profile_reset()
+    b.compass_profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    b.compass_profile_enable(False)
+    stats = kernel_stats(b, b.compass_profile_kernel_names())
+    return (t1 - t0) / steps, stats
+
+
+# ------------------------------------------------------------------------ workloads
+def setup_c1(H, W, O, torch):
+    from synth.workloads import WORKLOADS
+    cfg = WORKLOADS[1]
+    sh = cfg["shape"]
+    L = cfg["L"]
+    w = W.make_layer_weights(sh, 1, 0)
+    x = W.make_layer_input(sh, 1, L).reshape(1, L, sh.hidden)
+    tok, grid, off = W.c1_tokens(W.stream_seed(1, 0, W.TensorId.TOKENS))
+    return sh, w, x, tok, grid, off
+
+
+def run_c1(args, b, H, W, O, torch):
+    sh, w, x, tok, grid, off = setup_c1(H, W, O, torch)
+    L = x.shape[1]
+    wd = H.weights_to_dev(sh, w)
+    xd = H.to_dev(x, torch.bfloat16)
+    tokd, gridd, offd = H.ints_to_dev(tok), H.ints_to_dev(grid), H.ints_to_dev(off)
+    pos = torch.empty((3, 1, L), dtype=torch.int32, device="cuda")
+    delta = torch.empty((1,), dtype=torch.int32, device="cuda")
+    status = torch.empty((1,), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(xd)
+    d = H.desc(sh)
+    ws = H.workspace(b.compass_workspace_size(d, 1, L, 0, 0))
+    wts = b.make_weights(wd)
+
+    def step():
+        b.compass_mrope_positions(tokd, W.IMAGE_TOKEN_ID, gridd, offd, 2, pos, delta, status)
+        b.compass_layer_prefill(d, wts, xd, pos, None, None, None, out, ws)
+
+    sec, stats = timed(step, args.steps, args.warmup, b, torch)
+    assert int(status.item()) == 0
+    return sh, w, x, tok, grid, off, sec, stats
+
+
+def c1_flops(sh, L):
+    D, Hq, Hkv, hd, I = sh.hidden, sh.n_q_heads, sh.n_kv_heads, sh.head_dim, sh.intermediate
+    nv = (Hq + 2 * Hkv) * hd + 2 * I
+    proj = 2.0 * L * D * nv
+    out = 2.0 * L * (Hq * hd + I) * D
+    pairs = sum(min(i + 1, sh.window) for i in range(L)) if sh.kind == "sliding" else L * (L + 1) / 2
+    attn = 4.0 * pairs * Hq * hd
+    return proj, out, attn
+
+
+def run_c2(args, b, H, W, O, torch):
+    from synth.workloads import WORKLOADS
+    cfg = WORKLOADS[2]
+    sh, Bn, L = cfg["shape"], cfg["B"], cfg["L"]
+    w = W.make_layer_weights(sh, 2, 0)
+    import synth.rng_torch as RT
+    x = RT.normal(W.stream_seed(2, 0, W.TensorId.X), Bn * L * sh.hidden).to(torch.bfloat16).view(Bn, L, sh.hidden)
+    wd = H.weights_to_dev(sh, w)
+    d = H.desc(sh)
+    ws = H.workspace(b.compass_workspace_size(d, Bn, L, 0, 0))
+    out = torch.empty_like(x)
+    wts = b.make_weights(wd)
+    step = lambda: b.compass_layer_prefill(d, wts, x, None, None, None, None, out, ws)
+    sec, stats = timed(step, max(3, args.steps // 4), 2, b, torch)
+    proj, outf, attn = [Bn * f for f in c1_flops(sh, L)]
+    return {"workload": cfg["name"], "tokens_per_s_per_layer": Bn * L / sec, "ms_per_layer": 1e3 * sec,
+            "mfma_frac_layer": (proj + outf + attn) / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "kernels_us": {k: round(v["mean_us"], 1) for k, v in stats.items()}}
+
+
+def run_c3(args, b, H, W, O, torch):
+    from synth.workloads import WORKLOADS, layer_kind
+    import dataclasses
+    import synth.rng_torch as RT
+    cfg = WORKLOADS[3]
+    sh, Bn, n_layers, n = cfg["shape"], cfg["B"], cfg["layers"], cfg["cache_len"]
+    cap = n + 8
+    Hkv, hd = sh.n_kv_heads, sh.head_dim
+    layers = []
+    for i in range(n_layers):
+        shi = dataclasses.replace(sh, kind=layer_kind(i))
+        wd = H.weights_to_dev(shi, W.make_layer_weights(shi, 3, i))
+        kc = RT.normal(W.stream_seed(3, i, W.TensorId.K_CACHE), Bn * Hkv * cap * hd).to(torch.bfloat16).view(Bn, Hkv, cap, hd)
+        vc = RT.normal(W.stream_seed(3, i, W.TensorId.V_CACHE), Bn * Hkv * cap * hd).to(torch.bfloat16).view(Bn, Hkv, cap, hd)
+        d = H.desc(shi)
+        ws = H.workspace(b.compass_workspace_size(d, Bn, 1, cap, 1))
+        layers.append((d, b.make_weights(wd), wd, kc, vc, ws))
+    x = RT.normal(W.stream_seed(3, 0, W.TensorId.X), Bn * sh.hidden).to(torch.bfloat16).view(Bn, sh.hidden)
+    lens = torch.full((Bn,), n, dtype=torch.int32, device="cuda")
+    pos = torch.full((3, Bn), n, dtype=torch.int32, device="cuda")
+    h = torch.empty_like(x)
+
+    def step():
+        h.copy_(x)
+        for d, wts, _, kc, vc, ws in layers:
+            b.compass_layer_decode(d, wts, h, pos, b.make_kv(kc, vc, lens), h, ws)
+
+    sec, stats = timed(step, max(5, args.steps), 3, b, torch)
+    kv_bytes_slide = Bn * Hkv * sh.window * hd * 2 * 2
+    kv_bytes_full = Bn * Hkv * (n + 1) * hd * 2 * 2
+    w_bytes = 2 * (sh.hidden * ((sh.n_q_heads + 2 * Hkv) * hd + 2 * sh.intermediate)
+                   + (sh.n_q_heads * hd + sh.intermediate) * sh.hidden)
+    step_bytes = 3 * kv_bytes_slide + kv_bytes_full + n_layers * w_bytes
+    att = stats.get("decode_attn", {})
+    att_bytes_mean = (3 * kv_bytes_slide + kv_bytes_full) / 4
+    res = {"workload": cfg["name"], "us_per_step": 1e6 * sec, "hbm_frac_step": step_bytes / sec / 1e9 / HBM_PEAK_GBS,
+           "kernels_us": {k: round(v["mean_us"], 1) for k, v in stats.items()}}
+    if att:
+        res["decode_attn_hbm_frac"] = att_bytes_mean / (att["mean_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS
+    return res
+
+
+def run_c4(args, b, H, W, O, torch):
+    from synth.workloads import WORKLOADS, layer_kind
+    import dataclasses
+    import synth.rng_torch as RT
+    cfg = WORKLOADS[4]
+    sh, L, n_layers, V, scale = cfg["shape"], cfg["L"], cfg["layers"], cfg["vocab"], cfg["logit_scale"]
+    tok, grid, off = W.c1_tokens(W.stream_seed(4, 0, W.TensorId.TOKENS))
+    pos_np, _ = O.mrope_positions(tok, W.IMAGE_TOKEN_ID, grid, off, 2)
+    pos = H.ints_to_dev(pos_np)
+    layers = []
+    for i in range(n_layers):
+        shi = dataclasses.replace(sh, kind=layer_kind(i))
+        wd = H.weights_to_dev(shi, W.make_layer_weights(shi, 4, i))
+        layers.append((H.desc(shi), b.make_weights(wd), wd))
+    x = RT.normal(W.stream_seed(4, 0, W.TensorId.X), L * sh.hidden).to(torch.bfloat16).view(1, L, sh.hidden)
+    ds = [RT.normal(W.stream_seed(4, i, W.TensorId.DS + i), 1024 * sh.hidden).to(torch.bfloat16).view(1024, sh.hidden)
+          for i in range(3)]
+    ds_rows = torch.arange(64, 64 + 1024, dtype=torch.int32, device="cuda")
+    E = RT.normal(W.stream_seed(4, 0, W.TensorId.EMBED), V * sh.hidden, std=0.02).to(torch.bfloat16).view(V, sh.hidden)
+    nw = RT.normal(W.stream_seed(4, 0, W.TensorId.FINAL_LN), sh.hidden, std=0.02, mean=1.0).to(torch.bfloat16)
+    ws = H.workspace(max(b.compass_workspace_size(layers[0][0], 1, L, 0, 0),
+                         b.compass_logits_workspace_size(L, sh.hidden, 1)))
+    h = torch.empty_like(x)
+    logits = torch.empty((L, V), dtype=torch.float32, device="cuda")
+
+    def step():
+        h.copy_(x)
+        for i, (d, wts, _) in enumerate(layers):
+            use = i < 3
+            b.compass_layer_prefill(d, wts, h, pos, None, ds_rows if use else None, ds[i] if use else None, h, ws)
+        b.compass_logits(h.view(L, sh.hidden), nw, sh.ln_eps, E, scale, logits, ws, 1)
+
+    sec, stats = timed(step, max(3, args.steps // 4), 2, b, torch)
+    lg = stats.get("gemm_logits", {})
+    res = {"workload": cfg["name"], "ms_per_step": 1e3 * sec,
+           "kernels_us": {k: round(v["mean_us"], 1) for k, v in stats.items()}}
+    if lg:
+        res["logits_mfma_frac"] = 2.0 * L * sh.hidden * V / (lg["mean_us"] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS
+    return res
+
+
+def cpu_baseline(sh, w, x, tok, grid, off, O):
+    import threadpoolctl
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    t0 = time.perf_counter()
+    pos, _ = O.mrope_positions(tok, 255031, grid, off, 2)
+    O.layer_prefill(sh, w, x, pos)
+    sec = time.perf_counter() - t0
+    L = x.shape[1]
+    return {"value": L / sec, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"one full sliding-layer prefill of the headline workload ({L} tokens, positions + layer) in "
+                      f"fp64 numpy on {threads} BLAS threads, {sec:.1f} s"}
+
+
+def traffic_for(kernel_file: str, name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current source of the kernel (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = open(os.path.join(ROOT, "cohere2_block_mrope_amd", "csrc", kernel_file), "rb").read()
+    if rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU layout is a design "
+              f"note, not a measured path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from cohere2_block_mrope_amd import binding as b
+    from oracle import compass_oracle as O
+    from synth import workloads as W
+    from tests import helpers as H
+    torch.cuda.set_device(0)
+
+    res_extra = {}
+    if args.only in (None, "c1"):
+        log("c1: generating inputs")
+        sh, w, x, tok, grid, off, sec, stats = run_c1(args, b, H, W, O, torch)
+        L = x.shape[1]
+        proj, outf, attn = c1_flops(sh, L)
+        gp = stats["gemm_proj"]
+        achieved = proj / (gp["mean_us"] * 1e-6) / 1e12
+        line = {
+            "metric": "prefill tokens/s per layer + decode µs/step; % of MFMA / HBM peak",
+            "value": L / sec, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": 1e3 * sec, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16",
+            "data": "synthetic: seeded N(0,0.02) weights, LayerNorm 1+N(0,0.02), N(0,1) hidden states",
+            "config": {"workload": "sliding-layer prefill: D=2048, 16/4 heads, hd=128, I=8192, window=1024, "
+                                   "MRoPE [24,20,20], B=1, L=4096 (64 text + 1024 image + 3008 text); "
+                                   "step = position ids + one layer",
+                       "global_batch": 1, "seq_len": L, "parallelism": "single GPU"},
+            "layer_mfma_frac": (proj + outf + attn) / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "kernels_us": {k: round(v["mean_us"], 1) for k, v in stats.items()},
+            "roofline": {"kernel": "gemm_proj (fused LN-input q/k/v/gate/up projection + MRoPE/SwiGLU epilogue)",
+                         "bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                         "traffic": traffic_for("gemm_bf16.hip", "gemm_proj_c1"),
+                         "flops_per_launch": proj, "mean_launch_us": gp["mean_us"]},
+        }
+        if not args.no_cpu:
+            log("c1: timing the CPU oracle")
+            line["cpu_baseline"] = cpu_baseline(sh, w, x, tok, grid, off, O)
+        else:
+            line["cpu_baseline"] = None
+    else:
+        line = None
+    if not args.no_extra:
+        for key, fn in (("c2", run_c2), ("c3", run_c3), ("c4", run_c4)):
+            if args.only in (None, key):
+                log(f"{key}: running")
+                res_extra[key] = fn(args, b, H, W, O, torch)
+                torch.cuda.empty_cache()
+    if line is None:
+        print(json.dumps({"extra": res_extra}))
+    else:
+        line["extra"] = res_extra
+        print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
