@@ -26,55 +26,12 @@
 // two heads (hd = 64), so for hd = 128 block j and block j + 2 hold the two halves of
 // the same rows in the same lane and register. Gate and up come in 64-column chunk
 // pairs (see BMap kind 1), so silu(gate) * up is also a same-lane, same-register op.
-#include "common.h"
-#include "launch.h"
+#include "gemm_common.h"
 
 namespace compass {
 namespace {
 
-enum { MODE_PROJ = 0, MODE_RESID = 1, MODE_SCALED = 2, MODE_RAW = 3 };
-
-struct GemmParams {
-  const bf16_t* A;
-  int lda, M, K, N;
-  BMap bm;
-  int kchunk;        // K elements per split (RAW)
-  int tiles_m, tiles_n;
-  float* raw;        // RAW
-  const bf16_t* x;   // RESID
-  bf16_t* out;
-  int ldo;
-  float* outf;       // SCALED
-  long long ldof;
-  float scale;
-  ProjEpi ep;        // PROJ
-  RopeTable rt;
-};
-
-constexpr int BK = 64;
-
-__device__ __forceinline__ int swz(int row, int chunk) { return (row << 6) + ((chunk ^ (row & 7)) << 3); }
-
-// Workgroup id -> (tile_m, tile_n). Consecutive workgroup ids go round-robin over the
-// 8 XCDs; ids are first regrouped so that each XCD gets a contiguous range of logical
-// tiles, and logical tiles are ordered in column groups of GROUP_M row-tiles so that
-// the tiles resident on one XCD at a time share A rows and B rows in its L2.
-template <int GROUP_M>
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int nwg = tiles_m * tiles_n;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7, local = bid >> 3;
-  const int per = nwg >> 3, extra = nwg & 7;
-  const int logical = xcd * per + min(xcd, extra) + local;
-  const int group = logical / (GROUP_M * tiles_n);
-  const int first_m = group * GROUP_M;
-  const int gsize = min(tiles_m - first_m, GROUP_M);
-  const int in_group = logical - group * GROUP_M * tiles_n;
-  tm = first_m + in_group % gsize;
-  tn = in_group / gsize;
-}
-
-__device__ __forceinline__ void store_bf16(bf16_t* p, float v) { *p = f2bf(v); }
+using namespace gemm;
 
 template <int BM, int BN, int MODE, int BKIND>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams P) {
@@ -211,124 +168,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams P) {
     __syncthreads();
   }
 
-  // ------------------------------------------------------------------ epilogues
-  const int col_l = lane & 31;
-  const int row_l = 4 * (lane >> 5);
-  if constexpr (MODE == MODE_RAW || MODE == MODE_RESID || MODE == MODE_SCALED) {
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int n = n0 + wn * WN + 32 * j + col_l;
-        if (n >= P.N) continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm * WM + 32 * i + 8 * (r >> 2) + row_l + (r & 3);
-          if (m >= P.M) continue;
-          const float v = acc[i][j][r];
-          if constexpr (MODE == MODE_RAW) {
-            P.raw[((size_t)blockIdx.z * P.M + m) * P.N + n] = v;
-          } else if constexpr (MODE == MODE_RESID) {
-            const size_t o = (size_t)m * P.ldo + n;
-            P.out[o] = f2bf(bf2f(P.x[o]) + v);
-          } else {
-            P.outf[(size_t)m * P.ldof + n] = v * P.scale;
-          }
-        }
-      }
-  } else {
-    // MODE_PROJ: requires WN == 128 (BN == 256); see the header comment.
-    static_assert(MODE != MODE_PROJ || WN == 128, "fused projection epilogue needs 128-column waves");
-    const ProjEpi& E = P.ep;
-    const int nw0 = n0 + wn * WN;
-    if (nw0 >= P.N) return;
-    const int ch0 = nw0 >> 6;
-    const int qe = E.nq64, ke = qe + E.nk64, ve = ke + E.nk64;
-    const int hd = E.hd;
-    if (ch0 >= ve) {
-      // SwiGLU: chunk ch0 is gate columns, ch0 + 1 the up columns of the same c.
-      const int cbase = ((ch0 - ve) >> 1) * 64;
-      bf16_t* act = (bf16_t*)E.act;
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm * WM + 32 * i + 8 * (r >> 2) + row_l + (r & 3);
-          if (m >= P.M) continue;
-          bf16_t* dst = act + (size_t)m * E.ldact + E.act_col0 + cbase + col_l;
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const float g = acc[i][j][r], u = acc[i][j + 2][r];
-            dst[32 * j] = f2bf(silu_f(g) * u);
-          }
-        }
-      return;
-    }
-    // q / k / v heads. For hd == 128 the wave holds one head: halves are blocks {0,1}
-    // and {2,3}. For hd == 64 it holds two heads: blocks {0,1} and {2,3}.
-    // This lane's frequencies: col_l (+ 32 for hd == 128).
-    float invf[2];
-    int axf[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int f = 32 * j + col_l;
-      invf[j] = rope_inv_freq(P.rt, f, hd);
-      axf[j] = rope_axis(P.rt, f);
-    }
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      if (hd == 128 && hf == 1) break;
-      const int ch = ch0 + hf;  // first chunk of this head
-      int kind, head;
-      if (ch < qe) { kind = 0; head = ch * 64 / hd; }
-      else if (ch < ke) { kind = 1; head = (ch - qe) * 64 / hd; }
-      else { kind = 2; head = (ch - ke) * 64 / hd; }
-      const int half = hd >> 1;
-      const bool rot = E.rope && kind < 2;
-      // Blocks of this head: jlo .. jlo + hd/32 - 1; partner of block j is j + half/32.
-      const int jlo = (hd == 128) ? 0 : 2 * hf;
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm * WM + 32 * i + 8 * (r >> 2) + row_l + (r & 3);
-          if (m >= P.M) continue;
-          int b, l;
-          if (E.decode) { b = m; l = E.lens[b]; } else { b = m / E.L; l = m - b * E.L; }
-          bf16_t* dst;
-          if (kind == 0) dst = (bf16_t*)E.q + (((size_t)b * E.Hq + head) * E.Lq + (E.decode ? 0 : l)) * hd;
-          else dst = (bf16_t*)(kind == 1 ? E.kc : E.vc) + (((size_t)b * E.Hkv + head) * E.cap + l) * hd;
-          if (hd == 128) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              float x1 = acc[i][j][r], x2 = acc[i][j + 2][r];
-              const int f = 32 * j + col_l;
-              if (rot) {
-                const float p = (float)E.pos[(size_t)axf[j] * E.pos_stride + m];
-                float sn, cs;
-                sincosf(p * invf[j], &sn, &cs);
-                const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
-                x1 = y1; x2 = y2;
-              }
-              dst[f] = f2bf(x1);
-              dst[f + half] = f2bf(x2);
-            }
-          } else {
-            float x1 = acc[i][jlo][r], x2 = acc[i][jlo + 1][r];
-            const int f = col_l;
-            if (rot) {
-              const float p = (float)E.pos[(size_t)axf[0] * E.pos_stride + m];
-              float sn, cs;
-              sincosf(p * invf[0], &sn, &cs);
-              const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
-              x1 = y1; x2 = y2;
-            }
-            dst[f] = f2bf(x1);
-            dst[f + half] = f2bf(x2);
-          }
-        }
-    }
-  }
+  gemm_epilogue<MODE, MB, NB>(P, acc, m0 + wm * WM, n0 + wn * WN, lane, blockIdx.z);
 }
 
 template <int BM, int BN, int MODE, int BKIND>
@@ -372,8 +212,8 @@ hipError_t launch_gemm_bf16_resid(const void* A, int lda, int M, int K, const BM
   P.x = (const bf16_t*)x;
   P.out = (bf16_t*)out;
   P.ldo = ldo;
-  // Pick the tile so the grid covers the 256 CUs: 256 x 256 when that gives at least
-  // 256 tiles, else 128 x 256.
+  // 256 x 256 tiles when that gives at least one tile per CU, else 128 x 256 tiles
+  // (twice as many workgroups).
   const long long t256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
   if (t256 >= 256) {
     P.tiles_m = (M + 255) / 256; P.tiles_n = (N + 255) / 256;
