@@ -192,8 +192,10 @@ PrefillWs prefill_ws(const compass_layer_desc* d, long long B, long long L) {
   return w;
 }
 
+// Split-K factor for the skinny decode GEMMs: enough workgroups (about 1024) to keep the
+// weight stream's loads in flight, with at least 256 K per split.
 int decode_splits(long long tiles, long long K) {
-  long long s = 512 / (tiles > 0 ? tiles : 1);
+  long long s = 1024 / (tiles > 0 ? tiles : 1);
   if (s > K / 256) s = K / 256;
   if (s < 1) s = 1;
   return (int)s;

@@ -177,37 +177,203 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
   }
 }
 
+// bf16 variant: the chunk's scores come from MFMA. For each 32-key block the wave computes
+// S^T = K Q^T with v_mfma_f32_32x32x16_bf16: operand A is 32 key rows (lane l loads key
+// l % 32, dims 8 (l / 32) + 16 ks .. + 8, straight from HBM into registers), operand B
+// holds the G query heads in columns 0..G-1 (other columns zero). Lanes whose column is
+// a real head then hold 16 keys' scores each, so no cross-lane reduction is needed for
+// q . k. The PV product stays on the vector ALUs: each key row is read by hd / 8 lanes
+// with 16-byte loads and the four key groups of a wave are summed once at the end.
+template <int HD, int G>
+__global__ __launch_bounds__(256) void decode_attn_mfma_kernel(const bf16_t* __restrict__ q,
+                                                               const bf16_t* __restrict__ k,
+                                                               const bf16_t* __restrict__ v,
+                                                               const int32_t* __restrict__ lens, int Hq,
+                                                               int Hkv, int cap, int sliding, int window,
+                                                               float scale_log2, int n_chunks,
+                                                               float* __restrict__ part) {
+  constexpr int KS = HD / 16;          // k-steps of 16 dims
+  constexpr int LPK = HD / 8;          // lanes per V row in the PV product
+  constexpr int KPS = 64 / LPK;        // V rows per wave step
+  constexpr int STEPS = 64 / KPS;      // 64 keys per wave
+  __shared__ float s_p[G][CHUNK];
+  __shared__ float s_red[G][4];
+  __shared__ float s_o[4][G][HD];
+
+  const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lens[b];
+  float* out = part + (((size_t)b * Hq + kvh * G) * n_chunks + chunk) * (HD + 2);
+  const size_t head_stride = (size_t)n_chunks * (HD + 2);
+  const bool row_ok = n >= 0 && n < cap;
+  const int lo = sliding ? max(0, n - window + 1) : 0;
+  const int kbeg = lo + chunk * CHUNK;
+  const int kend = min(kbeg + CHUNK, n + 1);
+  if (!row_ok || kbeg >= kend) {
+    if (tid < G) {
+      out[tid * head_stride + HD] = -INFINITY;
+      out[tid * head_stride + HD + 1] = 0.f;
+    }
+    return;
+  }
+  const bf16_t* kb = k + ((size_t)b * Hkv + kvh) * cap * HD;
+  const bf16_t* vb = v + ((size_t)b * Hkv + kvh) * cap * HD;
+
+  // K fragments of this wave's two 32-key blocks (keys clamped to the visible range).
+  const int col = lane & 31, half = lane >> 5;
+  u32x4_t kr[2][KS];
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2) {
+    const int key = min(kbeg + 64 * wave + 32 * kb2 + col, kend - 1);
+    const bf16_t* kp = kb + (size_t)key * HD + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kr[kb2][ks] = *reinterpret_cast<const u32x4_t*>(kp + 16 * ks);
+  }
+  // V rows for the PV product, issued now so they stream while the scores are formed.
+  const int sub = lane % LPK, kin = lane / LPK;
+  u32x4_t vr[STEPS];
+#pragma unroll
+  for (int st = 0; st < STEPS; ++st) {
+    const int key = min(kbeg + 64 * wave + st * KPS + kin, kend - 1);
+    vr[st] = *reinterpret_cast<const u32x4_t*>(vb + (size_t)key * HD + 8 * sub);
+  }
+  // Q^T operand: column `col` is head col (zero beyond G).
+  bf16x8_t qf[KS];
+  {
+    const bool live = col < G;
+    const bf16_t* qp = q + ((size_t)b * Hq + kvh * G + (live ? col : 0)) * HD + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4_t w = *reinterpret_cast<const u32x4_t*>(qp + 16 * ks);
+      if (!live) w = u32x4_t{0u, 0u, 0u, 0u};
+      qf[ks] = __builtin_bit_cast(bf16x8_t, w);
+    }
+  }
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2) {
+    f32x16_t sacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kr[kb2][ks]), qf[ks], sacc, 0, 0, 0);
+    if (col < G) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kl = 64 * wave + 32 * kb2 + 8 * (r >> 2) + 4 * half + (r & 3);
+        s_p[col][kl] = (kbeg + kl < kend) ? sacc[r] * scale_log2 : -INFINITY;
+      }
+    }
+  }
+  __syncthreads();
+  float sv[G], mx[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    sv[g] = s_p[g][tid];
+    const float wm = wave_max(sv[g]);
+    if (lane == 0) s_red[g][wave] = wm;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < G; ++g) mx[g] = fmaxf(fmaxf(s_red[g][0], s_red[g][1]), fmaxf(s_red[g][2], s_red[g][3]));
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float p = exp2f(sv[g] - mx[g]);
+    s_p[g][tid] = p;
+    const float ws = wave_sum(p);
+    if (lane == 0) s_red[g][wave] = ws;
+  }
+  __syncthreads();
+  float acc[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+#pragma unroll
+  for (int st = 0; st < STEPS; ++st) {
+    const u32x4_t r = vr[st];
+    const uint32_t w4[4] = {r.x, r.y, r.z, r.w};
+    float vf[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      vf[2 * j] = __uint_as_float(w4[j] << 16);
+      vf[2 * j + 1] = __uint_as_float(w4[j] & 0xffff0000u);
+    }
+    const int kl = 64 * wave + st * KPS + kin;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float p = s_p[g][kl];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e]);
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float a2 = acc[g][e];
+#pragma unroll
+      for (int o = LPK; o < 64; o <<= 1) a2 += __shfl_xor(a2, o, 64);
+      acc[g][e] = a2;
+    }
+  if (kin == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_o[wave][g][8 * sub + e] = acc[g][e];
+  }
+  __syncthreads();
+  for (int i = tid; i < G * HD; i += 256) {
+    const int g = i / HD, d = i % HD;
+    out[g * head_stride + d] = s_o[0][g][d] + s_o[1][g][d] + s_o[2][g][d] + s_o[3][g][d];
+  }
+  if (tid < G) {
+    out[tid * head_stride + HD] = mx[tid];
+    out[tid * head_stride + HD + 1] = s_red[tid][0] + s_red[tid][1] + s_red[tid][2] + s_red[tid][3];
+  }
+}
+
+// Merge the chunk partials of one (row, head): weights 2^(m_c - M) from the chunk maxima,
+// loaded in parallel into LDS; each thread then owns output dimensions d.
 template <typename T, int HD>
-__global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ part,
-                                                            const int32_t* __restrict__ lens, int Hq,
-                                                            int cap, int n_chunks, T* __restrict__ o,
-                                                            int ldo) {
-  const int bh = blockIdx.x, b = bh / Hq, h = bh % Hq, lane = threadIdx.x;
+__global__ __launch_bounds__(128) void decode_combine_kernel(const float* __restrict__ part,
+                                                             const int32_t* __restrict__ lens, int Hq,
+                                                             int cap, int n_chunks, T* __restrict__ o,
+                                                             int ldo) {
+  constexpr int MAXC = 512;  // chunk statistics held in LDS per pass
+  __shared__ float s_w[MAXC];
+  __shared__ float s_red[2];
+  const int bh = blockIdx.x, b = bh / Hq, h = bh % Hq, tid = threadIdx.x;
   const int n = lens[b];
   if (n < 0 || n >= cap) return;
   const float* p = part + (size_t)bh * n_chunks * (HD + 2);
-  float M = -INFINITY;
-  for (int c = 0; c < n_chunks; ++c) M = fmaxf(M, p[c * (HD + 2) + HD]);
-  constexpr int DPL = (HD + 63) / 64;
-  float acc[DPL] = {};
-  float l = 0.f;
-  for (int c = 0; c < n_chunks; ++c) {
-    const float mc = p[c * (HD + 2) + HD];
-    if (mc == -INFINITY) continue;
-    const float w = exp2f(mc - M);
-    l += w * p[c * (HD + 2) + HD + 1];
-#pragma unroll
-    for (int t = 0; t < DPL; ++t) {
-      const int d = lane + 64 * t;
-      if (d < HD) acc[t] += w * p[c * (HD + 2) + d];
+  // Global max over all chunks (strided over threads, then a block reduction).
+  float mx = -INFINITY;
+  for (int c = tid; c < n_chunks; c += 128) mx = fmaxf(mx, p[(size_t)c * (HD + 2) + HD]);
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) s_red[tid >> 6] = mx;
+  __syncthreads();
+  const float M = fmaxf(s_red[0], s_red[1]);
+  float acc = 0.f, l = 0.f;
+  for (int c0 = 0; c0 < n_chunks; c0 += MAXC) {
+    const int nc = min(MAXC, n_chunks - c0);
+    __syncthreads();
+    for (int c = tid; c < nc; c += 128) {
+      const float mc = p[(size_t)(c0 + c) * (HD + 2) + HD];
+      s_w[c] = (mc == -INFINITY) ? 0.f : exp2f(mc - M);
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int c = 0; c < nc; ++c) {
+      const float w = s_w[c];
+      if (w == 0.f) continue;  // empty chunk: only its max and sum were written
+      const float* pc = p + (size_t)(c0 + c) * (HD + 2);
+      l += w * pc[HD + 1];
+      if (tid < HD) acc += w * pc[tid];
     }
   }
-  T* op = o + (size_t)b * ldo + (size_t)h * HD;
-#pragma unroll
-  for (int t = 0; t < DPL; ++t) {
-    const int d = lane + 64 * t;
-    if (d < HD) op[d] = Elt<T>::from_f(acc[t] / l);
-  }
+  if (tid < HD) o[(size_t)b * ldo + (size_t)h * HD + tid] = Elt<T>::from_f(acc / l);
 }
 
 template <typename T, int HD>
@@ -241,8 +407,23 @@ hipError_t launch_decode_attention(int dtype, const void* q, const void* k, cons
                                    hipStream_t s) {
   const int G = Hq / Hkv;
   if (dtype == 1) {
-    return hd == 128 ? launch_attn_g<bf16_t, 128>(G, q, k, v, lens, B, Hq, Hkv, cap, sliding, window, n_chunks, part, s)
-                     : launch_attn_g<bf16_t, 64>(G, q, k, v, lens, B, Hq, Hkv, cap, sliding, window, n_chunks, part, s);
+    const dim3 grid(n_chunks, Hkv, B);
+    const float sl = kLog2e / sqrtf((float)hd);
+#define COMPASS_DECM(HD, GG)                                                                    \
+  decode_attn_mfma_kernel<HD, GG><<<grid, 256, 0, s>>>((const bf16_t*)q, (const bf16_t*)k,      \
+                                                        (const bf16_t*)v, lens, Hq, Hkv, cap,    \
+                                                        sliding, window, sl, n_chunks, part)
+    if (hd == 128) {
+      switch (G) { case 1: COMPASS_DECM(128, 1); break; case 2: COMPASS_DECM(128, 2); break;
+                   case 4: COMPASS_DECM(128, 4); break; case 8: COMPASS_DECM(128, 8); break;
+                   default: return hipErrorInvalidValue; }
+    } else {
+      switch (G) { case 1: COMPASS_DECM(64, 1); break; case 2: COMPASS_DECM(64, 2); break;
+                   case 4: COMPASS_DECM(64, 4); break; case 8: COMPASS_DECM(64, 8); break;
+                   default: return hipErrorInvalidValue; }
+    }
+#undef COMPASS_DECM
+    return hipGetLastError();
   }
   return hd == 128 ? launch_attn_g<float, 128>(G, q, k, v, lens, B, Hq, Hkv, cap, sliding, window, n_chunks, part, s)
                    : launch_attn_g<float, 64>(G, q, k, v, lens, B, Hq, Hkv, cap, sliding, window, n_chunks, part, s);
@@ -252,11 +433,11 @@ hipError_t launch_decode_combine(int dtype, const float* part, const int32_t* le
                                  int cap, int hd, int n_chunks, void* o, int ldo, hipStream_t s) {
   const dim3 grid(B * Hq);
   if (dtype == 1) {
-    if (hd == 128) decode_combine_kernel<bf16_t, 128><<<grid, 64, 0, s>>>(part, lens, Hq, cap, n_chunks, (bf16_t*)o, ldo);
-    else decode_combine_kernel<bf16_t, 64><<<grid, 64, 0, s>>>(part, lens, Hq, cap, n_chunks, (bf16_t*)o, ldo);
+    if (hd == 128) decode_combine_kernel<bf16_t, 128><<<grid, 128, 0, s>>>(part, lens, Hq, cap, n_chunks, (bf16_t*)o, ldo);
+    else decode_combine_kernel<bf16_t, 64><<<grid, 128, 0, s>>>(part, lens, Hq, cap, n_chunks, (bf16_t*)o, ldo);
   } else {
-    if (hd == 128) decode_combine_kernel<float, 128><<<grid, 64, 0, s>>>(part, lens, Hq, cap, n_chunks, (float*)o, ldo);
-    else decode_combine_kernel<float, 64><<<grid, 64, 0, s>>>(part, lens, Hq, cap, n_chunks, (float*)o, ldo);
+    if (hd == 128) decode_combine_kernel<float, 128><<<grid, 128, 0, s>>>(part, lens, Hq, cap, n_chunks, (float*)o, ldo);
+    else decode_combine_kernel<float, 64><<<grid, 128, 0, s>>>(part, lens, Hq, cap, n_chunks, (float*)o, ldo);
   }
   return hipGetLastError();
 }
