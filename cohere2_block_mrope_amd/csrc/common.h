@@ -21,17 +21,17 @@ __device__ __forceinline__ float bf2f(bf16_t v) {
   return __uint_as_float(((uint32_t)v) << 16);
 }
 
-// fp32 -> bf16, round to nearest even (quiet NaN kept as NaN).
+// fp32 -> bf16, round to nearest even, NaN kept as a quiet NaN (gfx950's
+// v_cvt_pk_bf16_f32).
 __device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+  return __builtin_bit_cast(bf16_t, (__bf16)f);
 }
 
-// Two fp32 -> packed pair of bf16 (low half = a).
+// Two fp32 -> packed pair of bf16 (low half = a), one conversion instruction.
 __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
-  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Storage-type abstraction used by templated kernels.
@@ -58,6 +58,40 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
+// silu(g) = g / (1 + e^-g) from the hardware exp2 and reciprocal (a few ulp; the
+// limits g -> +inf, -inf give g and -0).
+__device__ __forceinline__ float silu_f(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
+}
+
+// Value of lane (lane ^ 1) / (lane ^ 2) of the same quad (DPP quad permutes; every lane
+// of the quad must be active).
+__device__ __forceinline__ float quad_xor1(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_xor2(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+}
+
+// 4 x 4 transpose inside each quad of lanes (q = lane & 3), in registers. On entry
+// lane q holds rows 0..3 of column q (v[r] = X[r][q]); on exit it holds columns 0..3
+// of row 2 (q & 1) + (q >> 1) (v[c] = X[row][c]). Used to turn MFMA result columns
+// into row-contiguous 8- and 16-byte stores. All 64 lanes must be active.
+__device__ __forceinline__ void quad_transpose(float (&v)[4], int lane) {
+  const bool odd = lane & 1, hi = lane & 2;
+  // Swap with lane ^ 1: even lanes keep rows 0, 1, odd lanes rows 2, 3; afterwards
+  // (a0, a1) and (a2, a3) are two consecutive rows over the column pair (q & 2) + {0, 1}.
+  const float r0 = quad_xor1(odd ? v[0] : v[2]);
+  const float r1 = quad_xor1(odd ? v[1] : v[3]);
+  const float a0 = odd ? r0 : v[0], a1 = odd ? v[2] : r0;
+  const float a2 = odd ? r1 : v[1], a3 = odd ? v[3] : r1;
+  // Swap with lane ^ 2: lanes q < 2 keep the first of the two rows, the others the second.
+  const float p0 = quad_xor2(hi ? a0 : a2);
+  const float p1 = quad_xor2(hi ? a1 : a3);
+  v[0] = hi ? p0 : a0;
+  v[1] = hi ? p1 : a1;
+  v[2] = hi ? a2 : p0;
+  v[3] = hi ? a3 : p1;
+}
 
 static constexpr float kLog2e = 1.4426950408889634f;

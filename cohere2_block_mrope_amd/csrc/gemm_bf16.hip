@@ -14,8 +14,9 @@
 // Tiling: a 256-thread workgroup (4 waves, 2 x 2) computes a BM x BN tile; each wave
 // owns a (BM/2) x (BN/2) sub-tile of 32 x 32 MFMA blocks. K advances in steps of 64
 // through a double-buffered LDS stage (A and B tiles, 16-byte chunks XOR-swizzled by
-// row so that the fragment reads of 8 consecutive rows hit distinct banks); the next
-// step's global loads are in flight while the current step's MFMAs run.
+// row so that the fragment reads of 8 consecutive rows hit distinct banks). Global
+// loads run two K steps ahead through registers and are interleaved, one 16-byte piece
+// at a time, with the MFMAs of the current step.
 //
 // MFMA lane layout (checked on gfx950): operand lane l holds row (l % 32) and
 // k = 8 * (l / 32) .. + 8; result register r of lane l holds
@@ -102,27 +103,30 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams P) {
     }
   }
 
+  // Stage k + 1 sits in registers while stage k is multiplied out of LDS. Its 16-byte
+  // pieces are written to the other LDS buffer one at a time between MFMAs, and each
+  // register is refilled with stage k + 2 right after its write, so the memory
+  // instructions spread over the MFMA stream instead of stalling it in one burst.
+  constexpr int PIECES = A_PER_T + B_PER_T;
+  constexpr int MFMAS = (BK / 16) * MB * NB;
   u32x4_t ra[A_PER_T], rb[B_PER_T];
-  auto gload = [&](int k0) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(P.A + aoff[i] + k0);
-    if (BKIND == 2 && k0 >= P.bm.ksplit) {
-#pragma unroll
-      for (int i = 0; i < B_PER_T; ++i) rb[i] = *reinterpret_cast<const u32x4_t*>(bbase1 + boff1[i] + k0);
+  auto load_piece = [&](int k0, int p) __attribute__((always_inline)) {
+    if (p < A_PER_T) {
+      ra[p] = *reinterpret_cast<const u32x4_t*>(P.A + aoff[p] + k0);
     } else {
-#pragma unroll
-      for (int i = 0; i < B_PER_T; ++i) rb[i] = *reinterpret_cast<const u32x4_t*>(bbase0 + boff[i] + k0);
+      const int i = p - A_PER_T;
+      if (BKIND == 2 && k0 >= P.bm.ksplit)
+        rb[i] = *reinterpret_cast<const u32x4_t*>(bbase1 + boff1[i] + k0);
+      else
+        rb[i] = *reinterpret_cast<const u32x4_t*>(bbase0 + boff[i] + k0);
     }
   };
-  auto sstore = [&](int buf) __attribute__((always_inline)) {
-    bf16_t* a = As + buf * BM * BK;
-    bf16_t* b = Bs + buf * BN * BK;
-#pragma unroll
-    for (int i = 0; i < A_PER_T; ++i)
-      *reinterpret_cast<u32x4_t*>(a + swz(arow0 + 8 * i, lchunk)) = ra[i];
-#pragma unroll
-    for (int i = 0; i < B_PER_T; ++i)
-      *reinterpret_cast<u32x4_t*>(b + swz(brow0 + 8 * i, lchunk)) = rb[i];
+  auto store_piece = [&](int buf, int p) __attribute__((always_inline)) {
+    if (p < A_PER_T)
+      *reinterpret_cast<u32x4_t*>(As + buf * BM * BK + swz(arow0 + 8 * p, lchunk)) = ra[p];
+    else
+      *reinterpret_cast<u32x4_t*>(Bs + buf * BN * BK + swz(brow0 + 8 * (p - A_PER_T), lchunk)) =
+          rb[p - A_PER_T];
   };
 
   f32x16_t acc[MB][NB];
@@ -133,39 +137,74 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams P) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = (kend - kbeg) / BK;
-  if (nk > 0) {
-    gload(kbeg);
-    sstore(0);
+  int fa_off[BK / 16], fb_off[BK / 16];
+#pragma unroll
+  for (int ks = 0; ks < BK / 16; ++ks) {
+    const int c = 2 * ks + (lane >> 5);
+    fa_off[ks] = swz(wm * WM + (lane & 31), c);
+    fb_off[ks] = swz(wn * WN + (lane & 31), c);
   }
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
+
+  // One K step: MFMAs over LDS buffer kt & 1; `wr` stores stage kt + 1 to the other
+  // buffer, `ld` fetches stage kt + 2.
+  auto step = [&](int kt, const bool wr, const bool ld) __attribute__((always_inline)) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kbeg + (kt + 1) * BK);
     const bf16_t* a = As + cur * BM * BK;
     const bf16_t* b = Bs + cur * BN * BK;
+    const int knext = kbeg + (kt + 2) * BK;
+    bf16x8_t fa[2][MB], fb[2][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) fa[0][i] = *reinterpret_cast<const bf16x8_t*>(a + fa_off[0] + 32 * i * BK);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) fb[0][j] = *reinterpret_cast<const bf16x8_t*>(b + fb_off[0] + 32 * j * BK);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8_t fa[MB], fb[NB];
-      const int c = 2 * ks + (lane >> 5);
+      const int fs = ks & 1;
+      if (ks + 1 < BK / 16) {
 #pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        const int r = wm * WM + 32 * i + (lane & 31);
-        fa[i] = *reinterpret_cast<const bf16x8_t*>(a + swz(r, c));
-      }
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int r = wn * WN + 32 * j + (lane & 31);
-        fb[j] = *reinterpret_cast<const bf16x8_t*>(b + swz(r, c));
-      }
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
+        for (int i = 0; i < MB; ++i)
+          fa[fs ^ 1][i] = *reinterpret_cast<const bf16x8_t*>(a + fa_off[ks + 1] + 32 * i * BK);
 #pragma unroll
         for (int j = 0; j < NB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          fb[fs ^ 1][j] = *reinterpret_cast<const bf16x8_t*>(b + fb_off[ks + 1] + 32 * j * BK);
+      }
+#pragma unroll
+      for (int t = 0; t < MB * NB; ++t) {
+        acc[t / NB][t % NB] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fs][t / NB], fb[fs][t % NB], acc[t / NB][t % NB], 0, 0, 0);
+        const int f = ks * MB * NB + t;
+#pragma unroll
+        for (int p = 0; p < PIECES; ++p) {
+          if ((p * MFMAS) / PIECES == f) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (wr) store_piece(cur ^ 1, p);
+            if (ld) load_piece(knext, p);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
     }
-    if (kt + 1 < nk) sstore(cur ^ 1);
     __syncthreads();
+  };
+
+  const int nk = (kend - kbeg) / BK;
+  if (nk > 0) {
+#pragma unroll
+    for (int p = 0; p < PIECES; ++p) load_piece(kbeg, p);
+#pragma unroll
+    for (int p = 0; p < PIECES; ++p) store_piece(0, p);
+    if (nk > 1) {
+#pragma unroll
+      for (int p = 0; p < PIECES; ++p) load_piece(kbeg + BK, p);
+    }
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) step(kt, true, true);
+    if (kt + 1 < nk) {
+      step(kt, true, false);
+      ++kt;
+    }
+    step(kt, false, false);
   }
 
   gemm_epilogue<MODE, MB, NB>(P, acc, m0 + wm * WM, n0 + wn * WN, lane, blockIdx.z);

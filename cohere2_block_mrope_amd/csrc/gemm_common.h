@@ -56,127 +56,198 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
   tn = in_group / gsize;
 }
 
-// Stores one wave's accumulators: MB x NB blocks of 32 x 32; the wave's block (i, j)
-// covers rows mw0 + 32 i .. and columns nw0 + 32 j ... Result register r of lane l holds
-// row 8 (r / 4) + 4 (l / 32) + r % 4 and column l % 32 of a block.
-template <int MODE, int MB, int NB>
-__device__ __forceinline__ void gemm_epilogue(const GemmParams& P, f32x16_t (&acc)[MB][NB], int mw0,
-                                              int nw0, int lane, int z) {
-  const int col_l = lane & 31;
-  const int row_l = 4 * (lane >> 5);
-  if constexpr (MODE == MODE_RAW || MODE == MODE_RESID || MODE == MODE_SCALED) {
+// Epilogue layout. The wave's block (i, j) covers rows mw0 + 32 i .. and columns
+// nw0 + 32 j ..; result register r of lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4
+// and column l % 32. Each group of 4 registers (rows 8 g + 4 (l / 32) + 0..3) is
+// transposed inside lane quads (quad_transpose), after which the lane holds 4
+// consecutive columns (l % 32) & ~3 .. + 3 of one row 8 g + 4 (l / 32) + rsel and
+// stores them with one 8-byte (bf16) or 16-byte (fp32) access.
+__device__ __forceinline__ int epi_row(int lane) {
+  const int q = lane & 3;
+  return 4 * (lane >> 5) + 2 * (q & 1) + (q >> 1);
+}
+
+template <int MB, int NB>
+__device__ __forceinline__ void load_group(const f32x16_t (&acc)[MB][NB], int i, int j, int g, float (&v)[4]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) v[t] = acc[i][j][4 * g + t];
+}
+
+__device__ __forceinline__ void store_bf16x4(bf16_t* dst, const float (&v)[4]) {
+  u32x2_t o;
+  o.x = pack_bf2(v[0], v[1]);
+  o.y = pack_bf2(v[2], v[3]);
+  *reinterpret_cast<u32x2_t*>(dst) = o;
+}
+
+// q / k / v part of the fused projection epilogue for head_dim HD. For HD = 128 the
+// wave's 128 columns are one head (first half blocks 0, 1, second half 2, 3); for
+// HD = 64 two heads (blocks {0, 1} and {2, 3}). Pairs (x_f, x_{f + HD/2}) sit in the
+// same lane and register of blocks j and j + HD/64, so MRoPE is applied after the
+// transpose, on whole rows. The rotation angle pos * inv_freq is evaluated in
+// revolutions (inv_freq / 2 pi rounded once to fp32, reduced to [-1/2, 1/2]) for the
+// hardware sin / cos.
+template <int HD, int MB, int NB>
+__device__ __forceinline__ void proj_qkv_epilogue(const GemmParams& P, const f32x16_t (&acc)[MB][NB], int mw0,
+                                                  int ch0, int lane) {
+  constexpr int PB = HD / 64;          // 32-column blocks per half head
+  constexpr int NHEAD = 128 / HD;      // heads per wave
+  constexpr int HALF = HD / 2;
+  const ProjEpi& E = P.ep;
+  const int qe = E.nq64, ke = qe + E.nk64;
+  const int col4 = (lane & 31) & ~3;
+  const int rowq = epi_row(lane);
+
+  // Inverse frequencies (in revolutions per position) and axes of this lane's columns:
+  // frequency 32 jj + col4 + t of the first half.
+  float invr[PB][4];
+  int axis[PB][4];
+  {
+    const double th = (double)P.rt.theta;
+    const double r1 = pow(th, -2.0 / HD), r32 = pow(th, -64.0 / HD);
+    double f0 = pow(th, -2.0 * col4 / HD) * 0.15915494309189535;  // / (2 pi)
+#pragma unroll
+    for (int jj = 0; jj < PB; ++jj) {
+      double f = f0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        invr[jj][t] = (float)f;
+        axis[jj][t] = rope_axis(P.rt, 32 * jj + col4 + t);
+        f *= r1;
+      }
+      f0 *= r32;
+    }
+  }
+
+#pragma unroll
+  for (int hf = 0; hf < NHEAD; ++hf) {
+    const int ch = ch0 + hf * PB;  // first 64-column chunk of this head
+    int kind, head;
+    if (ch < qe) { kind = 0; head = ch * 64 / HD; }
+    else if (ch < ke) { kind = 1; head = (ch - qe) * 64 / HD; }
+    else { kind = 2; head = (ch - ke) * 64 / HD; }
+    const bool rot = E.rope && kind < 2;
+    // Pointer chosen arithmetically: a select between fields of P would become a load
+    // through a selected address and force P out of registers.
+    const uint64_t sel_q = kind == 0, sel_k = kind == 1, sel_v = kind == 2;
+    bf16_t* const base = (bf16_t*)(sel_q * (uint64_t)E.q + sel_k * (uint64_t)E.kc + sel_v * (uint64_t)E.vc);
+    const int jlo = hf * 2 * PB;
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int n = nw0 + 32 * j + col_l;
-        if (n >= P.N) continue;
+      for (int g = 0; g < 4; ++g) {
+        const int m = mw0 + 32 * i + 8 * g + rowq;
+        const int mm = min(m, P.M - 1);
+        int b, l;
+        if (E.decode) { b = mm; l = E.lens[b]; } else { b = mm / E.L; l = mm - b * E.L; }
+        bf16_t* dst;
+        if (kind == 0) dst = base + (((size_t)b * E.Hq + head) * E.Lq + (E.decode ? 0 : l)) * HD;
+        else dst = base + (((size_t)b * E.Hkv + head) * E.cap + l) * HD;
+        float pt = 0.f, ph = 0.f, pw = 0.f;
+        if (rot) {
+          pt = (float)E.pos[mm];
+          ph = (float)E.pos[(size_t)E.pos_stride + mm];
+          pw = (float)E.pos[2 * (size_t)E.pos_stride + mm];
+        }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = mw0 + 32 * i + 8 * (r >> 2) + row_l + (r & 3);
-          if (m >= P.M) continue;
-          const float v = acc[i][j][r];
-          if constexpr (MODE == MODE_RAW) {
-            P.raw[((size_t)z * P.M + m) * P.N + n] = v;
-          } else if constexpr (MODE == MODE_RESID) {
-            const size_t o = (size_t)m * P.ldo + n;
-            P.out[o] = f2bf(bf2f(P.x[o]) + v);
-          } else {
-            P.outf[(size_t)m * P.ldof + n] = v * P.scale;
+        for (int jj = 0; jj < PB; ++jj) {
+          float x1[4], x2[4];
+          load_group(acc, i, jlo + jj, g, x1);
+          load_group(acc, i, jlo + jj + PB, g, x2);
+          quad_transpose(x1, lane);
+          quad_transpose(x2, lane);
+          if (rot) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const float p = axis[jj][t] == 0 ? pt : axis[jj][t] == 1 ? ph : pw;
+              float rev = p * invr[jj][t];
+              rev -= rintf(rev);
+              const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+              const float y1 = x1[t] * cs - x2[t] * sn, y2 = x2[t] * cs + x1[t] * sn;
+              x1[t] = y1;
+              x2[t] = y2;
+            }
+          }
+          if (m < P.M) {
+            store_bf16x4(dst + 32 * jj + col4, x1);
+            store_bf16x4(dst + HALF + 32 * jj + col4, x2);
           }
         }
       }
+  }
+}
+
+// Stores one wave's accumulators (MB x NB blocks of 32 x 32 at rows mw0.., columns nw0..).
+// RAW, RESID and PROJ need N and the row strides to be multiples of 4 (checked by the
+// launchers); SCALED falls back to element stores otherwise.
+template <int MODE, int MB, int NB>
+__device__ __forceinline__ void gemm_epilogue(const GemmParams& P, f32x16_t (&acc)[MB][NB], int mw0,
+                                              int nw0, int lane, int z) {
+  const int col4 = (lane & 31) & ~3;
+  const int rowq = epi_row(lane);
+  if constexpr (MODE == MODE_RAW || MODE == MODE_RESID || MODE == MODE_SCALED) {
+    const bool vec = MODE != MODE_SCALED || ((P.N & 3) == 0 && (P.ldof & 3) == 0);
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float v[4];
+          load_group(acc, i, j, g, v);
+          quad_transpose(v, lane);
+          const int m = mw0 + 32 * i + 8 * g + rowq;
+          const int n = nw0 + 32 * j + col4;
+          if (m >= P.M || n >= P.N) continue;
+          if constexpr (MODE == MODE_RAW) {
+            *reinterpret_cast<f32x4_t*>(P.raw + ((size_t)z * P.M + m) * P.N + n) = f32x4_t{v[0], v[1], v[2], v[3]};
+          } else if constexpr (MODE == MODE_RESID) {
+            const size_t o = (size_t)m * P.ldo + n;
+            const u32x2_t xv = *reinterpret_cast<const u32x2_t*>(P.x + o);
+            v[0] += __uint_as_float(xv.x << 16);
+            v[1] += __uint_as_float(xv.x & 0xffff0000u);
+            v[2] += __uint_as_float(xv.y << 16);
+            v[3] += __uint_as_float(xv.y & 0xffff0000u);
+            store_bf16x4(P.out + o, v);
+          } else {
+            float* d = P.outf + (size_t)m * P.ldof + n;
+            if (vec) {
+              *reinterpret_cast<f32x4_t*>(d) = f32x4_t{v[0] * P.scale, v[1] * P.scale, v[2] * P.scale, v[3] * P.scale};
+            } else {
+#pragma unroll
+              for (int t = 0; t < 4; ++t)
+                if (n + t < P.N) d[t] = v[t] * P.scale;
+            }
+          }
+        }
   } else {
-    // MODE_PROJ: requires WN == 128 (BN == 256); see the header comment.
+    // MODE_PROJ: requires WN == 128 (BN == 256).
     static_assert(MODE != MODE_PROJ || NB == 4, "fused projection epilogue needs 128-column waves");
     const ProjEpi& E = P.ep;
-    if (nw0 >= P.N) return;
+    if (nw0 >= P.N) return;  // wave-uniform
     const int ch0 = nw0 >> 6;
-    const int qe = E.nq64, ke = qe + E.nk64, ve = ke + E.nk64;
-    const int hd = E.hd;
+    const int ve = E.nq64 + 2 * E.nk64;
     if (ch0 >= ve) {
-      // SwiGLU: chunk ch0 is gate columns, ch0 + 1 the up columns of the same c.
-      const int cbase = ((ch0 - ve) >> 1) * 64;
-      bf16_t* act = (bf16_t*)E.act;
+      // SwiGLU: chunk ch0 holds gate columns, ch0 + 1 the up columns of the same c.
+      bf16_t* act = (bf16_t*)E.act + E.act_col0 + ((ch0 - ve) >> 1) * 64 + col4;
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = mw0 + 32 * i + 8 * (r >> 2) + row_l + (r & 3);
-          if (m >= P.M) continue;
-          bf16_t* dst = act + (size_t)m * E.ldact + E.act_col0 + cbase + col_l;
+        for (int g = 0; g < 4; ++g) {
+          const int m = mw0 + 32 * i + 8 * g + rowq;
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
-            const float g = acc[i][j][r], u = acc[i][j + 2][r];
-            dst[32 * j] = f2bf(silu_f(g) * u);
+            float v[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) v[t] = silu_f(acc[i][j][4 * g + t]) * acc[i][j + 2][4 * g + t];
+            quad_transpose(v, lane);
+            if (m < P.M) store_bf16x4(act + (size_t)m * E.ldact + 32 * j, v);
           }
         }
       return;
     }
-    // q / k / v heads. For hd == 128 the wave holds one head: halves are blocks {0,1}
-    // and {2,3}. For hd == 64 it holds two heads: blocks {0,1} and {2,3}.
-    // This lane's frequencies: col_l (+ 32 for hd == 128).
-    float invf[2];
-    int axf[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int f = 32 * j + col_l;
-      invf[j] = rope_inv_freq(P.rt, f, hd);
-      axf[j] = rope_axis(P.rt, f);
-    }
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      if (hd == 128 && hf == 1) break;
-      const int ch = ch0 + hf;  // first chunk of this head
-      int kind, head;
-      if (ch < qe) { kind = 0; head = ch * 64 / hd; }
-      else if (ch < ke) { kind = 1; head = (ch - qe) * 64 / hd; }
-      else { kind = 2; head = (ch - ke) * 64 / hd; }
-      const int half = hd >> 1;
-      const bool rot = E.rope && kind < 2;
-      // Blocks of this head: jlo .. jlo + hd/32 - 1; partner of block j is j + half/32.
-      const int jlo = (hd == 128) ? 0 : 2 * hf;
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = mw0 + 32 * i + 8 * (r >> 2) + row_l + (r & 3);
-          if (m >= P.M) continue;
-          int b, l;
-          if (E.decode) { b = m; l = E.lens[b]; } else { b = m / E.L; l = m - b * E.L; }
-          bf16_t* dst;
-          if (kind == 0) dst = (bf16_t*)E.q + (((size_t)b * E.Hq + head) * E.Lq + (E.decode ? 0 : l)) * hd;
-          else dst = (bf16_t*)(kind == 1 ? E.kc : E.vc) + (((size_t)b * E.Hkv + head) * E.cap + l) * hd;
-          if (hd == 128) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              float x1 = acc[i][j][r], x2 = acc[i][j + 2][r];
-              const int f = 32 * j + col_l;
-              if (rot) {
-                const float p = (float)E.pos[(size_t)axf[j] * E.pos_stride + m];
-                float sn, cs;
-                sincosf(p * invf[j], &sn, &cs);
-                const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
-                x1 = y1; x2 = y2;
-              }
-              dst[f] = f2bf(x1);
-              dst[f + half] = f2bf(x2);
-            }
-          } else {
-            float x1 = acc[i][jlo][r], x2 = acc[i][jlo + 1][r];
-            const int f = col_l;
-            if (rot) {
-              const float p = (float)E.pos[(size_t)axf[0] * E.pos_stride + m];
-              float sn, cs;
-              sincosf(p * invf[0], &sn, &cs);
-              const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
-              x1 = y1; x2 = y2;
-            }
-            dst[f] = f2bf(x1);
-            dst[f + half] = f2bf(x2);
-          }
-        }
-    }
+    if (E.hd == 128) proj_qkv_epilogue<128>(P, acc, mw0, ch0, lane);
+    else proj_qkv_epilogue<64>(P, acc, mw0, ch0, lane);
   }
 }
 
