@@ -18,7 +18,6 @@ this host on one full layer of the same workload.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -41,6 +40,8 @@ def parse():
     p.add_argument("--no-extra", action="store_true", help="headline workload only")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--only", default=None, help="run one workload: c1|c2|c3|c4 (for profiling)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run plain 512 MiB copies (reference launches for the HBM byte counters)")
     return p.parse_args()
 
 
@@ -74,7 +75,7 @@ def timed(fn, steps, warmup, b, torch):
 
 
 # ------------------------------------------------------------------------ workloads
-def setup_c1(H, W, O, torch):
+def setup_c1(H, W, torch):
     from synth.workloads import WORKLOADS
     cfg = WORKLOADS[1]
     sh = cfg["shape"]
@@ -85,8 +86,8 @@ def setup_c1(H, W, O, torch):
     return sh, w, x, tok, grid, off
 
 
-def run_c1(args, b, H, W, O, torch):
-    sh, w, x, tok, grid, off = setup_c1(H, W, O, torch)
+def run_c1(args, b, H, W, torch):
+    sh, w, x, tok, grid, off = setup_c1(H, W, torch)
     L = x.shape[1]
     wd = H.weights_to_dev(sh, w)
     xd = H.to_dev(x, torch.bfloat16)
@@ -118,7 +119,7 @@ def c1_flops(sh, L):
     return proj, out, attn
 
 
-def run_c2(args, b, H, W, O, torch):
+def run_c2(args, b, H, W, torch):
     from synth.workloads import WORKLOADS
     cfg = WORKLOADS[2]
     sh, Bn, L = cfg["shape"], cfg["B"], cfg["L"]
@@ -138,7 +139,7 @@ def run_c2(args, b, H, W, O, torch):
             "kernels_us": {k: round(v["mean_us"], 1) for k, v in stats.items()}}
 
 
-def run_c3(args, b, H, W, O, torch):
+def run_c3(args, b, H, W, torch):
     from synth.workloads import WORKLOADS, layer_kind
     import dataclasses
     import synth.rng_torch as RT
@@ -180,15 +181,19 @@ def run_c3(args, b, H, W, O, torch):
     return res
 
 
-def run_c4(args, b, H, W, O, torch):
+def run_c4(args, b, H, W, torch):
     from synth.workloads import WORKLOADS, layer_kind
     import dataclasses
     import synth.rng_torch as RT
     cfg = WORKLOADS[4]
     sh, L, n_layers, V, scale = cfg["shape"], cfg["L"], cfg["layers"], cfg["vocab"], cfg["logit_scale"]
     tok, grid, off = W.c1_tokens(W.stream_seed(4, 0, W.TensorId.TOKENS))
-    pos_np, _ = O.mrope_positions(tok, W.IMAGE_TOKEN_ID, grid, off, 2)
-    pos = H.ints_to_dev(pos_np)
+    pos = torch.empty((3, 1, L), dtype=torch.int32, device="cuda")
+    delta = torch.empty((1,), dtype=torch.int32, device="cuda")
+    status = torch.empty((1,), dtype=torch.int32, device="cuda")
+    b.compass_mrope_positions(H.ints_to_dev(tok), W.IMAGE_TOKEN_ID, H.ints_to_dev(grid), H.ints_to_dev(off), 2,
+                              pos, delta, status)
+    assert int(status.item()) == 0
     layers = []
     for i in range(n_layers):
         shi = dataclasses.replace(sh, kind=layer_kind(i))
@@ -221,12 +226,15 @@ def run_c4(args, b, H, W, O, torch):
     return res
 
 
-def cpu_baseline(sh, w, x, tok, grid, off, O):
+def cpu_baseline(sh, w, x, tok, grid, off):
+    """The fp64 oracle (test infrastructure) timed on this host: the only use of oracle/ here."""
     import threadpoolctl
+    from oracle import compass_oracle as O
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
     t0 = time.perf_counter()
-    pos, _ = O.mrope_positions(tok, 255031, grid, off, 2)
+    from synth.workloads import IMAGE_TOKEN_ID
+    pos, _ = O.mrope_positions(tok, IMAGE_TOKEN_ID, grid, off, 2)
     O.layer_prefill(sh, w, x, pos)
     sec = time.perf_counter() - t0
     L = x.shape[1]
@@ -235,17 +243,42 @@ def cpu_baseline(sh, w, x, tok, grid, off, O):
                       f"fp64 numpy on {threads} BLAS threads, {sec:.1f} s"}
 
 
-def traffic_for(kernel_file: str, name: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
-    the current source of the kernel (else None)."""
+GEMM_SOURCES = ["gemm_bf16.hip", "gemm_common.h", "common.h", "launch.h"]
+
+
+def traffic_for(name: str, sources):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (profiles/<name>_traffic.json), if it was taken on the current sources of the kernel;
+    else None."""
+    from cohere2_block_mrope_amd.pmc_traffic import source_digest
     path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path))
-    src = open(os.path.join(ROOT, "cohere2_block_mrope_amd", "csrc", kernel_file), "rb").read()
-    if rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256") != source_digest(sources):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(torch, nbytes=512 << 20, copies=3):
+    """Plain device-to-device copies of a known size: the reference launches for scaling
+    the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(copies):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "copies": copies}
+
+
+def c1_proj_bytes(sh, L):
+    """Algorithmic HBM bytes of one fused-projection launch: the normalized activations and
+    the five weight matrices read once, q / k / v / SwiGLU output written once (bf16)."""
+    D, Hq, Hkv, hd, I = sh.hidden, sh.n_q_heads, sh.n_kv_heads, sh.head_dim, sh.intermediate
+    nv = (Hq + 2 * Hkv) * hd + 2 * I
+    return 2.0 * (L * D + nv * D + L * ((Hq + 2 * Hkv) * hd + I))
 
 
 def main():
@@ -256,7 +289,6 @@ def main():
         sys.exit(2)
     import torch
     from cohere2_block_mrope_amd import binding as b
-    from oracle import compass_oracle as O
     from synth import workloads as W
     from tests import helpers as H
     torch.cuda.set_device(0)
@@ -264,7 +296,7 @@ def main():
     res_extra = {}
     if args.only in (None, "c1"):
         log("c1: generating inputs")
-        sh, w, x, tok, grid, off, sec, stats = run_c1(args, b, H, W, O, torch)
+        sh, w, x, tok, grid, off, sec, stats = run_c1(args, b, H, W, torch)
         L = x.shape[1]
         proj, outf, attn = c1_flops(sh, L)
         gp = stats["gemm_proj"]
@@ -284,12 +316,13 @@ def main():
             "roofline": {"kernel": "gemm_proj (fused LN-input q/k/v/gate/up projection + MRoPE/SwiGLU epilogue)",
                          "bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                         "traffic": traffic_for("gemm_bf16.hip", "gemm_proj_c1"),
-                         "flops_per_launch": proj, "mean_launch_us": gp["mean_us"]},
+                         "traffic": traffic_for("gemm_proj_c1", GEMM_SOURCES),
+                         "flops_per_launch": proj, "mean_launch_us": gp["mean_us"],
+                         "algorithmic_bytes": c1_proj_bytes(sh, L)},
         }
         if not args.no_cpu:
             log("c1: timing the CPU oracle")
-            line["cpu_baseline"] = cpu_baseline(sh, w, x, tok, grid, off, O)
+            line["cpu_baseline"] = cpu_baseline(sh, w, x, tok, grid, off)
         else:
             line["cpu_baseline"] = None
     else:
@@ -298,8 +331,10 @@ def main():
         for key, fn in (("c2", run_c2), ("c3", run_c3), ("c4", run_c4)):
             if args.only in (None, key):
                 log(f"{key}: running")
-                res_extra[key] = fn(args, b, H, W, O, torch)
+                res_extra[key] = fn(args, b, H, W, torch)
                 torch.cuda.empty_cache()
+    if args.copy_calibration:
+        res_extra["copy_calibration"] = copy_calibration(torch)
     if line is None:
         print(json.dumps({"extra": res_extra}))
     else:

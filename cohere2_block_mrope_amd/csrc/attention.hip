@@ -14,6 +14,10 @@
 // K/V tiles of 64 keys are double-buffered in LDS (rows padded against bank
 // conflicts); tiles outside the causal/window range are skipped, and only tiles that
 // straddle the diagonal or the window edge are masked.
+// Online softmax in the log2 domain with a lazily moved reference: a row's running
+// maximum m is only raised (rescaling O and l by 2^(m_old - m_new)) when a tile's
+// maximum exceeds it by more than 2^8, so probabilities 2^(s - m) stay below 256 and
+// most tiles skip the rescale. O / l is unchanged by the choice of m.
 //
 // fp32 kernel: one wave per query, keys in 64-lane chunks with an online softmax.
 #include "common.h"
@@ -35,11 +39,14 @@ struct AttnParams {
 };
 
 constexpr int QB = 128, KB = 64;
+constexpr float kLazyMax = 8.0f;  // log2 headroom before the reference max is raised
 
 template <int HD>
 __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
   constexpr int KS = HD + 8;    // K row stride (elements): 8 consecutive rows -> distinct banks
-  constexpr int VS = HD + 16;   // V row stride: 4 rows x 32 B of a tr16 read -> distinct banks
+  // V row stride = 16 dwords mod 64 banks: the 32 lanes of a tr16 read (4 rows x 2 column
+  // groups of 32 B) then hit 64 distinct banks.
+  constexpr int VS = HD + 32;
   constexpr int DB = HD / 32;   // 32-wide d blocks of O^T
   constexpr int QK = HD / 16;   // 16-deep k-steps of S^T
   constexpr int CH = HD / 8;    // 16-byte chunks per key row
@@ -47,7 +54,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
   __shared__ __align__(16) bf16_t Ks[2][KB * KS];
   __shared__ __align__(16) bf16_t Vs[2][KB * VS];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int qb = P.nqb - 1 - blockIdx.x;  // heaviest (latest) query blocks first
   const int h = blockIdx.y, b = blockIdx.z;
   const int g = P.Hq / P.Hkv, kvh = h / g;
@@ -122,25 +130,44 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
       }
     }
     // Mask only tiles that are not entirely visible to every query of the workgroup.
+    // The maximum is taken on raw scores (the scale is positive) and the scale folded
+    // into the exponent's FMA.
     const bool full_vis = (k0 + KB - 1 <= q0) && (!P.sliding || k0 >= q0 + QB - P.window);
     float mx = -INFINITY;
+    if (full_vis) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float s = S[kb][r] * P.scale_log2;
-        if (!full_vis) {
-          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool vis = key <= qw && (!P.sliding || key > qw - P.window);
-          s = vis ? s : -INFINITY;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][r]);
+    } else {
+      // Key k0 + c is visible to query qw iff 0 <= qw - k0 - c < window (causal: window =
+      // 2^31 - 1), one unsigned compare.
+      const unsigned wlim = P.sliding ? (unsigned)P.window : 0x7fffffffu;
+      const int dq = qw - k0 - 4 * half;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float sc = ((unsigned)(dq - (32 * kb + 8 * (r >> 2) + (r & 3))) < wlim) ? S[kb][r] : -INFINITY;
+          S[kb][r] = sc;
+          mx = fmaxf(mx, sc);
         }
-        S[kb][r] = s;
-        mx = fmaxf(mx, s);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    }
+    mx = pair32_max(mx) * P.scale_log2;
+    // Raise the reference only when this tile's maximum is more than kLazyMax above it
+    // (always on a row's first visible tile, where m_run = -inf). alpha = 2^(m_old - m_new)
+    // is 1 when the reference stays and 0 on the first raise.
+    const bool raise = mx > m_run + kLazyMax;
+    const float alpha = __builtin_amdgcn_exp2f(raise ? m_run - mx : 0.f);
+    m_run = raise ? mx : m_run;
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[i][r] *= alpha;
+    }
+    // Rows with no visible key yet keep m_run = -inf and get p = 0 (their scores are -inf).
+    const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
     float rs = 0.f;
     bf16x8_t pf[2][2];
 #pragma unroll
@@ -149,17 +176,11 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const float p = exp2f(S[kb][8 * st + t] - m_use);
+          const float p = __builtin_amdgcn_exp2f(fmaf(S[kb][8 * st + t], P.scale_log2, neg_m));
           rs += p;
           pf[kb][st][t] = (__bf16)p;
         }
-    rs += __shfl_xor(rs, 32, 64);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < DB; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) O[i][r] *= alpha;
+    l_run = l_run * alpha + pair32_sum(rs);
 
     // O^T[d, q] += sum_key V[key, d] P[q, key]. The V^T operand comes from two
     // transpose reads: lane m of each 16-lane group addresses row key0 + m / 4,

@@ -73,6 +73,28 @@ __device__ __forceinline__ float quad_xor2(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
 }
 
+// Max / sum of x over the lane pair (l, l ^ 32) with gfx950's v_permlane32_swap (one
+// VALU op, no LDS). Both lanes of a pair get bitwise the same result. The two results
+// of the swap are copied to scalars before reinterpreting them: hipcc lowers
+// __builtin_bit_cast applied directly to an element of the returned vector as element 0.
+__device__ __forceinline__ void pair32_swap(float x, float& lo, float& hi) {
+  const unsigned a = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  lo = __builtin_bit_cast(float, r0);  // x of lane l & 31
+  hi = __builtin_bit_cast(float, r1);  // x of lane (l & 31) + 32
+}
+__device__ __forceinline__ float pair32_max(float x) {
+  float lo, hi;
+  pair32_swap(x, lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  float lo, hi;
+  pair32_swap(x, lo, hi);
+  return lo + hi;
+}
+
 // 4 x 4 transpose inside each quad of lanes (q = lane & 3), in registers. On entry
 // lane q holds rows 0..3 of column q (v[r] = X[r][q]); on exit it holds columns 0..3
 // of row 2 (q & 1) + (q >> 1) (v[c] = X[row][c]). Used to turn MFMA result columns

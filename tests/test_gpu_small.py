@@ -127,6 +127,8 @@ PREFILL_CASES = [
     ("bf16", "full", 64, 8, 4, 512, 256, 0, 1, 130),
     ("bf16", "sliding", 128, 8, 1, 512, 1024, 1, 1, 70),    # window of one key
     ("bf16", "sliding", 128, 2, 2, 256, 256, 5000, 1, 257),  # window >= L
+    ("bf16", "sliding", 128, 4, 2, 256, 256, 300, 1, 700),   # window spans several key tiles
+    ("bf16", "full", 128, 2, 1, 256, 256, 0, 1, 600),        # several 256-query blocks, ragged tail
 ]
 
 
