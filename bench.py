@@ -12,8 +12,11 @@ and the 4-layer stack prefill with deepstack plus tied 256000-vocab logits.
 
 "roofline" describes the dominant kernel of the headline step (the fused projection
 GEMM): algorithmic flops per launch / its mean launch time from HIP events recorded
-around every launch in the timed region. "cpu_baseline" is the fp64 oracle timed on
-this host on one full layer of the same workload.
+around every launch while the timed steps are repeated (the throughput itself is timed
+without the events). "traffic" is its HBM bytes per launch from committed rocprofv3
+counter passes (profiles/gemm_proj_c1_traffic.json) while they match the current kernel
+sources. "cpu_baseline" is the fp64 oracle timed on this host on one full layer of the
+same workload.
 """
 from __future__ import annotations
 
@@ -59,19 +62,26 @@ def kernel_stats(b, names):
 
 
 def timed(fn, steps, warmup, b, torch):
+    """Warm up, then time `steps` steps twice on the same inputs: first plain (the step
+    time reported as throughput), then with a HIP event pair recorded around every library
+    launch (per-kernel mean durations for the roofline; the events cost a few percent of
+    the step, so they stay out of the throughput figure)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    b.compass_profile_reset()
-    b.compass_profile_enable(True)
     t0 = time.perf_counter()
     for _ in range(steps):
         fn()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    sec = (time.perf_counter() - t0) / steps
+    b.compass_profile_reset()
+    b.compass_profile_enable(True)
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
     b.compass_profile_enable(False)
     stats = kernel_stats(b, b.compass_profile_kernel_names())
-    return (t1 - t0) / steps, stats
+    return sec, stats
 
 
 # ------------------------------------------------------------------------ workloads

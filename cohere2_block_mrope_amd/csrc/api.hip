@@ -266,6 +266,8 @@ int compass_mrope_positions(const int32_t* token_ids, int32_t B, int32_t L, int3
                             int32_t* pos, int32_t* rope_delta, int32_t* status, void* stream) {
   if (B < 1 || L < 1) return fail(COMPASS_E_INVALID, "B=%d, L=%d must be >= 1", B, L);
   if ((long long)B * L * 3 > (1LL << 31) - 1) return fail(COMPASS_E_UNSUPPORTED, "B*L too large");
+  if (L > COMPASS_MAX_TOKENS_PER_ROW)
+    return fail(COMPASS_E_UNSUPPORTED, "L=%d exceeds COMPASS_MAX_TOKENS_PER_ROW=%d", L, COMPASS_MAX_TOKENS_PER_ROW);
   if (!token_ids || !img_offset || !pos || !rope_delta || !status)
     return fail(COMPASS_E_INVALID, "NULL pointer argument");
   if (spatial_merge < 1) return fail(COMPASS_E_INVALID, "spatial_merge %d < 1", spatial_merge);

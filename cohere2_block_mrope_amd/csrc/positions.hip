@@ -3,11 +3,13 @@
 // an image get start + (t_i, h_i, w_i) on the merged grid; the next text token
 // starts at max position + 1; rope_delta = max position + 1 - L.
 //
-// One workgroup per row. The images of a row are walked in order by the whole
-// workgroup: each step finds the next pad token with a cooperative scan, checks
-// the image's span, and records (start, end, first position, offset after). The
-// positions of all L tokens are then written in parallel from those records.
-// Errors are detected in the order a left-to-right walk over the tokens meets them.
+// One 1024-thread workgroup per row. The row's tokens are read once, coalesced, into an
+// LDS bitmask of image-pad tokens (one ballot per wave and 64 tokens). The images of the
+// row are then walked in order on that mask: each step finds the next pad with one
+// parallel pass over the mask words, checks the image's span, and records (start, end,
+// first position, offset after). The positions of all L tokens are then written in
+// parallel from those records. Errors are detected in the order a left-to-right walk
+// over the tokens meets them.
 #include "common.h"
 #include "launch.h"
 #include "../../include/compass.h"
@@ -16,36 +18,49 @@ namespace compass {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
 constexpr int kMaxImg = COMPASS_MAX_IMAGES_PER_ROW;
+constexpr int kRecInts = 6 * kMaxImg;  // per-image records in dynamic LDS, then the mask
 
 __global__ __launch_bounds__(kThreads) void positions_kernel(
     const int32_t* __restrict__ tok, int L, int image_id, const int32_t* __restrict__ grid,
     const int32_t* __restrict__ img_off, int merge, int32_t* __restrict__ pos,
     int32_t* __restrict__ delta, int32_t* __restrict__ status, int B) {
-  __shared__ int s_start[kMaxImg];
-  __shared__ int s_end[kMaxImg];
-  __shared__ int s_base[kMaxImg];   // position of the image's first pad (t, h, w all equal)
-  __shared__ int s_after[kMaxImg];  // text offset (position - index) after the image
-  __shared__ int s_gh[kMaxImg];
-  __shared__ int s_gw[kMaxImg];
+  extern __shared__ __align__(16) int smem[];
+  int* s_start = smem;                  // first pad of image k
+  int* s_end = smem + kMaxImg;          // one past its last pad
+  int* s_base = smem + 2 * kMaxImg;     // position of the image's first pad (t, h, w all equal)
+  int* s_after = smem + 3 * kMaxImg;    // text offset (position - index) after the image
+  int* s_gh = smem + 4 * kMaxImg;
+  int* s_gw = smem + 5 * kMaxImg;
+  uint32_t* s_mask = reinterpret_cast<uint32_t*>(smem + kRecInts);  // bit l: token l is a pad
   __shared__ int s_found;
   __shared__ int s_bad;
   __shared__ int s_err;
   __shared__ int s_nimg;
 
   const int b = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t* row = tok + (size_t)b * L;
   const int k0 = img_off[b];
   const int nimg = img_off[b + 1] - k0;
+  const int nw = (L + 31) >> 5;
 
   if (tid == 0) { s_err = COMPASS_POS_OK; s_nimg = 0; }
-  __syncthreads();
   if (nimg > kMaxImg || nimg < 0) {
     if (tid == 0) status[b] = COMPASS_POS_TOO_MANY_IMAGES;
     return;
   }
+  // Pad bitmask: wave w covers tokens 64 i .. 64 i + 63 for i = w, w + 16, ...
+  for (int base = 64 * wave; base < L; base += 64 * (kThreads / 64)) {
+    const int idx = base + lane;
+    const uint64_t bal = __ballot(idx < L && row[idx] == image_id);
+    if (lane == 0) {
+      s_mask[base >> 5] = (uint32_t)bal;
+      if ((base >> 5) + 1 < nw) s_mask[(base >> 5) + 1] = (uint32_t)(bal >> 32);
+    }
+  }
+  __syncthreads();
 
   int p = 0;        // next token index the walk has not consumed
   int offset = 0;   // position - index of text tokens at p
@@ -53,28 +68,19 @@ __global__ __launch_bounds__(kThreads) void positions_kernel(
     // Next pad token at or after p (L if none).
     if (tid == 0) s_found = L;
     __syncthreads();
-    for (int base = p; base < L; base += kThreads * 4) {
-      int best = L;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        int idx = base + u * kThreads + tid;
-        if (idx < L && row[idx] == image_id) best = min(best, idx);
-      }
-      if (best < L) atomicMin(&s_found, best);
-      __syncthreads();
-      int f = s_found;
-      __syncthreads();
-      if (f < L) break;
+    for (int w = (p >> 5) + tid; w < nw; w += kThreads) {
+      uint32_t m = s_mask[w];
+      if (w == (p >> 5)) m &= ~0u << (p & 31);
+      if (m) atomicMin(&s_found, 32 * w + __ffs((int)m) - 1);
     }
+    __syncthreads();
     const int sidx = s_found;
     if (k == nimg) {  // all images consumed: any pad left over is an error
       if (tid == 0 && sidx < L) s_err = COMPASS_POS_EXTRA_PADS;
-      __syncthreads();
       break;
     }
     if (sidx >= L) {
       if (tid == 0) s_err = COMPASS_POS_UNUSED_IMAGES;
-      __syncthreads();
       break;
     }
     const int t = grid[(size_t)(k0 + k) * 3 + 0];
@@ -82,29 +88,31 @@ __global__ __launch_bounds__(kThreads) void positions_kernel(
     const int w = grid[(size_t)(k0 + k) * 3 + 2];
     if (t < 1 || h < 1 || w < 1 || h % merge || w % merge) {
       if (tid == 0) s_err = COMPASS_POS_BAD_GRID;
-      __syncthreads();
       break;
     }
     const int gh = h / merge, gw = w / merge;
     const long long nll = (long long)t * gh * gw;
     if (nll > (long long)(L - sidx)) {
       if (tid == 0) s_err = COMPASS_POS_SPAN_MISMATCH;
-      __syncthreads();
       break;
     }
     const int n = (int)nll;
+    // Every token of [sidx, sidx + n) must be a pad.
     if (tid == 0) s_bad = 0;
     __syncthreads();
-    int bad = 0;
-    for (int idx = sidx + tid; idx < sidx + n; idx += kThreads) bad |= (row[idx] != image_id);
-    if (bad) s_bad = 1;
+    const int wlo = sidx >> 5, whi = (sidx + n - 1) >> 5;
+    for (int wi = wlo + tid; wi <= whi; wi += kThreads) {
+      uint32_t need = ~0u;
+      if (wi == wlo) need &= ~0u << (sidx & 31);
+      if (wi == whi) need &= ~0u >> (31 - ((sidx + n - 1) & 31));
+      if ((s_mask[wi] & need) != need) s_bad = 1;
+    }
     __syncthreads();
     if (s_bad) {
       if (tid == 0) s_err = COMPASS_POS_SPAN_MISMATCH;
-      __syncthreads();
       break;
     }
-    const int first = sidx + offset;          // position of the image's first pad
+    const int first = sidx + offset;  // position of the image's first pad
     const int adv = max(t, max(gh, gw));
     if (tid == 0) {
       s_start[k] = sidx;
@@ -117,7 +125,6 @@ __global__ __launch_bounds__(kThreads) void positions_kernel(
     }
     offset = first + adv - (sidx + n);
     p = sidx + n;
-    __syncthreads();
   }
   __syncthreads();
   const int err = s_err;
@@ -131,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void positions_kernel(
     // Last image whose span starts at or before l.
     int lo = 0, hi = ni - 1, kk = -1;
     while (lo <= hi) {
-      int mid = (lo + hi) >> 1;
+      const int mid = (lo + hi) >> 1;
       if (s_start[mid] <= l) { kk = mid; lo = mid + 1; } else { hi = mid - 1; }
     }
     int pt_t, pt_h, pt_w;
@@ -157,8 +164,16 @@ __global__ __launch_bounds__(kThreads) void positions_kernel(
 hipError_t launch_positions(const int32_t* tok, int B, int L, int image_id, const int32_t* grid,
                             const int32_t* img_off, int merge, int32_t* pos, int32_t* delta,
                             int32_t* status, hipStream_t s) {
-  positions_kernel<<<B, kThreads, 0, s>>>(tok, L, image_id, grid, img_off, merge, pos, delta,
-                                          status, B);
+  const size_t lds = sizeof(int) * ((size_t)kRecInts + ((size_t)L + 31) / 32);
+  static bool attr_set = false;
+  if (!attr_set) {
+    const size_t max_lds = sizeof(int) * ((size_t)kRecInts + COMPASS_MAX_TOKENS_PER_ROW / 32);
+    hipError_t e = hipFuncSetAttribute((const void*)positions_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)max_lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  positions_kernel<<<B, kThreads, lds, s>>>(tok, L, image_id, grid, img_off, merge, pos, delta, status, B);
   return hipGetLastError();
 }
 

@@ -60,6 +60,7 @@ enum {
   COMPASS_POS_TOO_MANY_IMAGES = 5 /* more than COMPASS_MAX_IMAGES_PER_ROW images in a row */
 };
 #define COMPASS_MAX_IMAGES_PER_ROW 2048
+#define COMPASS_MAX_TOKENS_PER_ROW 524288 /* compass_mrope_positions: L above this is unsupported */
 
 /* One decoder layer's shape (host struct).
  * kind: COMPASS_SLIDING applies MRoPE and the window; COMPASS_FULL uses no
