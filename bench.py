@@ -38,7 +38,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-extra", action="store_true", help="headline workload only")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")

@@ -178,12 +178,22 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
 }
 
 // bf16 variant: the chunk's scores come from MFMA. For each 32-key block the wave computes
-// S^T = K Q^T with v_mfma_f32_32x32x16_bf16: operand A is 32 key rows (lane l loads key
-// l % 32, dims 8 (l / 32) + 16 ks .. + 8, straight from HBM into registers), operand B
-// holds the G query heads in columns 0..G-1 (other columns zero). Lanes whose column is
-// a real head then hold 16 keys' scores each, so no cross-lane reduction is needed for
-// q . k. The PV product stays on the vector ALUs: each key row is read by hd / 8 lanes
-// with 16-byte loads and the four key groups of a wave are summed once at the end.
+// S^T = K Q^T with v_mfma_f32_32x32x16_bf16: operand A is 32 key rows (lane l holds key
+// l % 32, dims 8 (l / 32) + 16 ks .. + 8), operand B holds the G query heads in columns
+// 0..G-1 (other columns zero). Lanes whose column is a real head then hold 16 keys'
+// scores each, so no cross-lane reduction is needed for q . k.
+// K and V rows are streamed with nontemporal 16-byte loads, hd / 8 lanes per row (whole
+// rows per instruction: the nontemporal path only pays off for fully coalesced rows).
+// Each wave's 64 K rows go through its own LDS tile, 16-byte chunks XOR-swizzled by row,
+// from which the MFMA operand is read without bank conflicts. The PV product stays on
+// the vector ALUs: each V row is read by hd / 8 lanes and the four key groups of a wave
+// are summed once at the end.
+template <int HD>
+__device__ __forceinline__ int dk_swz(int row, int chunk) {  // 16-byte slot of (row, chunk)
+  if constexpr (HD == 128) return row * 16 + (chunk ^ (row & 15));
+  else return row * 8 + (chunk ^ ((row >> 1) & 7));
+}
+
 template <int HD, int G>
 __global__ __launch_bounds__(256) void decode_attn_mfma_kernel(const bf16_t* __restrict__ q,
                                                                const bf16_t* __restrict__ k,
@@ -193,12 +203,15 @@ __global__ __launch_bounds__(256) void decode_attn_mfma_kernel(const bf16_t* __r
                                                                float scale_log2, int n_chunks,
                                                                float* __restrict__ part) {
   constexpr int KS = HD / 16;          // k-steps of 16 dims
-  constexpr int LPK = HD / 8;          // lanes per V row in the PV product
-  constexpr int KPS = 64 / LPK;        // V rows per wave step
-  constexpr int STEPS = 64 / KPS;      // 64 keys per wave
+  constexpr int LPK = HD / 8;          // lanes per K / V row (16-byte chunks per row)
+  constexpr int KPS = 64 / LPK;        // rows per wave load instruction
+  constexpr int STEPS = 64 / KPS;      // load instructions for the wave's 64 rows
+  // Per-wave K tiles; reused for the per-wave output partials once every wave is done.
+  __shared__ __align__(16) u32x4_t s_kbuf[4 * 64 * LPK];
   __shared__ float s_p[G][CHUNK];
   __shared__ float s_red[G][4];
-  __shared__ float s_o[4][G][HD];
+  static_assert(sizeof(float) * 4 * G * HD <= sizeof(u32x4_t) * 4 * 64 * LPK, "s_o must fit in the K tiles");
+  float (*s_o)[G][HD] = reinterpret_cast<float (*)[G][HD]>(s_kbuf);
 
   const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -219,23 +232,20 @@ __global__ __launch_bounds__(256) void decode_attn_mfma_kernel(const bf16_t* __r
   const bf16_t* kb = k + ((size_t)b * Hkv + kvh) * cap * HD;
   const bf16_t* vb = v + ((size_t)b * Hkv + kvh) * cap * HD;
 
-  // K fragments of this wave's two 32-key blocks (keys clamped to the visible range).
+  // K and V rows of this wave's 64 keys (clamped to the visible range), whole rows per
+  // instruction: lane l reads chunk l % LPK of row KPS i + l / LPK.
   const int col = lane & 31, half = lane >> 5;
-  u32x4_t kr[2][KS];
-#pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2) {
-    const int key = min(kbeg + 64 * wave + 32 * kb2 + col, kend - 1);
-    const bf16_t* kp = kb + (size_t)key * HD + 8 * half;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kr[kb2][ks] = *reinterpret_cast<const u32x4_t*>(kp + 16 * ks);
-  }
-  // V rows for the PV product, issued now so they stream while the scores are formed.
   const int sub = lane % LPK, kin = lane / LPK;
-  u32x4_t vr[STEPS];
+  u32x4_t kr[STEPS], vr[STEPS];
 #pragma unroll
   for (int st = 0; st < STEPS; ++st) {
     const int key = min(kbeg + 64 * wave + st * KPS + kin, kend - 1);
-    vr[st] = *reinterpret_cast<const u32x4_t*>(vb + (size_t)key * HD + 8 * sub);
+    kr[st] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + (size_t)key * HD + 8 * sub));
+  }
+#pragma unroll
+  for (int st = 0; st < STEPS; ++st) {
+    const int key = min(kbeg + 64 * wave + st * KPS + kin, kend - 1);
+    vr[st] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vb + (size_t)key * HD + 8 * sub));
   }
   // Q^T operand: column `col` is head col (zero beyond G).
   bf16x8_t qf[KS];
@@ -249,14 +259,20 @@ __global__ __launch_bounds__(256) void decode_attn_mfma_kernel(const bf16_t* __r
       qf[ks] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
+  u32x4_t* kt = s_kbuf + 64 * LPK * wave;
+#pragma unroll
+  for (int st = 0; st < STEPS; ++st) kt[dk_swz<HD>(st * KPS + kin, sub)] = kr[st];
+  __syncthreads();
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2) {
     f32x16_t sacc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kr[kb2][ks]), qf[ks], sacc, 0, 0, 0);
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4_t kf = kt[dk_swz<HD>(32 * kb2 + col, 2 * ks + half)];
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf), qf[ks], sacc, 0, 0, 0);
+    }
     if (col < G) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
