@@ -192,10 +192,12 @@ PrefillWs prefill_ws(const compass_layer_desc* d, long long B, long long L) {
   return w;
 }
 
-// Split-K factor for the skinny decode GEMMs: enough workgroups (about 1024) to keep the
-// weight stream's loads in flight, with at least 256 K per split.
+// Split-K factor of the skinny decode GEMMs: about 512 workgroups in total (measured on
+// MI355X: more splits cost more in the partial-sum traffic than they gain in
+// parallelism), and at least 256 K elements per split.
 int decode_splits(long long tiles, long long K) {
-  long long s = 1024 / (tiles > 0 ? tiles : 1);
+  if (tiles < 1) tiles = 1;
+  long long s = (512 + tiles - 1) / tiles;
   if (s > K / 256) s = K / 256;
   if (s < 1) s = 1;
   return (int)s;

@@ -115,10 +115,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams P) {
       ra[p] = *reinterpret_cast<const u32x4_t*>(P.A + aoff[p] + k0);
     } else {
       const int i = p - A_PER_T;
-      if (BKIND == 2 && k0 >= P.bm.ksplit)
-        rb[i] = *reinterpret_cast<const u32x4_t*>(bbase1 + boff1[i] + k0);
-      else
-        rb[i] = *reinterpret_cast<const u32x4_t*>(bbase0 + boff[i] + k0);
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(
+          (BKIND == 2 && k0 >= P.bm.ksplit) ? bbase1 + boff1[i] + k0 : bbase0 + boff[i] + k0);
+      // Split-K skinny GEMMs (decode) read each weight once: stream it past the caches.
+      if constexpr (MODE == MODE_RAW) rb[i] = __builtin_nontemporal_load(src);
+      else rb[i] = *src;
     }
   };
   auto store_piece = [&](int buf, int p) __attribute__((always_inline)) {
