@@ -350,46 +350,50 @@ __global__ __launch_bounds__(256) void decode_attn_mfma_kernel(const bf16_t* __r
   }
 }
 
-// Merge the chunk partials of one (row, head): weights 2^(m_c - M) from the chunk maxima,
-// loaded in parallel into LDS; each thread then owns output dimensions d.
+// Merge the chunk partials of one (row, head): thread d owns output dimension d. Chunks
+// are taken 16 at a time with every load of the group issued up front (chunk max, sum
+// and the thread's output dimension), merged with an online maximum, so the merge costs
+// about one memory round trip per 16 chunks. Weights are 2^(m_c - M); empty chunks
+// (max -inf, only their statistics written) are skipped.
 template <typename T, int HD>
-__global__ __launch_bounds__(128) void decode_combine_kernel(const float* __restrict__ part,
-                                                             const int32_t* __restrict__ lens, int Hq,
-                                                             int cap, int n_chunks, T* __restrict__ o,
-                                                             int ldo) {
-  constexpr int MAXC = 512;  // chunk statistics held in LDS per pass
-  __shared__ float s_w[MAXC];
-  __shared__ float s_red[2];
-  const int bh = blockIdx.x, b = bh / Hq, h = bh % Hq, tid = threadIdx.x;
+__global__ __launch_bounds__(HD) void decode_combine_kernel(const float* __restrict__ part,
+                                                            const int32_t* __restrict__ lens, int Hq,
+                                                            int cap, int n_chunks, T* __restrict__ o,
+                                                            int ldo) {
+  constexpr int CG = 16;  // chunks per group
+  const int bh = blockIdx.x, b = bh / Hq, h = bh % Hq, d = threadIdx.x;
   const int n = lens[b];
   if (n < 0 || n >= cap) return;
   const float* p = part + (size_t)bh * n_chunks * (HD + 2);
-  // Global max over all chunks (strided over threads, then a block reduction).
-  float mx = -INFINITY;
-  for (int c = tid; c < n_chunks; c += 128) mx = fmaxf(mx, p[(size_t)c * (HD + 2) + HD]);
-  mx = wave_max(mx);
-  if ((tid & 63) == 0) s_red[tid >> 6] = mx;
-  __syncthreads();
-  const float M = fmaxf(s_red[0], s_red[1]);
-  float acc = 0.f, l = 0.f;
-  for (int c0 = 0; c0 < n_chunks; c0 += MAXC) {
-    const int nc = min(MAXC, n_chunks - c0);
-    __syncthreads();
-    for (int c = tid; c < nc; c += 128) {
-      const float mc = p[(size_t)(c0 + c) * (HD + 2) + HD];
-      s_w[c] = (mc == -INFINITY) ? 0.f : exp2f(mc - M);
+  float M = -INFINITY, l = 0.f, acc = 0.f;
+  for (int c0 = 0; c0 < n_chunks; c0 += CG) {
+    float mc[CG], lc[CG], oc[CG];
+#pragma unroll
+    for (int j = 0; j < CG; ++j) {
+      const int c = min(c0 + j, n_chunks - 1);
+      const float* pc = p + (size_t)c * (HD + 2);
+      mc[j] = (c0 + j < n_chunks) ? pc[HD] : -INFINITY;
+      lc[j] = pc[HD + 1];
+      oc[j] = pc[d];
     }
-    __syncthreads();
-#pragma unroll 8
-    for (int c = 0; c < nc; ++c) {
-      const float w = s_w[c];
-      if (w == 0.f) continue;  // empty chunk: only its max and sum were written
-      const float* pc = p + (size_t)(c0 + c) * (HD + 2);
-      l += w * pc[HD + 1];
-      if (tid < HD) acc += w * pc[tid];
+    float mb = M;
+#pragma unroll
+    for (int j = 0; j < CG; ++j) mb = fmaxf(mb, mc[j]);
+    if (mb == -INFINITY) continue;  // nothing visible yet
+    const float r = (M == -INFINITY) ? 0.f : exp2f(M - mb);
+    l *= r;
+    acc *= r;
+#pragma unroll
+    for (int j = 0; j < CG; ++j) {
+      // Skipped, not weighted by 0: an empty chunk's output slots are never written.
+      if (mc[j] == -INFINITY) continue;
+      const float w = exp2f(mc[j] - mb);
+      l += w * lc[j];
+      acc += w * oc[j];
     }
+    M = mb;
   }
-  if (tid < HD) o[(size_t)b * ldo + (size_t)h * HD + tid] = Elt<T>::from_f(acc / l);
+  o[(size_t)b * ldo + (size_t)h * HD + d] = Elt<T>::from_f(acc / l);
 }
 
 template <typename T, int HD>
@@ -450,10 +454,10 @@ hipError_t launch_decode_combine(int dtype, const float* part, const int32_t* le
   const dim3 grid(B * Hq);
   if (dtype == 1) {
     if (hd == 128) decode_combine_kernel<bf16_t, 128><<<grid, 128, 0, s>>>(part, lens, Hq, cap, n_chunks, (bf16_t*)o, ldo);
-    else decode_combine_kernel<bf16_t, 64><<<grid, 128, 0, s>>>(part, lens, Hq, cap, n_chunks, (bf16_t*)o, ldo);
+    else decode_combine_kernel<bf16_t, 64><<<grid, 64, 0, s>>>(part, lens, Hq, cap, n_chunks, (bf16_t*)o, ldo);
   } else {
     if (hd == 128) decode_combine_kernel<float, 128><<<grid, 128, 0, s>>>(part, lens, Hq, cap, n_chunks, (float*)o, ldo);
-    else decode_combine_kernel<float, 64><<<grid, 128, 0, s>>>(part, lens, Hq, cap, n_chunks, (float*)o, ldo);
+    else decode_combine_kernel<float, 64><<<grid, 64, 0, s>>>(part, lens, Hq, cap, n_chunks, (float*)o, ldo);
   }
   return hipGetLastError();
 }
