@@ -25,11 +25,23 @@ __global__ __launch_bounds__(256) void proj_epilogue_kernel(const float* __restr
   const int m = (int)(idx / units);
   const int u = (int)(idx - (long long)m * units);
   const size_t slab = (size_t)M * N;
+  // Sum of the split-K partials of column c, four splits' loads in flight at a time.
   auto sum = [&](int c) {
+    const float* r = raw + (size_t)m * N + c;
     float s = 0.f;
-    for (int z = 0; z < splits; ++z) s += raw[z * slab + (size_t)m * N + c];
+    int z = 0;
+    for (; z + 4 <= splits; z += 4)
+      s += (r[z * slab] + r[(z + 1) * slab]) + (r[(z + 2) * slab] + r[(z + 3) * slab]);
+    for (; z < splits; ++z) s += r[z * slab];
     return s;
   };
+  // The columns' sums are loaded before the row's cache index (independent loads).
+  const bool gu = u >= qkv_units;
+  const int hh = u / half, f = u - hh * half;
+  const int c1 = hh * hd + f;
+  const int cg = u - qkv_units;                                             // gate/up column
+  const int vg = (E.nq64 + 2 * E.nk64) * 64 + (cg >> 6) * 128 + (cg & 63);  // virtual gate col
+  float x1 = sum(gu ? vg : c1), x2 = sum(gu ? vg + 64 : c1 + half);
   int b, l;
   if (E.decode) {
     b = m; l = E.lens[b];
@@ -37,17 +49,11 @@ __global__ __launch_bounds__(256) void proj_epilogue_kernel(const float* __restr
   } else {
     b = m / E.L; l = m - b * E.L;
   }
-  if (u >= qkv_units) {
-    const int c = u - qkv_units;                                   // gate/up column
-    const int vg = (E.nq64 + 2 * E.nk64) * 64 + (c >> 6) * 128 + (c & 63);  // virtual gate col
-    const float g = sum(vg), up = sum(vg + 64);
+  if (gu) {
     T* act = (T*)E.act;
-    act[(size_t)m * E.ldact + E.act_col0 + c] = Elt<T>::from_f(silu_f(g) * up);
+    act[(size_t)m * E.ldact + E.act_col0 + cg] = Elt<T>::from_f(silu_f(x1) * x2);
     return;
   }
-  const int hh = u / half, f = u - hh * half;
-  const int c1 = hh * hd + f;
-  float x1 = sum(c1), x2 = sum(c1 + half);
   T* dst;
   if (hh < E.Hq) {
     dst = (T*)E.q + (((size_t)b * E.Hq + hh) * E.Lq + (E.decode ? 0 : l)) * hd;
@@ -74,13 +80,18 @@ __global__ __launch_bounds__(256) void splitk_resid_kernel(const float* __restri
                                                            const int32_t* __restrict__ lens, int cap) {
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (long long)M * N) return;
+  const size_t slab = (size_t)M * N;
+  const float* r = raw + idx;
+  float s = 0.f;
+  int z = 0;
+  for (; z + 4 <= splits; z += 4)  // four splits' loads in flight at a time
+    s += (r[z * slab] + r[(z + 1) * slab]) + (r[(z + 2) * slab] + r[(z + 3) * slab]);
+  for (; z < splits; ++z) s += r[z * slab];
   if (lens) {  // decode: rows whose cache index is out of range are left untouched
     const int l = lens[idx / N];
     if (l < 0 || l >= cap) return;
   }
-  float s = Elt<T>::to_f(x[idx]);
-  for (int z = 0; z < splits; ++z) s += raw[(size_t)z * M * N + idx];
-  out[idx] = Elt<T>::from_f(s);
+  out[idx] = Elt<T>::from_f(Elt<T>::to_f(x[idx]) + s);
 }
 
 template <typename T>
