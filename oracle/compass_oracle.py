@@ -24,6 +24,8 @@ the design notes of the repository):
   * Deepstack rows are added after the layer's residual sum.
   * Decode: the new token's key/value sit at cache index n = lens[b]; it sees
     keys n - W < j <= n (sliding) or j <= n (full).
+  * Chunked prefill: new token i of row b sits at cache index start[b] + i, with
+    the same visibility rule as decode.
 """
 from __future__ import annotations
 
@@ -319,6 +321,47 @@ def layer_decode(shape, w: Dict[str, np.ndarray], x: np.ndarray, pos: np.ndarray
         out = x[b] + (o @ np.asarray(w["wo"], dtype=F64).T)[0] + (act @ np.asarray(w["w_down"], dtype=F64).T)[0]
         outs.append(out); ks.append(kh[:, 0, :]); vs.append(vh[:, 0, :])
     return np.stack(outs), np.stack(ks), np.stack(vs)
+
+
+# ----------------------------------------------------------------------------------------
+# Chunked prefill. Page 5 ("feat(mm): serve image input on the Qwen families", "How it fits
+# together") serves prompts through chunked prefill over a prefix cache, with image spans
+# crossing chunk boundaries; page 1 keeps a dense cache with the window as a mask
+# ("Acceptance criteria" correction). A chunk of L new tokens in row b continues a cache
+# that already holds start[b] tokens: new token i sits at cache index n = start[b] + i,
+# its key/value (rotated on sliding layers) are appended there, and it sees keys j <= n
+# (and j > n - W on sliding layers) over cache and chunk together. With L = 1 this is
+# the decode step; with start = 0 it is the plain prefill.
+# ----------------------------------------------------------------------------------------
+def layer_prefill_chunk(shape, w: Dict[str, np.ndarray], x: np.ndarray, pos: Optional[np.ndarray],
+                        k_cache: np.ndarray, v_cache: np.ndarray, start: np.ndarray):
+    """x [B, L, D]; pos [3, B, L] (sliding layers; the new tokens' positions); caches
+    [B, Hkv, cap, hd] holding at least start[b] tokens (read only here).
+
+    Returns (out [B, L, D], k_new [B, Hkv, L, hd], v_new [B, Hkv, L, hd]).
+    """
+    x = np.asarray(x, dtype=F64)
+    B, L, D = x.shape
+    Hq, Hkv, hd = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
+    out = np.empty_like(x)
+    k_new = np.empty((B, Hkv, L, hd), dtype=F64)
+    v_new = np.empty_like(k_new)
+    for b in range(B):
+        s0 = int(start[b])
+        a = layer_norm(x[b], w["ln_w"], shape.ln_eps)
+        q, k, v, g, u = projections(a, w)
+        qh, kh, vh = _heads(q, Hq, hd), _heads(k, Hkv, hd), _heads(v, Hkv, hd)
+        if shape.kind == "sliding":
+            ang = mrope_angles(pos[:, b, :], shape.mrope_section, shape.rope_theta, hd)
+            qh, kh = apply_rope(qh, ang), apply_rope(kh, ang)
+        kk = np.concatenate([np.asarray(k_cache[b, :, :s0, :], dtype=F64), kh], axis=1)
+        vv = np.concatenate([np.asarray(v_cache[b, :, :s0, :], dtype=F64), vh], axis=1)
+        o = attention(qh, kk, vv, shape.kind, shape.window, q_index=s0 + np.arange(L),
+                      k_index=np.arange(s0 + L))
+        act = silu(g) * u
+        out[b] = x[b] + o @ np.asarray(w["wo"], dtype=F64).T + act @ np.asarray(w["w_down"], dtype=F64).T
+        k_new[b], v_new[b] = kh, vh
+    return out, k_new, v_new
 
 
 # ----------------------------------------------------------------------------------------

@@ -89,6 +89,17 @@ def _silu_sigmoid_only(x):
     return 1.0 / (1.0 + np.exp(-x))
 
 
+_orig_chunk = O.layer_prefill_chunk
+
+
+def _chunk_ignores_cache(shape, w, x, pos, k_cache, v_cache, start):
+    return _orig_chunk(shape, w, x, pos, k_cache, v_cache, np.zeros_like(start))
+
+
+def _chunk_start_off_by_one(shape, w, x, pos, k_cache, v_cache, start):
+    return _orig_chunk(shape, w, x, pos, k_cache, v_cache, np.maximum(np.asarray(start) - 1, 0))
+
+
 MUTANTS = {
     "rotate_half sign": ("rotate_half", _rotate_half_wrong_sign),
     "pairwise rope": ("rotate_half", _rotate_half_pairwise),
@@ -102,6 +113,8 @@ MUTANTS = {
     "attention scale dropped": ("attention", _attention_no_scale),
     "full layer not causal": ("attention", _attention_not_causal),
     "silu term dropped": ("silu", _silu_sigmoid_only),
+    "chunk ignores the cache": ("layer_prefill_chunk", _chunk_ignores_cache),
+    "chunk start off by one": ("layer_prefill_chunk", _chunk_start_off_by_one),
 }
 
 PINS = [
@@ -115,6 +128,8 @@ PINS = [
     lambda: P.test_parallel_block_vs_library_routines("sliding", 3, 5),
     lambda: P.test_parallel_block_vs_library_routines("full", 0, 5),
     P.test_logits_vs_library_and_scale,
+    lambda: P.test_chunked_prefill_equals_one_prefill("sliding", 3),
+    lambda: P.test_chunked_prefill_equals_one_prefill("full", 0),
 ]
 
 

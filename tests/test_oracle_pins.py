@@ -359,6 +359,52 @@ def test_prefill_decode_consistency():
         np.testing.assert_allclose(out, full_out[:, L - 1], atol=1e-11)
 
 
+@pytest.mark.parametrize("kind,W", [("sliding", 3), ("sliding", 6), ("full", 0)])
+def test_chunked_prefill_equals_one_prefill(kind, W):
+    """A chunk continuing a cache of start[b] tokens gives the rows start[b].. of one prefill
+    of the whole row (ragged starts per row), and appends exactly that prefill's K/V."""
+    sh = tiny_shape(kind, W)
+    w = rand_weights(sh, seed=60)
+    starts = np.array([0, 3, 9])
+    Lc = 5
+    B, cap = len(starts), int(starts.max()) + Lc + 2
+    xr = np.random.default_rng(61).standard_normal((B, cap, sh.hidden))
+    posr = mixed_pos(B, cap, seed=62)
+    kc = np.full((B, sh.n_kv_heads, cap, sh.head_dim), np.nan)
+    vc = np.full_like(kc, np.nan)
+    x = np.empty((B, Lc, sh.hidden))
+    pos = np.empty((3, B, Lc), dtype=np.int64)
+    ref_out, ref_k, ref_v = [], [], []
+    for b, s0 in enumerate(starts):
+        n = s0 + Lc
+        full, st = O.layer_prefill(sh, w, xr[b:b + 1, :n], posr[:, b:b + 1, :n], return_stages=True)
+        kc[b, :, :s0], vc[b, :, :s0] = st["k"][0][:, :s0], st["v"][0][:, :s0]
+        x[b], pos[:, b] = xr[b, s0:n], posr[:, b, s0:n]
+        ref_out.append(full[0, s0:]); ref_k.append(st["k"][0][:, s0:]); ref_v.append(st["v"][0][:, s0:])
+    out, knew, vnew = O.layer_prefill_chunk(sh, w, x, pos, kc, vc, starts)
+    np.testing.assert_allclose(out, np.stack(ref_out), atol=1e-11)
+    np.testing.assert_allclose(knew, np.stack(ref_k), atol=1e-12)
+    np.testing.assert_allclose(vnew, np.stack(ref_v), atol=1e-12)
+
+
+def test_one_token_chunk_equals_decode():
+    for kind, W in (("sliding", 4), ("full", 0)):
+        sh = tiny_shape(kind, W)
+        w = rand_weights(sh, seed=63)
+        B, cap = 3, 12
+        lens = np.array([0, 5, 10])
+        r = np.random.default_rng(64)
+        kc = r.standard_normal((B, sh.n_kv_heads, cap, sh.head_dim))
+        vc = r.standard_normal(kc.shape)
+        x = r.standard_normal((B, sh.hidden))
+        pos = mixed_pos(B, 1, seed=65)[:, :, 0]
+        out_d, k_d, v_d = O.layer_decode(sh, w, x, pos, kc, vc, lens)
+        out_c, k_c, v_c = O.layer_prefill_chunk(sh, w, x[:, None], pos[:, :, None], kc, vc, lens)
+        np.testing.assert_allclose(out_c[:, 0], out_d, atol=1e-11)
+        np.testing.assert_allclose(k_c[:, :, 0], k_d, atol=1e-12)
+        np.testing.assert_allclose(v_c[:, :, 0], v_d, atol=1e-12)
+
+
 # ------------------------------------------------------------------------------ logits
 def test_logits_vs_library_and_scale():
     r = np.random.default_rng(60)
