@@ -63,6 +63,10 @@ _sig = {
     "compass_layer_prefill": (ctypes.c_int, [ctypes.POINTER(compass_layer_desc), ctypes.POINTER(compass_layer_weights),
                                              _I, _I, _P, _P, ctypes.POINTER(compass_kv), _P, _P, _I, _P, _P,
                                              ctypes.c_size_t, _P]),
+    "compass_layer_prefill_chunk": (ctypes.c_int, [ctypes.POINTER(compass_layer_desc),
+                                                   ctypes.POINTER(compass_layer_weights), _I, _I, _P, _P,
+                                                   ctypes.POINTER(compass_kv), _P, _P, _I, _P, _P,
+                                                   ctypes.c_size_t, _P]),
     "compass_layer_decode": (ctypes.c_int, [ctypes.POINTER(compass_layer_desc), ctypes.POINTER(compass_layer_weights),
                                             _I, _P, _P, ctypes.POINTER(compass_kv), _P, _P, ctypes.c_size_t, _P]),
     "compass_logits_workspace_size": (ctypes.c_size_t, [_I, _I, _I]),
@@ -152,6 +156,16 @@ def compass_layer_prefill(desc, weights: compass_layer_weights, x, pos, kv: Opti
                                       None if kv is None else ctypes.byref(kv), _ptr(ds_rows), _ptr(ds), n_ds,
                                       _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                       _stream(stream)))
+
+
+def compass_layer_prefill_chunk(desc, weights: compass_layer_weights, x, pos, kv: compass_kv, ds_rows, ds,
+                                out, workspace, stream=None) -> None:
+    B, L = x.shape[0], x.shape[1]
+    n_ds = 0 if ds_rows is None else int(ds_rows.numel())
+    _check(_lib.compass_layer_prefill_chunk(ctypes.byref(desc), ctypes.byref(weights), B, L, _ptr(x), _ptr(pos),
+                                            ctypes.byref(kv), _ptr(ds_rows), _ptr(ds), n_ds, _ptr(out),
+                                            _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                            _stream(stream)))
 
 
 def compass_layer_decode(desc, weights: compass_layer_weights, x, pos, kv: compass_kv, out, workspace,

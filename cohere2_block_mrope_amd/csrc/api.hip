@@ -292,10 +292,12 @@ size_t compass_workspace_size(const compass_layer_desc* d, int32_t B, int32_t L,
   return prefill_ws(d, B, L).total;
 }
 
-int compass_layer_prefill(const compass_layer_desc* d, const compass_layer_weights* w, int32_t B,
-                          int32_t L, const void* x, const int32_t* pos, const compass_kv* kv,
-                          const int32_t* ds_rows, const void* ds, int32_t n_ds, void* out,
-                          void* workspace, size_t ws_bytes, void* stream) {
+// Prefill of a [B, L] chunk. start == NULL: plain prefill (K/V at cache rows [0, L) when a
+// cache is given); start = kv->lens: the chunk continues the cache of each row.
+static int prefill_impl(const compass_layer_desc* d, const compass_layer_weights* w, int32_t B,
+                        int32_t L, const void* x, const int32_t* pos, const compass_kv* kv,
+                        const int32_t* start, const int32_t* ds_rows, const void* ds, int32_t n_ds,
+                        void* out, void* workspace, size_t ws_bytes, void* stream) {
   int rc = check_desc(d);
   if (rc) return rc;
   if ((rc = check_weights(w))) return rc;
@@ -348,11 +350,13 @@ int compass_layer_prefill(const compass_layer_desc* d, const compass_layer_weigh
   ep.q = q; ep.Lq = L;
   ep.kc = kc; ep.vc = vc; ep.cap = cap;
   ep.lens = nullptr;
+  ep.kv_start = start;
   ep.act = a2; ep.ldact = (int)m.K2; ep.act_col0 = (int)m.qd;
   ep.nq64 = (int)(m.qd / 64); ep.nk64 = (int)(m.Hkv * m.hd / 64);
   ep.I = (int)m.I;
   const RopeTable rt = rope_table(d);
   const BMap pb = proj_bmap(d, w), ob = out_bmap(d, w);
+  const RowStart rs{start, L, cap};
 
   (void)hipGetLastError();
   LAUNCH("layernorm", s, launch_layernorm(dt, x, w->ln_w, d->ln_eps, a, (int)T, (int)m.D, s));
@@ -363,17 +367,32 @@ int compass_layer_prefill(const compass_layer_desc* d, const compass_layer_weigh
     LAUNCH("proj_epilogue", s, launch_proj_epilogue(dt, raw, 1, (int)T, (int)m.Nv, ep, rt, s));
   }
   LAUNCH("attn_prefill", s, launch_attention_prefill(dt, q, kc, vc, B, (int)m.Hq, (int)m.Hkv, L, cap,
-                                                     (int)m.hd, sliding, d->window, a2, (int)m.K2, s));
+                                                     (int)m.hd, sliding, d->window, start, a2, (int)m.K2, s));
   if (dt == COMPASS_BF16) {
     LAUNCH("gemm_out", s, launch_gemm_bf16_resid(a2, (int)m.K2, (int)T, (int)m.K2, ob, (int)m.D, x, out,
-                                                 (int)m.D, s));
+                                                 (int)m.D, rs, s));
   } else {
     LAUNCH("gemm_out_f32", s, launch_gemm_f32_raw(a2, (int)m.K2, (int)T, (int)m.K2, ob, (int)m.D, 1, raw, 1.f, s));
-    LAUNCH("splitk_resid", s, launch_splitk_resid(dt, raw, 1, (int)T, (int)m.D, x, out, nullptr, 0, s));
+    LAUNCH("splitk_resid", s, launch_splitk_resid(dt, raw, 1, (int)T, (int)m.D, x, out, rs, s));
   }
   if (n_ds > 0)
-    LAUNCH("deepstack", s, launch_deepstack(dt, ds_rows, ds, n_ds, (int)m.D, (int)T, out, s));
+    LAUNCH("deepstack", s, launch_deepstack(dt, ds_rows, ds, n_ds, (int)m.D, (int)T, rs, out, s));
   return ok();
+}
+
+int compass_layer_prefill(const compass_layer_desc* d, const compass_layer_weights* w, int32_t B,
+                          int32_t L, const void* x, const int32_t* pos, const compass_kv* kv,
+                          const int32_t* ds_rows, const void* ds, int32_t n_ds, void* out,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  return prefill_impl(d, w, B, L, x, pos, kv, nullptr, ds_rows, ds, n_ds, out, workspace, ws_bytes, stream);
+}
+
+int compass_layer_prefill_chunk(const compass_layer_desc* d, const compass_layer_weights* w, int32_t B,
+                                int32_t L, const void* x, const int32_t* pos, const compass_kv* kv,
+                                const int32_t* ds_rows, const void* ds, int32_t n_ds, void* out,
+                                void* workspace, size_t ws_bytes, void* stream) {
+  if (!kv || !kv->lens) return fail(COMPASS_E_INVALID, "chunked prefill needs kv with lens (tokens already cached)");
+  return prefill_impl(d, w, B, L, x, pos, kv, kv->lens, ds_rows, ds, n_ds, out, workspace, ws_bytes, stream);
 }
 
 int compass_layer_decode(const compass_layer_desc* d, const compass_layer_weights* w, int32_t B,
@@ -446,8 +465,8 @@ int compass_layer_decode(const compass_layer_desc* d, const compass_layer_weight
     LAUNCH("gemm_out_decode", s, launch_gemm_bf16_raw(a2, (int)m.K2, B, (int)m.K2, ob, (int)m.D, ws.s2, raw2, s));
   else
     LAUNCH("gemm_out_decode", s, launch_gemm_f32_raw(a2, (int)m.K2, B, (int)m.K2, ob, (int)m.D, ws.s2, raw2, 1.f, s));
-  LAUNCH("splitk_resid", s, launch_splitk_resid(dt, raw2, ws.s2, B, (int)m.D, x, out, kv->lens,
-                                                kv->capacity, s));
+  LAUNCH("splitk_resid", s, launch_splitk_resid(dt, raw2, ws.s2, B, (int)m.D, x, out,
+                                                RowStart{kv->lens, 1, kv->capacity}, s));
   return ok();
 }
 

@@ -32,6 +32,7 @@ struct AttnParams {
   const bf16_t* v;
   int B, Hq, Hkv, L, cap;
   int sliding, window;
+  const int32_t* start;  // chunked prefill: query l of row b sits at cache index start[b] + l
   bf16_t* o;
   int ldo;
   float scale_log2;  // log2(e) / sqrt(hd)
@@ -61,7 +62,13 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
   const int g = P.Hq / P.Hkv, kvh = h / g;
   const int q0 = qb * QB;
   const int L = P.L;
-  const int qw = q0 + 32 * wave + (lane & 31);  // this lane's query
+  const int qw = q0 + 32 * wave + (lane & 31);  // this lane's query (row of the chunk)
+  // Cache index of the chunk's first query (rows whose chunk does not fit are computed
+  // as if it started at 0: in bounds, and their outputs are never stored by the layer).
+  int s0 = P.start ? P.start[b] : 0;
+  if (s0 < 0 || s0 > P.cap - L) s0 = 0;
+  const int a0 = s0 + q0;   // cache index of the workgroup's first query
+  const int aw = s0 + qw;   // cache index of this lane's query
   const int half = lane >> 5;
 
   // Q fragments (B operand of S^T): lane holds query qw, d = 16 ks + 8 half .. + 8.
@@ -72,8 +79,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
     for (int ks = 0; ks < QK; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * ks);
   }
 
-  const int q_hi = min(q0 + QB - 1, L - 1);
-  const int k_lo = P.sliding ? max(0, q0 - P.window + 1) : 0;
+  const int q_hi = s0 + min(q0 + QB - 1, L - 1);
+  const int k_lo = P.sliding ? max(0, a0 - P.window + 1) : 0;
   const int kt0 = k_lo / KB, kt1 = q_hi / KB;
 
   const bf16_t* kbase = P.k + ((size_t)b * P.Hkv + kvh) * P.cap * HD;
@@ -83,7 +90,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
 #pragma unroll
     for (int i = 0; i < LD_PER_T; ++i) {
       const int c = tid + 256 * i;
-      const int key = min(kt * KB + c / CH, L - 1);
+      const int key = min(kt * KB + c / CH, s0 + L - 1);
       const size_t off = (size_t)key * HD + 8 * (c % CH);
       rk[i] = *reinterpret_cast<const u32x4_t*>(kbase + off);
       rv[i] = *reinterpret_cast<const u32x4_t*>(vbase + off);
@@ -132,7 +139,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
     // Mask only tiles that are not entirely visible to every query of the workgroup.
     // The maximum is taken on raw scores (the scale is positive) and the scale folded
     // into the exponent's FMA.
-    const bool full_vis = (k0 + KB - 1 <= q0) && (!P.sliding || k0 >= q0 + QB - P.window);
+    const bool full_vis = (k0 + KB - 1 <= a0) && (!P.sliding || k0 >= a0 + QB - P.window);
     float mx = -INFINITY;
     if (full_vis) {
 #pragma unroll
@@ -140,10 +147,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][r]);
     } else {
-      // Key k0 + c is visible to query qw iff 0 <= qw - k0 - c < window (causal: window =
-      // 2^31 - 1), one unsigned compare.
+      // Key k0 + c is visible to the query at cache index aw iff 0 <= aw - k0 - c < window
+      // (causal: window = 2^31 - 1), one unsigned compare.
       const unsigned wlim = P.sliding ? (unsigned)P.window : 0x7fffffffu;
-      const int dq = qw - k0 - 4 * half;
+      const int dq = aw - k0 - 4 * half;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -227,12 +234,16 @@ __global__ __launch_bounds__(64) void attn_prefill_f32(const float* __restrict__
                                                        const float* __restrict__ k,
                                                        const float* __restrict__ v, int Hq, int Hkv,
                                                        int L, int cap, int sliding, int window,
+                                                       const int32_t* __restrict__ start,
                                                        float scale, float* __restrict__ o, int ldo) {
   constexpr int DPL = (HD + 63) / 64;  // d values per lane in the PV accumulation
   __shared__ float qs[HD];
-  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+  const int il = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+  int s0 = start ? start[b] : 0;  // cache index of the chunk's first query
+  if (s0 < 0 || s0 > cap - L) s0 = 0;
+  const int i = s0 + il;          // cache index of this query
   const int kvh = h / (Hq / Hkv);
-  const float* qp = q + (((size_t)b * Hq + h) * L + i) * HD;
+  const float* qp = q + (((size_t)b * Hq + h) * L + il) * HD;
   for (int d = lane; d < HD; d += 64) qs[d] = qp[d];
   __syncthreads();
   const float* kb = k + ((size_t)b * Hkv + kvh) * cap * HD;
@@ -268,7 +279,7 @@ __global__ __launch_bounds__(64) void attn_prefill_f32(const float* __restrict__
       }
     }
   }
-  float* op = o + ((size_t)b * L + i) * ldo + (size_t)h * HD;
+  float* op = o + ((size_t)b * L + il) * ldo + (size_t)h * HD;
 #pragma unroll
   for (int t = 0; t < DPL; ++t) {
     const int d = lane + 64 * t;
@@ -280,12 +291,13 @@ __global__ __launch_bounds__(64) void attn_prefill_f32(const float* __restrict__
 
 hipError_t launch_attention_prefill(int dtype, const void* q, const void* k, const void* v, int B,
                                     int Hq, int Hkv, int L, int cap, int hd, int sliding, int window,
-                                    void* o, int ldo, hipStream_t s) {
+                                    const int32_t* start, void* o, int ldo, hipStream_t s) {
   if (dtype == 1) {
     AttnParams P;
     P.q = (const bf16_t*)q; P.k = (const bf16_t*)k; P.v = (const bf16_t*)v;
     P.B = B; P.Hq = Hq; P.Hkv = Hkv; P.L = L; P.cap = cap;
     P.sliding = sliding; P.window = window;
+    P.start = start;
     P.o = (bf16_t*)o; P.ldo = ldo;
     P.scale_log2 = kLog2e / sqrtf((float)hd);
     P.nqb = (L + QB - 1) / QB;
@@ -297,10 +309,10 @@ hipError_t launch_attention_prefill(int dtype, const void* q, const void* k, con
     const float scale = 1.0f / sqrtf((float)hd);
     if (hd == 128)
       attn_prefill_f32<128><<<grid, 64, 0, s>>>((const float*)q, (const float*)k, (const float*)v, Hq,
-                                                Hkv, L, cap, sliding, window, scale, (float*)o, ldo);
+                                                Hkv, L, cap, sliding, window, start, scale, (float*)o, ldo);
     else
       attn_prefill_f32<64><<<grid, 64, 0, s>>>((const float*)q, (const float*)k, (const float*)v, Hq,
-                                               Hkv, L, cap, sliding, window, scale, (float*)o, ldo);
+                                               Hkv, L, cap, sliding, window, start, scale, (float*)o, ldo);
   }
   return hipGetLastError();
 }

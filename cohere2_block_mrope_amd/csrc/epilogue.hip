@@ -42,12 +42,19 @@ __global__ __launch_bounds__(256) void proj_epilogue_kernel(const float* __restr
   const int cg = u - qkv_units;                                             // gate/up column
   const int vg = (E.nq64 + 2 * E.nk64) * 64 + (cg >> 6) * 128 + (cg & 63);  // virtual gate col
   float x1 = sum(gu ? vg : c1), x2 = sum(gu ? vg + 64 : c1 + half);
-  int b, l;
+  int b, l, lc;
   if (E.decode) {
     b = m; l = E.lens[b];
     if (l < 0 || l >= E.cap) return;
+    lc = l;
   } else {
     b = m / E.L; l = m - b * E.L;
+    lc = l;
+    if (E.kv_start) {  // chunked prefill: rows whose chunk does not fit the cache are skipped
+      const int s0 = E.kv_start[b];
+      if (s0 < 0 || s0 > E.cap - E.L) return;
+      lc = l + s0;
+    }
   }
   if (gu) {
     T* act = (T*)E.act;
@@ -61,7 +68,7 @@ __global__ __launch_bounds__(256) void proj_epilogue_kernel(const float* __restr
     const int kv = hh - E.Hq;
     const bool isk = kv < E.Hkv;
     const int head = isk ? kv : kv - E.Hkv;
-    dst = (T*)(isk ? E.kc : E.vc) + (((size_t)b * E.Hkv + head) * E.cap + l) * hd;
+    dst = (T*)(isk ? E.kc : E.vc) + (((size_t)b * E.Hkv + head) * E.cap + lc) * hd;
   }
   if (E.rope && hh < E.Hq + E.Hkv) {
     const float p = (float)E.pos[(size_t)rope_axis(rt, f) * E.pos_stride + m];
@@ -76,8 +83,7 @@ __global__ __launch_bounds__(256) void proj_epilogue_kernel(const float* __restr
 
 template <typename T>
 __global__ __launch_bounds__(256) void splitk_resid_kernel(const float* __restrict__ raw, int splits,
-                                                           int M, int N, const T* x, T* out,
-                                                           const int32_t* __restrict__ lens, int cap) {
+                                                           int M, int N, const T* x, T* out, RowStart rs) {
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (long long)M * N) return;
   const size_t slab = (size_t)M * N;
@@ -87,20 +93,17 @@ __global__ __launch_bounds__(256) void splitk_resid_kernel(const float* __restri
   for (; z + 4 <= splits; z += 4)  // four splits' loads in flight at a time
     s += (r[z * slab] + r[(z + 1) * slab]) + (r[(z + 2) * slab] + r[(z + 3) * slab]);
   for (; z < splits; ++z) s += r[z * slab];
-  if (lens) {  // decode: rows whose cache index is out of range are left untouched
-    const int l = lens[idx / N];
-    if (l < 0 || l >= cap) return;
-  }
+  if (!row_live(rs, (int)(idx / N) / rs.L)) return;  // rows left untouched
   out[idx] = Elt<T>::from_f(Elt<T>::to_f(x[idx]) + s);
 }
 
 template <typename T>
 __global__ __launch_bounds__(256) void deepstack_kernel(const int32_t* __restrict__ rows,
                                                         const T* __restrict__ ds, int D, int n_rows,
-                                                        T* out) {
+                                                        RowStart rs, T* out) {
   const int r = blockIdx.x;
   const int row = rows[r];
-  if (row < 0 || row >= n_rows) return;
+  if (row < 0 || row >= n_rows || !row_live(rs, row / rs.L)) return;
   for (int c = blockIdx.y * 256 + threadIdx.x; c < D; c += gridDim.y * 256) {
     T* o = out + (size_t)row * D + c;
     *o = Elt<T>::from_f(Elt<T>::to_f(*o) + Elt<T>::to_f(ds[(size_t)r * D + c]));
@@ -119,24 +122,28 @@ hipError_t launch_proj_epilogue(int dtype, const float* raw, int splits, int M, 
 }
 
 hipError_t launch_splitk_resid(int dtype, const float* raw, int splits, int M, int N, const void* x,
-                               void* out, const int32_t* lens, int cap, hipStream_t s) {
+                               void* out, const RowStart& rs_in, hipStream_t s) {
   const long long n = (long long)M * N;
   const dim3 grid((unsigned)((n + 255) / 256));
+  RowStart rs = rs_in;
+  if (rs.L < 1) rs.L = 1;
   if (dtype == 1)
-    splitk_resid_kernel<bf16_t><<<grid, 256, 0, s>>>(raw, splits, M, N, (const bf16_t*)x, (bf16_t*)out, lens, cap);
+    splitk_resid_kernel<bf16_t><<<grid, 256, 0, s>>>(raw, splits, M, N, (const bf16_t*)x, (bf16_t*)out, rs);
   else
-    splitk_resid_kernel<float><<<grid, 256, 0, s>>>(raw, splits, M, N, (const float*)x, (float*)out, lens, cap);
+    splitk_resid_kernel<float><<<grid, 256, 0, s>>>(raw, splits, M, N, (const float*)x, (float*)out, rs);
   return hipGetLastError();
 }
 
 hipError_t launch_deepstack(int dtype, const int32_t* rows, const void* ds, int n_ds, int D,
-                            int n_rows, void* out, hipStream_t s) {
+                            int n_rows, const RowStart& rs_in, void* out, hipStream_t s) {
   if (n_ds <= 0) return hipSuccess;
   const dim3 grid(n_ds, (D + 255) / 256);
+  RowStart rs = rs_in;
+  if (rs.L < 1) rs.L = 1;
   if (dtype == 1)
-    deepstack_kernel<bf16_t><<<grid, 256, 0, s>>>(rows, (const bf16_t*)ds, D, n_rows, (bf16_t*)out);
+    deepstack_kernel<bf16_t><<<grid, 256, 0, s>>>(rows, (const bf16_t*)ds, D, n_rows, rs, (bf16_t*)out);
   else
-    deepstack_kernel<float><<<grid, 256, 0, s>>>(rows, (const float*)ds, D, n_rows, (float*)out);
+    deepstack_kernel<float><<<grid, 256, 0, s>>>(rows, (const float*)ds, D, n_rows, rs, (float*)out);
   return hipGetLastError();
 }
 

@@ -247,8 +247,10 @@ hipError_t launch_gemm_bf16_proj(const void* A, int lda, int M, int K, const BMa
 }
 
 hipError_t launch_gemm_bf16_resid(const void* A, int lda, int M, int K, const BMap& bm, int N,
-                                  const void* x, void* out, int ldo, hipStream_t s) {
+                                  const void* x, void* out, int ldo, const RowStart& rs, hipStream_t s) {
   GemmParams P = base_params(A, lda, M, K, bm, N);
+  P.rs = rs;
+  if (P.rs.L < 1) P.rs.L = 1;
   P.x = (const bf16_t*)x;
   P.out = (bf16_t*)out;
   P.ldo = ldo;

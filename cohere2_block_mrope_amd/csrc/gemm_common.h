@@ -23,6 +23,7 @@ struct GemmParams {
   float* outf;       // SCALED
   long long ldof;
   float scale;
+  RowStart rs;       // RESID: rows of batch rows that are not live are not stored
   ProjEpi ep;        // PROJ
   RopeTable rt;
 };
@@ -140,9 +141,18 @@ __device__ __forceinline__ void proj_qkv_epilogue(const GemmParams& P, const f32
         const int mm = min(m, P.M - 1);
         int b, l;
         if (E.decode) { b = mm; l = E.lens[b]; } else { b = mm / E.L; l = mm - b * E.L; }
+        // Cache index of this row's K/V: chunked prefill continues after kv_start[b]
+        // tokens (rows whose chunk does not fit are not written).
+        int lc = l;
+        bool store = m < P.M;
+        if (kind != 0 && !E.decode && E.kv_start) {
+          const int s0 = E.kv_start[b];
+          store = store && s0 >= 0 && s0 <= E.cap - E.L;
+          lc = l + (store ? s0 : 0);
+        }
         bf16_t* dst;
         if (kind == 0) dst = base + (((size_t)b * E.Hq + head) * E.Lq + (E.decode ? 0 : l)) * HD;
-        else dst = base + (((size_t)b * E.Hkv + head) * E.cap + l) * HD;
+        else dst = base + (((size_t)b * E.Hkv + head) * E.cap + lc) * HD;
         float pt = 0.f, ph = 0.f, pw = 0.f;
         if (rot) {
           pt = (float)E.pos[mm];
@@ -168,7 +178,7 @@ __device__ __forceinline__ void proj_qkv_epilogue(const GemmParams& P, const f32
               x2[t] = y2;
             }
           }
-          if (m < P.M) {
+          if (store) {
             store_bf16x4(dst + 32 * jj + col4, x1);
             store_bf16x4(dst + HALF + 32 * jj + col4, x2);
           }
@@ -199,6 +209,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& P, f32x16_t (&ac
           const int m = mw0 + 32 * i + 8 * g + rowq;
           const int n = nw0 + 32 * j + col4;
           if (m >= P.M || n >= P.N) continue;
+          if constexpr (MODE == MODE_RESID) {
+            if (!row_live(P.rs, m / P.rs.L)) continue;
+          }
           if constexpr (MODE == MODE_RAW) {
             *reinterpret_cast<f32x4_t*>(P.raw + ((size_t)z * P.M + m) * P.N + n) = f32x4_t{v[0], v[1], v[2], v[3]};
           } else if constexpr (MODE == MODE_RESID) {

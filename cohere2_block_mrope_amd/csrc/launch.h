@@ -55,12 +55,30 @@ struct ProjEpi {
   void* vc;
   int cap;
   const int32_t* lens;  // decode: cache index of the new token, per row
+  const int32_t* kv_start;  // chunked prefill: row b's K/V go to cache index kv_start[b] + l
+                            // (rows with kv_start[b] outside [0, cap - L] write none); else NULL
   void* act;            // act[m * ldact + act_col0 + c] = silu(gate) * up
   int ldact;
   int act_col0;
   int nq64, nk64;
   int I;
 };
+
+// Chunked prefill rows: row b of a [B, L] chunk continues a cache holding start[b] tokens
+// and is processed only when 0 <= start[b] <= cap - L; otherwise it is skipped (no K/V
+// written, its output rows left as they were). start == NULL: every row is live.
+struct RowStart {
+  const int32_t* start;
+  int L;
+  int cap;
+};
+#ifdef __HIPCC__
+__device__ __forceinline__ bool row_live(const RowStart& r, int b) {
+  if (!r.start) return true;
+  const int s0 = r.start[b];
+  return s0 >= 0 && s0 <= r.cap - r.L;
+}
+#endif
 
 // ---------------------------------------------------------------- launchers
 hipError_t launch_positions(const int32_t* tok, int B, int L, int image_id, const int32_t* grid,
@@ -75,9 +93,10 @@ hipError_t launch_layernorm(int dtype, const void* x, const void* w, float eps, 
 // Fused projection epilogue (MRoPE, q/k/v scatter, SwiGLU); N = virtual projection width.
 hipError_t launch_gemm_bf16_proj(const void* A, int lda, int M, int K, const BMap& bm, int N,
                                  const ProjEpi& ep, const RopeTable& rt, hipStream_t s);
-// out[m, n] = x[m, n] + C (bf16; out may alias x).
+// out[m, n] = x[m, n] + C (bf16; out may alias x); rows m of batch rows b = m / rs.L that
+// are not live (RowStart) are not stored.
 hipError_t launch_gemm_bf16_resid(const void* A, int lda, int M, int K, const BMap& bm, int N,
-                                  const void* x, void* out, int ldo, hipStream_t s);
+                                  const void* x, void* out, int ldo, const RowStart& rs, hipStream_t s);
 // out[m, n] = C * scale (fp32).
 hipError_t launch_gemm_bf16_scaled_f32(const void* A, int lda, int M, int K, const BMap& bm, int N,
                                        float scale, float* out, long long ldo, hipStream_t s);
@@ -93,16 +112,18 @@ hipError_t launch_gemm_f32_raw(const void* A, int lda, int M, int K, const BMap&
 // Projection epilogue over raw fp32 partial sums [splits][M][N].
 hipError_t launch_proj_epilogue(int dtype, const float* raw, int splits, int M, int N,
                                 const ProjEpi& ep, const RopeTable& rt, hipStream_t s);
-// out[m, n] = x[m, n] + sum_z raw[z][m][n]; with lens != NULL (decode), rows m whose
-// lens[m] is outside [0, cap) are skipped.
+// out[m, n] = x[m, n] + sum_z raw[z][m][n]; rows m of batch rows b = m / rs.L that are not
+// live (RowStart; decode passes lens with L = 1) are skipped.
 hipError_t launch_splitk_resid(int dtype, const float* raw, int splits, int M, int N, const void* x,
-                               void* out, const int32_t* lens, int cap, hipStream_t s);
+                               void* out, const RowStart& rs, hipStream_t s);
 
 // Prefill attention: q [B, Hq, L, hd]; k, v [B, Hkv, cap, hd]; o written to
-// o[(b*L + l) * ldo + h*hd + d].
+// o[(b*L + l) * ldo + h*hd + d]. Query l of row b sits at cache index start[b] + l
+// (start == NULL: l) and sees the cache keys up to it; rows that are not live are
+// computed as if start[b] = 0 (memory-safe; their outputs are not used).
 hipError_t launch_attention_prefill(int dtype, const void* q, const void* k, const void* v, int B,
                                     int Hq, int Hkv, int L, int cap, int hd, int sliding, int window,
-                                    void* o, int ldo, hipStream_t s);
+                                    const int32_t* start, void* o, int ldo, hipStream_t s);
 
 // Decode attention, split over key chunks, then combine.
 int decode_chunk_keys(int dtype, int hd);
@@ -113,8 +134,8 @@ hipError_t launch_decode_attention(int dtype, const void* q, const void* k, cons
 hipError_t launch_decode_combine(int dtype, const float* part, const int32_t* lens, int B, int Hq,
                                  int cap, int hd, int n_chunks, void* o, int ldo, hipStream_t s);
 
-// out[rows[r]] += ds[r], rows outside [0, n_rows) skipped.
+// out[rows[r]] += ds[r], rows outside [0, n_rows) or in batch rows that are not live skipped.
 hipError_t launch_deepstack(int dtype, const int32_t* rows, const void* ds, int n_ds, int D,
-                            int n_rows, void* out, hipStream_t s);
+                            int n_rows, const RowStart& rs, void* out, hipStream_t s);
 
 }  // namespace compass

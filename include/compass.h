@@ -152,6 +152,25 @@ int compass_layer_prefill(const compass_layer_desc *d, const compass_layer_weigh
                           int32_t n_ds, void *out, void *workspace, size_t ws_bytes,
                           void *stream);
 
+/* Chunked prefill: the [B, L] chunk continues a dense cache ("Acceptance criteria"
+ * correction of the mlxcel Compass issue: dense cache, window as a mask; chunk
+ * boundaries as in FreeToken's "How it fits together"). Row b already holds
+ * kv->lens[b] tokens; token l of the chunk sits at cache index lens[b] + l, its K/V
+ * (after MRoPE on sliding layers) are written there, and it attends to cache keys
+ * j <= lens[b] + l (and j > lens[b] + l - window on sliding layers). pos [3, B, L]
+ * holds the chunk tokens' positions (they continue the row's positions). With L = 1 this
+ * is the decode step; with lens = 0 it is compass_layer_prefill writing the cache.
+ *   kv (required, lens required, capacity >= L). Rows with lens[b] < 0 or
+ *   lens[b] + L > capacity are skipped: no K/V written, their out rows (deepstack
+ *   included) left as they were. The library does not advance lens.
+ *   Other arguments, the workspace (compass_workspace_size(d, B, L, 0, 0)) and the
+ *   error behaviour are those of compass_layer_prefill. */
+int compass_layer_prefill_chunk(const compass_layer_desc *d, const compass_layer_weights *w,
+                                int32_t B, int32_t L, const void *x, const int32_t *pos,
+                                const compass_kv *kv, const int32_t *ds_rows, const void *ds,
+                                int32_t n_ds, void *out, void *workspace, size_t ws_bytes,
+                                void *stream);
+
 /* One decode step of one layer: one new token per row.
  *   x [B, D]; pos [3, B] int32 (lens[b] + rope_delta[b] on every axis; unread for FULL)
  *   kv (required): the new token's K/V are written at index lens[b]; keys

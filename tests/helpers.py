@@ -62,6 +62,18 @@ def run_prefill(shape: LayerShape, wdev: dict, x: torch.Tensor, pos, kv=None, ds
     return out
 
 
+def run_prefill_chunk(shape: LayerShape, wdev: dict, x: torch.Tensor, pos, kc, vc, lens, ds_rows=None, ds=None,
+                      out=None, stream=None):
+    b = B()
+    d = desc(shape)
+    Bn, L = x.shape[0], x.shape[1]
+    ws = workspace(b.compass_workspace_size(d, Bn, L, 0, 0))
+    out = torch.empty_like(x) if out is None else out
+    b.compass_layer_prefill_chunk(d, b.make_weights(wdev), x, pos, b.make_kv(kc, vc, lens), ds_rows, ds, out, ws,
+                                  stream)
+    return out
+
+
 def run_decode(shape: LayerShape, wdev: dict, x: torch.Tensor, pos, kc, vc, lens, out=None, stream=None):
     b = B()
     d = desc(shape)

@@ -161,3 +161,19 @@ def test_positions_argument_errors(b):
 
 def test_version(b):
     assert "gfx950" in b.compass_version()
+
+
+def test_chunk_argument_errors(b):
+    """compass_layer_prefill_chunk needs a cache with lens; the rest is checked as in prefill."""
+    d = compass_shape(b)
+    x, out, ws = FakePtr(0x100000), FakePtr(0x300000), FakePtr(0x400000)
+    kv = b.compass_kv()
+    kv.k, kv.v, kv.capacity = 0x500000, 0x600000, 64
+    with pytest.raises(b.CompassError) as e:  # no lens
+        b.compass_layer_prefill_chunk(d, weights(b), x, FakePtr(0x200000), kv, None, None, out, ws, stream=0)
+    assert e.value.code == b.COMPASS_E_INVALID
+    kv.lens = 0x700000
+    kv.capacity = 8
+    with pytest.raises(b.CompassError) as e:  # capacity 8 < L = 16
+        b.compass_layer_prefill_chunk(d, weights(b), x, FakePtr(0x200000), kv, None, None, out, ws, stream=0)
+    assert e.value.code == b.COMPASS_E_INVALID
