@@ -8,7 +8,8 @@ already resident in HBM. value = tokens per second per layer.
 
 Also reported (one JSON line, key "extra"): the full-attention prefill (B=2, L=8192),
 batched decode of a 4-layer 3:1 stack (B=64, cache 8192, window 4096) in us/step,
-and the 4-layer stack prefill with deepstack plus tied 256000-vocab logits.
+the 4-layer stack prefill with deepstack plus tied 256000-vocab logits, and the
+headline row prefilled as 4 chunks continuing the KV cache.
 
 "roofline" describes the dominant kernel of the headline step (the fused projection
 GEMM): algorithmic flops per launch / its mean launch time from HIP events recorded
@@ -42,7 +43,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-extra", action="store_true", help="headline workload only")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--only", default=None, help="run one workload: c1|c2|c3|c4 (for profiling)")
+    p.add_argument("--only", default=None, help="run one workload: c1|c2|c3|c4|c5 (for profiling)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run plain 512 MiB copies (reference launches for the HBM byte counters)")
     return p.parse_args()
@@ -236,6 +237,51 @@ def run_c4(args, b, H, W, torch):
     return res
 
 
+def run_c5(args, b, H, W, torch):
+    """The headline row prefilled as 4 chunks of 1024 tokens, each continuing the dense cache
+    (compass_layer_prefill_chunk; positions from the whole row), against one prefill of the
+    row writing the same cache."""
+    sh, w, x, tok, grid, off = setup_c1(H, W, torch)
+    L = x.shape[1]
+    n_chunks, Lc = 4, L // 4
+    wd = H.weights_to_dev(sh, w)
+    xd = H.to_dev(x, torch.bfloat16)
+    pos = torch.empty((3, 1, L), dtype=torch.int32, device="cuda")
+    delta = torch.empty((1,), dtype=torch.int32, device="cuda")
+    status = torch.empty((1,), dtype=torch.int32, device="cuda")
+    b.compass_mrope_positions(H.ints_to_dev(tok), W.IMAGE_TOKEN_ID, H.ints_to_dev(grid), H.ints_to_dev(off), 2,
+                              pos, delta, status)
+    assert int(status.item()) == 0
+    cap = L
+    kc = torch.empty((1, sh.n_kv_heads, cap, sh.head_dim), dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty_like(kc)
+    d = H.desc(sh)
+    wts = b.make_weights(wd)
+    ws = H.workspace(b.compass_workspace_size(d, 1, L, 0, 0))
+    out = torch.empty_like(xd)
+    xs = [xd[:, i * Lc:(i + 1) * Lc].contiguous() for i in range(n_chunks)]
+    ps = [pos[:, :, i * Lc:(i + 1) * Lc].contiguous() for i in range(n_chunks)]
+    outs = [torch.empty_like(t) for t in xs]
+    starts = [torch.full((1,), i * Lc, dtype=torch.int32, device="cuda") for i in range(n_chunks)]
+    kvs = [b.make_kv(kc, vc, s_) for s_ in starts]
+    kv0 = b.make_kv(kc, vc)
+
+    def chunked():
+        for i in range(n_chunks):
+            b.compass_layer_prefill_chunk(d, wts, xs[i], ps[i], kvs[i], None, None, outs[i], ws)
+
+    def whole():
+        b.compass_layer_prefill(d, wts, xd, pos, kv0, None, None, out, ws)
+
+    sec_c, stats = timed(chunked, args.steps, args.warmup, b, torch)
+    sec_w, _ = timed(whole, args.steps, args.warmup, b, torch)
+    return {"workload": f"chunked prefill of the sliding-layer headline row: {n_chunks} chunks of {Lc} tokens "
+                        f"continuing the dense cache",
+            "ms_per_row_chunked": 1e3 * sec_c, "ms_per_row_one_prefill": 1e3 * sec_w,
+            "tokens_per_s_chunked": L / sec_c,
+            "kernels_us": {k: round(v["mean_us"], 1) for k, v in stats.items()}}
+
+
 def cpu_baseline(sh, w, x, tok, grid, off):
     """The fp64 oracle (test infrastructure) timed on this host: the only use of oracle/ here."""
     import threadpoolctl
@@ -338,7 +384,7 @@ def main():
     else:
         line = None
     if not args.no_extra:
-        for key, fn in (("c2", run_c2), ("c3", run_c3), ("c4", run_c4)):
+        for key, fn in (("c2", run_c2), ("c3", run_c3), ("c4", run_c4), ("c5", run_c5)):
             if args.only in (None, key):
                 log(f"{key}: running")
                 res_extra[key] = fn(args, b, H, W, torch)

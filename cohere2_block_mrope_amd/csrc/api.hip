@@ -188,6 +188,10 @@ PrefillWs prefill_ws(const compass_layer_desc* d, long long B, long long L) {
   w.a2 = off; off += up(T * m.K2 * m.esz);
   w.raw = off;
   if (d->dtype == COMPASS_F32) off += up(T * (m.Nv > m.D ? m.Nv : m.D) * 4);
+  else {
+    const int so = gemm_bf16_resid_splits((int)T, (int)m.D, (int)m.K2);  // split-K output partials
+    if (so > 1) off += up((long long)so * T * m.D * 4);
+  }
   w.total = off;
   return w;
 }
@@ -369,8 +373,14 @@ static int prefill_impl(const compass_layer_desc* d, const compass_layer_weights
   LAUNCH("attn_prefill", s, launch_attention_prefill(dt, q, kc, vc, B, (int)m.Hq, (int)m.Hkv, L, cap,
                                                      (int)m.hd, sliding, d->window, start, a2, (int)m.K2, s));
   if (dt == COMPASS_BF16) {
-    LAUNCH("gemm_out", s, launch_gemm_bf16_resid(a2, (int)m.K2, (int)T, (int)m.K2, ob, (int)m.D, x, out,
-                                                 (int)m.D, rs, s));
+    const int so = gemm_bf16_resid_splits((int)T, (int)m.D, (int)m.K2);
+    if (so > 1) {  // too few output tiles to fill the CUs: split K, then reduce with the residual
+      LAUNCH("gemm_out", s, launch_gemm_bf16_raw_wide(a2, (int)m.K2, (int)T, (int)m.K2, ob, (int)m.D, so, raw, s));
+      LAUNCH("splitk_resid", s, launch_splitk_resid(dt, raw, so, (int)T, (int)m.D, x, out, rs, s));
+    } else {
+      LAUNCH("gemm_out", s, launch_gemm_bf16_resid(a2, (int)m.K2, (int)T, (int)m.K2, ob, (int)m.D, x, out,
+                                                   (int)m.D, rs, s));
+    }
   } else {
     LAUNCH("gemm_out_f32", s, launch_gemm_f32_raw(a2, (int)m.K2, (int)T, (int)m.K2, ob, (int)m.D, 1, raw, 1.f, s));
     LAUNCH("splitk_resid", s, launch_splitk_resid(dt, raw, 1, (int)T, (int)m.D, x, out, rs, s));

@@ -81,20 +81,25 @@ __global__ __launch_bounds__(256) void proj_epilogue_kernel(const float* __restr
   dst[f + half] = Elt<T>::from_f(x2);
 }
 
+// out = x + sum of the split-K partials; four consecutive columns per thread (16-byte
+// partial loads), four splits' loads in flight at a time. N % 4 == 0.
 template <typename T>
 __global__ __launch_bounds__(256) void splitk_resid_kernel(const float* __restrict__ raw, int splits,
                                                            int M, int N, const T* x, T* out, RowStart rs) {
-  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long long)M * N) return;
+  const long long q = (long long)blockIdx.x * 256 + threadIdx.x;  // quad of columns
+  if (q * 4 >= (long long)M * N) return;
+  const long long idx = q * 4;
   const size_t slab = (size_t)M * N;
-  const float* r = raw + idx;
-  float s = 0.f;
+  const f32x4_t* r = reinterpret_cast<const f32x4_t*>(raw + idx);
+  const size_t sq = slab / 4;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   int z = 0;
-  for (; z + 4 <= splits; z += 4)  // four splits' loads in flight at a time
-    s += (r[z * slab] + r[(z + 1) * slab]) + (r[(z + 2) * slab] + r[(z + 3) * slab]);
-  for (; z < splits; ++z) s += r[z * slab];
+  for (; z + 4 <= splits; z += 4)
+    acc += (r[z * sq] + r[(z + 1) * sq]) + (r[(z + 2) * sq] + r[(z + 3) * sq]);
+  for (; z < splits; ++z) acc += r[z * sq];
   if (!row_live(rs, (int)(idx / N) / rs.L)) return;  // rows left untouched
-  out[idx] = Elt<T>::from_f(Elt<T>::to_f(x[idx]) + s);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) out[idx + e] = Elt<T>::from_f(Elt<T>::to_f(x[idx + e]) + acc[e]);
 }
 
 template <typename T>
@@ -123,7 +128,7 @@ hipError_t launch_proj_epilogue(int dtype, const float* raw, int splits, int M, 
 
 hipError_t launch_splitk_resid(int dtype, const float* raw, int splits, int M, int N, const void* x,
                                void* out, const RowStart& rs_in, hipStream_t s) {
-  const long long n = (long long)M * N;
+  const long long n = (long long)M * N / 4;  // column quads (N % 4 == 0)
   const dim3 grid((unsigned)((n + 255) / 256));
   RowStart rs = rs_in;
   if (rs.L < 1) rs.L = 1;

@@ -236,14 +236,59 @@ GemmParams base_params(const void* A, int lda, int M, int K, const BMap& bm, int
 
 }  // namespace
 
+// Compute units of the current device (the tile-shape choices below count rounds of
+// one workgroup per CU).
+int device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
 hipError_t launch_gemm_bf16_proj(const void* A, int lda, int M, int K, const BMap& bm, int N,
                                  const ProjEpi& ep, const RopeTable& rt, hipStream_t s) {
   GemmParams P = base_params(A, lda, M, K, bm, N);
   P.ep = ep;
   P.rt = rt;
+  P.tiles_n = (N + 255) / 256;
+  // 128-row tiles when they need fewer rounds over the CUs, counting a 128 x 256 tile at
+  // 0.6 of a 256 x 256 one (measured per-flop efficiency of the smaller tile).
+  const long long cus = device_cus();
+  const long long r256 = ((long long)((M + 255) / 256) * P.tiles_n + cus - 1) / cus;
+  const long long r128 = ((long long)((M + 127) / 128) * P.tiles_n + cus - 1) / cus;
+  if (3 * r128 < 5 * r256) {
+    P.tiles_m = (M + 127) / 128;
+    return launch<128, 256, MODE_PROJ, 1>(P, dim3(P.tiles_m * P.tiles_n), s);
+  }
+  P.tiles_m = (M + 255) / 256;
+  return launch<256, 256, MODE_PROJ, 1>(P, dim3(P.tiles_m * P.tiles_n), s);
+}
+
+int gemm_bf16_resid_splits(int M, int N, int K) {
+  const long long cus = device_cus();
+  const long long t128 = (long long)((M + 127) / 128) * ((N + 255) / 256);
+  if (t128 >= cus) return 1;
+  const long long t256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
+  long long sp = (cus + t256 - 1) / t256;
+  if (sp > K / 1024) sp = K / 1024;  // at least 16 K steps per split
+  if (sp > 16) sp = 16;
+  return sp < 2 ? 1 : (int)sp;
+}
+
+hipError_t launch_gemm_bf16_raw_wide(const void* A, int lda, int M, int K, const BMap& bm, int N,
+                                     int splits, float* raw, hipStream_t s) {
+  GemmParams P = base_params(A, lda, M, K, bm, N);
+  P.raw = raw;
+  P.kchunk = ((K / splits + BK - 1) / BK) * BK;
   P.tiles_m = (M + 255) / 256;
   P.tiles_n = (N + 255) / 256;
-  return launch<256, 256, MODE_PROJ, 1>(P, dim3(P.tiles_m * P.tiles_n), s);
+  const dim3 grid(P.tiles_m * P.tiles_n, 1, splits);
+  return bm.kind == 2 ? launch<256, 256, MODE_RAW, 2>(P, grid, s) : launch<256, 256, MODE_RAW, 0>(P, grid, s);
 }
 
 hipError_t launch_gemm_bf16_resid(const void* A, int lda, int M, int K, const BMap& bm, int N,

@@ -100,9 +100,15 @@ hipError_t launch_gemm_bf16_resid(const void* A, int lda, int M, int K, const BM
 // out[m, n] = C * scale (fp32).
 hipError_t launch_gemm_bf16_scaled_f32(const void* A, int lda, int M, int K, const BMap& bm, int N,
                                        float scale, float* out, long long ldo, hipStream_t s);
-// raw[z][m][n] = partial C over K-slice z (fp32), splits slices of K.
+// raw[z][m][n] = partial C over K-slice z (fp32), splits slices of K (64 x 64 tiles, for
+// skinny decode GEMMs; the _wide variant uses 256 x 256 tiles).
 hipError_t launch_gemm_bf16_raw(const void* A, int lda, int M, int K, const BMap& bm, int N,
                                 int splits, float* raw, hipStream_t s);
+hipError_t launch_gemm_bf16_raw_wide(const void* A, int lda, int M, int K, const BMap& bm, int N,
+                                     int splits, float* raw, hipStream_t s);
+// K splits for the residual output GEMM: 1 when 128 x 256 tiles fill the CUs, else enough
+// 256 x 256 split-K workgroups to (the partials then go through launch_splitk_resid).
+int gemm_bf16_resid_splits(int M, int N, int K);
 
 // fp32 GEMM (VALU), same contract as launch_gemm_bf16_raw with fp32 operands; every
 // stored sum is multiplied by `scale` (1 for raw partials).
