@@ -394,3 +394,70 @@ def stack_prefill(shape, layer_weights: Sequence[Dict[str, np.ndarray]], x: np.n
         use_ds = ds is not None and i < 3 and i < len(ds)
         h = layer_prefill(sh, w, h, pos, ds_rows if use_ds else None, ds[i] if use_ds else None)
     return h
+
+
+# ----------------------------------------------------------------------------------------
+# Token-id front end and greedy generation. Page 1, "Text decoder forward": h =
+# embed_tokens(tokens), and the vision tower's final merger produces "the image embeddings
+# that replace the image-pad tokens"; page 5 ("How it fits together") writes those
+# gathered rows into the batch with one index_copy. Generation continues a row after its
+# prompt with position lens + rope_delta on every axis (page 1, "Position ids") and takes
+# the next token as the argmax of the tied-embedding logits (smallest id on ties).
+# ----------------------------------------------------------------------------------------
+def embed(tokens: np.ndarray, embed_table: np.ndarray, image_rows: Optional[np.ndarray] = None,
+          image_feats: Optional[np.ndarray] = None) -> np.ndarray:
+    """tokens [N] int -> h [N, D] = E[tokens]; then h[image_rows[r]] = image_feats[r]."""
+    h = np.asarray(embed_table, dtype=F64)[np.asarray(tokens)].copy()
+    if image_rows is not None and len(image_rows):
+        h[np.asarray(image_rows)] = np.asarray(image_feats, dtype=F64)
+    return h
+
+
+def greedy_token(h_last: np.ndarray, norm_w: np.ndarray, eps: float, embed_table: np.ndarray,
+                 logit_scale: float) -> np.ndarray:
+    """h_last [R, D] -> argmax of the logits per row (first index on ties)."""
+    return np.argmax(logits(h_last, norm_w, eps, embed_table, logit_scale), axis=1)
+
+
+def greedy_generate(shape, layer_weights: Sequence[Dict[str, np.ndarray]], embed_table: np.ndarray,
+                    norm_w: np.ndarray, logit_scale: float, tokens: np.ndarray, grid_thw: np.ndarray,
+                    img_offset: np.ndarray, image_feats: Optional[np.ndarray], ds: Optional[Sequence[np.ndarray]],
+                    image_token_id: int, spatial_merge: int, n_new: int, return_hidden: bool = False):
+    """Prompt tokens [B, L] (image pads expanded), image_feats [n_pad_rows, D] for the pad
+    tokens in row-major order, ds[i] [n_pad_rows, D] deepstack inputs of layers 0..2.
+    Returns the n_new greedily generated tokens [B, n_new] (and, with return_hidden, the
+    final hidden row each token was chosen from, [B, n_new, D])."""
+    tokens = np.asarray(tokens)
+    B, L = tokens.shape
+    pos, rope_delta = mrope_positions(tokens, image_token_id, grid_thw, img_offset, spatial_merge)
+    pad_rows = np.flatnonzero(tokens.reshape(-1) == image_token_id)
+    h = embed(tokens.reshape(-1), embed_table, pad_rows, image_feats).reshape(B, L, -1)
+    caches = []
+    for i, w in enumerate(layer_weights):
+        sh = shape.with_kind(layer_kind(i))
+        use_ds = ds is not None and i < 3 and len(pad_rows) > 0
+        h, st = layer_prefill(sh, w, h, pos, pad_rows if use_ds else None, ds[i] if use_ds else None,
+                              return_stages=True)
+        caches.append((st["k"], st["v"]))
+    out = np.empty((B, n_new), dtype=np.int64)
+    hid = np.empty((B, n_new, h.shape[-1]), dtype=F64)
+    hid[:, 0] = h[:, -1]
+    tok = greedy_token(h[:, -1], norm_w, shape.ln_eps, embed_table, logit_scale)
+    for step in range(n_new):
+        out[:, step] = tok
+        if step == n_new - 1:
+            break
+        lens = np.full(B, L + step)
+        p3 = decode_positions(lens, rope_delta)
+        x = embed(tok, embed_table)
+        for i, w in enumerate(layer_weights):
+            sh = shape.with_kind(layer_kind(i))
+            kc, vc = caches[i]
+            kpad = np.concatenate([kc, np.zeros_like(kc[:, :, :1])], axis=2)
+            vpad = np.concatenate([vc, np.zeros_like(vc[:, :, :1])], axis=2)
+            x, knew, vnew = layer_decode(sh, w, x, p3, kpad, vpad, lens)
+            kpad[:, :, -1], vpad[:, :, -1] = knew, vnew
+            caches[i] = (kpad, vpad)
+        hid[:, step + 1] = x
+        tok = greedy_token(x, norm_w, shape.ln_eps, embed_table, logit_scale)
+    return (out, hid) if return_hidden else out

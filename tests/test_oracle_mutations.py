@@ -96,6 +96,11 @@ def _chunk_ignores_cache(shape, w, x, pos, k_cache, v_cache, start):
     return _orig_chunk(shape, w, x, pos, k_cache, v_cache, np.zeros_like(start))
 
 
+def _decode_positions_without_delta(lens, rope_delta):
+    p = np.asarray(lens, dtype=np.int64)
+    return np.stack([p, p, p])
+
+
 def _chunk_start_off_by_one(shape, w, x, pos, k_cache, v_cache, start):
     return _orig_chunk(shape, w, x, pos, k_cache, v_cache, np.maximum(np.asarray(start) - 1, 0))
 
@@ -115,6 +120,7 @@ MUTANTS = {
     "silu term dropped": ("silu", _silu_sigmoid_only),
     "chunk ignores the cache": ("layer_prefill_chunk", _chunk_ignores_cache),
     "chunk start off by one": ("layer_prefill_chunk", _chunk_start_off_by_one),
+    "decode positions ignore rope_delta": ("decode_positions", _decode_positions_without_delta),
 }
 
 PINS = [
@@ -130,6 +136,7 @@ PINS = [
     P.test_logits_vs_library_and_scale,
     lambda: P.test_chunked_prefill_equals_one_prefill("sliding", 3),
     lambda: P.test_chunked_prefill_equals_one_prefill("full", 0),
+    P.test_greedy_generation_equals_full_recompute,
 ]
 
 

@@ -405,6 +405,43 @@ def test_one_token_chunk_equals_decode():
         np.testing.assert_allclose(v_c[:, :, 0], v_d, atol=1e-12)
 
 
+def test_embed_front_end():
+    E = np.arange(5 * 3, dtype=float).reshape(5, 3)
+    h = O.embed(np.array([4, 0, 2, 2]), E, np.array([1, 3]), np.array([[9.0, 9, 9], [8, 8, 8]]))
+    np.testing.assert_array_equal(h, [[12, 13, 14], [9, 9, 9], [6, 7, 8], [8, 8, 8]])
+
+
+def test_greedy_generation_equals_full_recompute():
+    """Every generated token equals the argmax of the last row of a cache-free stack prefill
+    over prompt + the tokens generated so far, with positions recomputed by the position
+    rule over the extended rows (pins the decode positions lens + rope_delta, the cache
+    continuation and the deepstack / image-row handling of the prompt)."""
+    sh = tiny_shape("sliding", 4)
+    ws = [rand_weights(sh, seed=70 + i, std=0.2) for i in range(4)]
+    r = np.random.default_rng(75)
+    V, IMG = 64, 63
+    E = 0.6 * r.standard_normal((V, sh.hidden))
+    nw = 1 + 0.1 * r.standard_normal(sh.hidden)
+    tokens = np.array([[5, 7, IMG, IMG, IMG, IMG, 9, 2],   # image 2 x 2 merged: rope_delta = -2
+                       [3, 8, 8, 1, 0, 6, 5, 2]])
+    grid, off = np.array([[1, 4, 4]]), np.array([0, 1, 1])
+    assert O.mrope_positions(tokens, IMG, grid, off, 2)[1].tolist() == [-2, 0]
+    feats = r.standard_normal((4, sh.hidden))
+    ds = [0.5 * r.standard_normal((4, sh.hidden)) for _ in range(3)]
+    n_new = 5
+    gen, hid = O.greedy_generate(sh, ws, E, nw, 0.25, tokens, grid, off, feats, ds, IMG, 2, n_new,
+                                 return_hidden=True)
+    assert gen.shape == (2, n_new) and not (gen == IMG).any()
+    for k in range(n_new):
+        seq = np.concatenate([tokens, gen[:, :k]], axis=1)
+        pos, _ = O.mrope_positions(seq, IMG, grid, off, 2)
+        pad = np.flatnonzero(seq.reshape(-1) == IMG)
+        h = O.embed(seq.reshape(-1), E, pad, feats).reshape(2, seq.shape[1], -1)
+        h = O.stack_prefill(sh, ws, h, pos, pad, ds)
+        np.testing.assert_allclose(hid[:, k], h[:, -1], atol=1e-10)
+        np.testing.assert_array_equal(O.greedy_token(h[:, -1], nw, sh.ln_eps, E, 0.25), gen[:, k])
+
+
 # ------------------------------------------------------------------------------ logits
 def test_logits_vs_library_and_scale():
     r = np.random.default_rng(60)
