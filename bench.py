@@ -178,6 +178,27 @@ def run_c3(args, b, H, W, torch):
             b.compass_layer_decode(d, wts, h, pos, b.make_kv(kc, vc, lens), h, ws)
 
     sec, stats = timed(step, max(5, args.steps), 3, b, torch)
+
+    # A whole greedy decode step: embed the 64 tokens, decode positions, the 4 layers, then
+    # the tied 256000-vocab head reduced to the next token ids, which feed the next step.
+    # lens is not advanced (advance 0), so every timed step does the same work.
+    V = WORKLOADS[4]["vocab"]
+    E = RT.normal(W.stream_seed(3, 0, W.TensorId.EMBED), V * sh.hidden, std=0.02).to(torch.bfloat16).view(V, sh.hidden)
+    nw = RT.normal(W.stream_seed(3, 0, W.TensorId.FINAL_LN), sh.hidden, std=0.02, mean=1.0).to(torch.bfloat16)
+    tok = torch.arange(Bn, dtype=torch.int32, device="cuda") * 17
+    delta = torch.zeros((Bn,), dtype=torch.int32, device="cuda")
+    gws = H.workspace(b.compass_logits_argmax_workspace_size(Bn, sh.hidden, V, 1))
+    est = torch.zeros((1,), dtype=torch.int32, device="cuda")
+
+    def greedy_step():
+        b.compass_embed(tok, E, None, None, h, est, 1)
+        b.compass_decode_positions(lens, delta, 0, pos)
+        for d, wts, _, kc, vc, ws in layers:
+            b.compass_layer_decode(d, wts, h, pos, b.make_kv(kc, vc, lens), h, ws)
+        b.compass_logits_argmax(h, nw, sh.ln_eps, E, WORKLOADS[4]["logit_scale"], tok, None, gws, 1)
+
+    sec_g, stats_g = timed(greedy_step, max(5, args.steps), 3, b, torch)
+    assert int(est.item()) == 0
     kv_bytes_slide = Bn * Hkv * sh.window * hd * 2 * 2
     kv_bytes_full = Bn * Hkv * (n + 1) * hd * 2 * 2
     w_bytes = 2 * (sh.hidden * ((sh.n_q_heads + 2 * Hkv) * hd + 2 * sh.intermediate)
@@ -189,6 +210,14 @@ def run_c3(args, b, H, W, torch):
            "kernels_us": {k: round(v["mean_us"], 1) for k, v in stats.items()}}
     if att:
         res["decode_attn_hbm_frac"] = att_bytes_mean / (att["mean_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS
+    lg = stats_g.get("gemm_logits", {})
+    res["greedy_step"] = {"us_per_step": 1e6 * sec_g,
+                          "what": "embed + decode positions + the 4 layers + tied 256000-vocab logits argmax",
+                          "kernels_us": {k: round(v["mean_us"], 1) for k, v in stats_g.items()
+                                         if k in ("embed", "decode_positions", "logits_layernorm", "gemm_logits",
+                                                  "argmax")}}
+    if lg:
+        res["greedy_step"]["logits_hbm_frac"] = V * sh.hidden * 2 / (lg["mean_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS
     return res
 
 

@@ -72,6 +72,11 @@ _sig = {
     "compass_logits_workspace_size": (ctypes.c_size_t, [_I, _I, _I]),
     "compass_logits": (ctypes.c_int, [_I, _I, _I, _I, _P, _P, ctypes.c_float, _P, ctypes.c_float, _P, _P,
                                       ctypes.c_size_t, _P]),
+    "compass_embed": (ctypes.c_int, [_I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P]),
+    "compass_decode_positions": (ctypes.c_int, [_I, _P, _P, _I, _P, _P]),
+    "compass_logits_argmax_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "compass_logits_argmax": (ctypes.c_int, [_I, _I, _I, _I, _P, ctypes.c_int64, _P, ctypes.c_float, _P,
+                                             ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
     "compass_last_error": (ctypes.c_char_p, []),
     "compass_version": (ctypes.c_char_p, []),
     "compass_profile_enable": (ctypes.c_int, [ctypes.c_int]),
@@ -187,6 +192,37 @@ def compass_logits(h, norm_w, ln_eps: float, embed, logit_scale: float, logits, 
     _check(_lib.compass_logits(R, D, V, dtype, _ptr(h), _ptr(norm_w), ln_eps, _ptr(embed), logit_scale,
                                _ptr(logits), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                _stream(stream)))
+
+
+def compass_embed(tokens, embed, img_rows, img_feats, h, status, dtype: int, stream=None) -> None:
+    """tokens [R] int32, embed [V, D], img_rows [n_img] int32 or None, img_feats [n_img, D], h out [R, D]."""
+    R = int(tokens.numel())
+    V, D = embed.shape
+    n_img = 0 if img_rows is None else int(img_rows.numel())
+    _check(_lib.compass_embed(R, D, V, dtype, _ptr(tokens), _ptr(embed), _ptr(img_rows), _ptr(img_feats), n_img,
+                              _ptr(h), _ptr(status), _stream(stream)))
+
+
+def compass_decode_positions(lens, rope_delta, advance: int, pos, stream=None) -> None:
+    """lens [B] int32 (updated in place), rope_delta [B] int32 or None, pos out [3, B] int32."""
+    B = int(lens.numel())
+    _check(_lib.compass_decode_positions(B, _ptr(lens), _ptr(rope_delta), advance, _ptr(pos), _stream(stream)))
+
+
+def compass_logits_argmax_workspace_size(R: int, D: int, V: int, dtype: int) -> int:
+    return int(_lib.compass_logits_argmax_workspace_size(R, D, V, dtype))
+
+
+def compass_logits_argmax(h, norm_w, ln_eps: float, embed, logit_scale: float, token, max_logit, workspace,
+                          dtype: int, stream=None) -> None:
+    """h [R, D] with unit column stride (rows may be strided, e.g. x[:, -1] of [B, L, D])."""
+    R, D = h.shape
+    if R > 1 and h.stride(1) != 1:
+        raise ValueError("h must have unit column stride")
+    V = embed.shape[0]
+    _check(_lib.compass_logits_argmax(R, D, V, dtype, _ptr(h), h.stride(0) if R > 1 else D, _ptr(norm_w), ln_eps,
+                                      _ptr(embed), logit_scale, _ptr(token), _ptr(max_logit), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def compass_profile_enable(on: bool) -> None:

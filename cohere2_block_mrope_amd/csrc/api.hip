@@ -517,6 +517,90 @@ int compass_logits(int32_t R, int32_t D, int32_t V, int32_t dtype, const void* h
   return ok();
 }
 
+int compass_embed(int32_t R, int32_t D, int32_t V, int32_t dtype, const int32_t* tokens, const void* embed,
+                  const int32_t* img_rows, const void* img_feats, int32_t n_img, void* h, int32_t* status,
+                  void* stream) {
+  if (R < 1 || D < 1 || V < 1) return fail(COMPASS_E_INVALID, "R=%d D=%d V=%d must be >= 1", R, D, V);
+  if (dtype != COMPASS_F32 && dtype != COMPASS_BF16)
+    return fail(COMPASS_E_UNSUPPORTED, "dtype %d not supported", dtype);
+  if (D % 8) return fail(COMPASS_E_UNSUPPORTED, "D=%d must be a multiple of 8", D);
+  if (n_img < 0) return fail(COMPASS_E_INVALID, "n_img=%d < 0", n_img);
+  if (!tokens || !embed || !h) return fail(COMPASS_E_INVALID, "NULL pointer argument");
+  if (n_img > 0 && (!img_rows || !img_feats))
+    return fail(COMPASS_E_INVALID, "image pointers NULL with n_img > 0");
+  if (!aligned16(embed) || !aligned16(h) || (n_img > 0 && !aligned16(img_feats)))
+    return fail(COMPASS_E_ALIGN, "tensor not 16-byte aligned");
+  const size_t esz = dtype == COMPASS_BF16 ? 2 : 4;
+  const size_t hbytes = (size_t)R * D * esz;
+  if (overlap(h, hbytes, embed, (size_t)V * D * esz) ||
+      (n_img > 0 && overlap(h, hbytes, img_feats, (size_t)n_img * D * esz)))
+    return fail(COMPASS_E_INVALID, "h overlaps an input");
+  const hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  LAUNCH("embed", s, launch_embed(dtype, tokens, R, D, V, embed, img_rows, img_feats, n_img, h, status, s));
+  return ok();
+}
+
+int compass_decode_positions(int32_t B, int32_t* lens, const int32_t* rope_delta, int32_t advance, int32_t* pos,
+                             void* stream) {
+  if (B < 1) return fail(COMPASS_E_INVALID, "B=%d must be >= 1", B);
+  if (advance < 0) return fail(COMPASS_E_INVALID, "advance=%d < 0", advance);
+  if (!lens || !pos) return fail(COMPASS_E_INVALID, "lens or pos is NULL");
+  if (overlap(lens, (size_t)B * 4, pos, (size_t)B * 12)) return fail(COMPASS_E_INVALID, "pos overlaps lens");
+  const hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  LAUNCH("decode_positions", s, launch_decode_positions(lens, rope_delta, B, pos, advance, s));
+  return ok();
+}
+
+size_t compass_logits_argmax_workspace_size(int32_t R, int32_t D, int32_t V, int32_t dtype) {
+  if (R < 1 || D < 1 || V < 1 || (dtype != COMPASS_F32 && dtype != COMPASS_BF16)) return 0;
+  return up((size_t)R * D * (dtype == COMPASS_BF16 ? 2 : 4)) + up((size_t)R * V * 4) +
+         2 * up((size_t)R * argmax_chunks(V) * 4);
+}
+
+int compass_logits_argmax(int32_t R, int32_t D, int32_t V, int32_t dtype, const void* h, int64_t ldh,
+                          const void* norm_w, float ln_eps, const void* embed, float logit_scale, int32_t* token,
+                          float* max_logit, void* workspace, size_t ws_bytes, void* stream) {
+  if (R < 1 || D < 1 || V < 1) return fail(COMPASS_E_INVALID, "R=%d D=%d V=%d must be >= 1", R, D, V);
+  if (dtype != COMPASS_F32 && dtype != COMPASS_BF16)
+    return fail(COMPASS_E_UNSUPPORTED, "dtype %d not supported", dtype);
+  if (D % 64 || D > 8192) return fail(COMPASS_E_UNSUPPORTED, "D=%d must be a multiple of 64, <= 8192", D);
+  if (ldh == 0) ldh = D;
+  if (ldh < D) return fail(COMPASS_E_INVALID, "ldh=%lld < D=%d", (long long)ldh, D);
+  if ((ldh * (dtype == COMPASS_BF16 ? 2 : 4)) % 16)
+    return fail(COMPASS_E_ALIGN, "rows of h not 16-byte aligned (ldh=%lld)", (long long)ldh);
+  if (R > 65535 || (long long)R * V > (1LL << 40) || (long long)V * D > (1LL << 31) - 1)
+    return fail(COMPASS_E_UNSUPPORTED, "R > 65535, or R*V or V*D too large");
+  if (!h || !norm_w || !embed || !token) return fail(COMPASS_E_INVALID, "NULL pointer argument");
+  if (!aligned16(h) || !aligned16(norm_w) || !aligned16(embed))
+    return fail(COMPASS_E_ALIGN, "tensor not 16-byte aligned");
+  if (!(ln_eps >= 0.f) || !isfinite(ln_eps)) return fail(COMPASS_E_INVALID, "ln_eps must be finite and >= 0");
+  const size_t need = compass_logits_argmax_workspace_size(R, D, V, dtype);
+  if (!workspace || ws_bytes < need)
+    return fail(COMPASS_E_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return fail(COMPASS_E_ALIGN, "workspace not 256-byte aligned");
+  const hipStream_t s = (hipStream_t)stream;
+  void* a = workspace;
+  float* lg = (float*)((char*)workspace + up((size_t)R * D * (dtype == COMPASS_BF16 ? 2 : 4)));
+  float* pv = (float*)((char*)lg + up((size_t)R * V * 4));
+  int* pi = (int*)((char*)pv + up((size_t)R * argmax_chunks(V) * 4));
+  BMap eb{};
+  eb.kind = 0;
+  eb.p[0] = embed;
+  eb.ld0 = D;
+  (void)hipGetLastError();
+  // Same LayerNorm and logits GEMM as compass_logits (the logits are bitwise those it
+  // returns for the same rows), then one argmax pass over them.
+  LAUNCH("logits_layernorm", s, launch_layernorm(dtype, h, norm_w, ln_eps, a, R, D, s, (long long)ldh));
+  if (dtype == COMPASS_BF16)
+    LAUNCH("gemm_logits", s, launch_gemm_bf16_scaled_f32(a, D, R, D, eb, V, logit_scale, lg, (long long)V, s));
+  else
+    LAUNCH("gemm_logits", s, launch_gemm_f32_raw(a, D, R, D, eb, V, 1, lg, logit_scale, s));
+  LAUNCH("argmax", s, launch_argmax(lg, R, V, (long long)V, 1.f, pv, pi, token, max_logit, s));
+  return ok();
+}
+
 int compass_profile_enable(int on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_on = on != 0;

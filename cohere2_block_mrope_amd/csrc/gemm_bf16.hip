@@ -117,8 +117,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams P) {
       const int i = p - A_PER_T;
       const u32x4_t* src = reinterpret_cast<const u32x4_t*>(
           (BKIND == 2 && k0 >= P.bm.ksplit) ? bbase1 + boff1[i] + k0 : bbase0 + boff[i] + k0);
-      // Split-K skinny GEMMs (decode) read each weight once: stream it past the caches.
-      if constexpr (MODE == MODE_RAW) rb[i] = __builtin_nontemporal_load(src);
+      // Skinny GEMMs (split-K decode projections, logits of at most 128 rows: one row
+      // tile) read each weight row once: stream it past the caches.
+      if constexpr (MODE == MODE_RAW || (MODE == MODE_SCALED && BM <= 128)) rb[i] = __builtin_nontemporal_load(src);
       else rb[i] = *src;
     }
   };
@@ -318,6 +319,18 @@ hipError_t launch_gemm_bf16_scaled_f32(const void* A, int lda, int M, int K, con
   P.outf = out;
   P.ldof = ldo;
   P.scale = scale;
+  // Few rows (a decode batch): the table streams through once either way, so smaller
+  // row tiles cut the padded MFMA work without adding table reads.
+  if (M <= 64) {
+    P.tiles_m = 1;
+    P.tiles_n = (N + 255) / 256;
+    return launch<64, 256, MODE_SCALED, 0>(P, dim3(P.tiles_n), s);
+  }
+  if (M <= 128) {
+    P.tiles_m = 1;
+    P.tiles_n = (N + 255) / 256;
+    return launch<128, 256, MODE_SCALED, 0>(P, dim3(P.tiles_n), s);
+  }
   P.tiles_m = (M + 255) / 256;
   P.tiles_n = (N + 255) / 256;
   return launch<256, 256, MODE_SCALED, 0>(P, dim3(P.tiles_m * P.tiles_n), s);

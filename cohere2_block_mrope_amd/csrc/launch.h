@@ -85,9 +85,10 @@ hipError_t launch_positions(const int32_t* tok, int B, int L, int image_id, cons
                             const int32_t* img_off, int merge, int32_t* pos, int32_t* delta,
                             int32_t* status, hipStream_t s);
 
-// a = LN(x) over rows [rows, D]; dtype 1 = bf16, 0 = f32 (a has the dtype of x).
+// a = LN(x) over rows [rows, D] (x rows ldx elements apart, default D; a contiguous);
+// dtype 1 = bf16, 0 = f32 (a has the dtype of x).
 hipError_t launch_layernorm(int dtype, const void* x, const void* w, float eps, void* a, int rows,
-                            int D, hipStream_t s);
+                            int D, hipStream_t s, long long ldx = 0);
 
 // bf16 MFMA GEMMs, C[m, n] = sum_k A[m, k] * B[n, k], A [M, lda] bf16.
 // Fused projection epilogue (MRoPE, q/k/v scatter, SwiGLU); N = virtual projection width.
@@ -143,5 +144,20 @@ hipError_t launch_decode_combine(int dtype, const float* part, const int32_t* le
 // out[rows[r]] += ds[r], rows outside [0, n_rows) or in batch rows that are not live skipped.
 hipError_t launch_deepstack(int dtype, const int32_t* rows, const void* ds, int n_ds, int D,
                             int n_rows, const RowStart& rs, void* out, hipStream_t s);
+
+// Token-id front end: h[r] = E[tokens[r]] (zero row for ids outside [0, V)), then
+// h[img_rows[i]] = feats[i] (rows outside [0, R) skipped); status[0] (may be NULL) gets
+// bit 0 if an id was outside [0, V), bit 1 if an image row was outside [0, R).
+hipError_t launch_embed(int dtype, const int32_t* tokens, int R, int D, int V, const void* E,
+                        const int32_t* img_rows, const void* feats, int n_img, void* h, int32_t* status,
+                        hipStream_t s);
+// lens[b] += advance; pos[a][b] = lens[b] + rope_delta[b] on the three axes.
+hipError_t launch_decode_positions(int32_t* lens, const int32_t* rope_delta, int B, int32_t* pos, int advance,
+                                   hipStream_t s);
+// token[r] = argmax_v scale * raw[r * ldr + v] (smallest v on ties); max_logit optional.
+// pv / pi: per-row chunk winners, R * argmax_chunks(V) floats / ints of scratch.
+int argmax_chunks(int V);
+hipError_t launch_argmax(const float* raw, int R, int V, long long ldr, float scale, float* pv, int* pi,
+                         int32_t* token, float* max_logit, hipStream_t s);
 
 }  // namespace compass

@@ -18,11 +18,11 @@ constexpr int kRowsPerBlock = 4;
 template <typename T, int VPL>
 __global__ __launch_bounds__(256) void layernorm_kernel(const T* __restrict__ x,
                                                         const T* __restrict__ w, float eps,
-                                                        T* __restrict__ a, int rows, int D) {
+                                                        T* __restrict__ a, int rows, int D, long long ldx) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const T* xr = x + (size_t)row * D;
+  const T* xr = x + (size_t)row * ldx;
   T* ar = a + (size_t)row * D;
   constexpr int V = (sizeof(T) == 2) ? 8 : 4;  // elements per 16-byte vector
   constexpr int NV = (VPL + V - 1) / V;        // vectors per lane
@@ -93,26 +93,27 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const T* __restrict__ x,
 }
 
 template <typename T>
-hipError_t launch_t(const void* x, const void* w, float eps, void* a, int rows, int D,
+hipError_t launch_t(const void* x, long long ldx, const void* w, float eps, void* a, int rows, int D,
                     hipStream_t s) {
   const dim3 grid((rows + kRowsPerBlock - 1) / kRowsPerBlock);
   const T* xp = (const T*)x;
   const T* wp = (const T*)w;
   T* ap = (T*)a;
   // D is a multiple of 64 and at most 16384 (checked by the caller).
-  if (D <= 64 * 8) layernorm_kernel<T, 8><<<grid, 256, 0, s>>>(xp, wp, eps, ap, rows, D);
-  else if (D <= 64 * 32) layernorm_kernel<T, 32><<<grid, 256, 0, s>>>(xp, wp, eps, ap, rows, D);
-  else if (D <= 64 * 64) layernorm_kernel<T, 64><<<grid, 256, 0, s>>>(xp, wp, eps, ap, rows, D);
-  else layernorm_kernel<T, 256><<<grid, 256, 0, s>>>(xp, wp, eps, ap, rows, D);
+  if (D <= 64 * 8) layernorm_kernel<T, 8><<<grid, 256, 0, s>>>(xp, wp, eps, ap, rows, D, ldx);
+  else if (D <= 64 * 32) layernorm_kernel<T, 32><<<grid, 256, 0, s>>>(xp, wp, eps, ap, rows, D, ldx);
+  else if (D <= 64 * 64) layernorm_kernel<T, 64><<<grid, 256, 0, s>>>(xp, wp, eps, ap, rows, D, ldx);
+  else layernorm_kernel<T, 256><<<grid, 256, 0, s>>>(xp, wp, eps, ap, rows, D, ldx);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_layernorm(int dtype, const void* x, const void* w, float eps, void* a, int rows,
-                            int D, hipStream_t s) {
-  return dtype == 1 ? launch_t<bf16_t>(x, w, eps, a, rows, D, s)
-                    : launch_t<float>(x, w, eps, a, rows, D, s);
+                            int D, hipStream_t s, long long ldx) {
+  if (ldx <= 0) ldx = D;
+  return dtype == 1 ? launch_t<bf16_t>(x, ldx, w, eps, a, rows, D, s)
+                    : launch_t<float>(x, ldx, w, eps, a, rows, D, s);
 }
 
 }  // namespace compass

@@ -194,6 +194,45 @@ int compass_logits(int32_t R, int32_t D, int32_t V, int32_t dtype, const void *h
                    const void *norm_w, float ln_eps, const void *embed, float logit_scale,
                    float *logits, void *workspace, size_t ws_bytes, void *stream);
 
+/* Token-id front end ("Text decoder forward" of the mlxcel Compass issue: the token
+ * embedding, whose image-pad rows are then replaced by the vision merger's output rows;
+ * FreeToken's "How it fits together" writes them with one indexed copy):
+ *   h[r] = embed[tokens[r]] for r < R, then h[img_rows[i]] = img_feats[i] for i < n_img.
+ *   tokens [R] int32 (device)   embed [V, D] (dtype)   img_rows [n_img] int32 (device;
+ *   distinct rows; NULL when n_img = 0)   img_feats [n_img, D] (dtype)   h out [R, D].
+ *   status (device int32, may be NULL): bit 0 set if a token id lies outside [0, V)
+ *   (that row of h is zero), bit 1 if an image row lies outside [0, R) (skipped);
+ *   read it after the stream has synchronized. D must be a multiple of 8; h must not
+ *   overlap embed or img_feats. Stream-ordered, allocates nothing. */
+int compass_embed(int32_t R, int32_t D, int32_t V, int32_t dtype, const int32_t *tokens,
+                  const void *embed, const int32_t *img_rows, const void *img_feats,
+                  int32_t n_img, void *h, int32_t *status, void *stream);
+
+/* Decode positions ("Position ids": a generated token sits at its cache index plus the
+ * row's rope_delta on all three axes). On the device: lens[b] += advance, then
+ * pos[a * B + b] = lens[b] + rope_delta[b] for a = 0, 1, 2.
+ *   lens [B] int32 (device, updated in place)   rope_delta [B] int32 (device, from
+ *   compass_mrope_positions; NULL = zeros)   advance >= 0 (0 for the first decode step
+ *   after a prefill whose lens the caller has set, 1 for each later step)
+ *   pos out [3, B] int32, the pos argument of compass_layer_decode. */
+int compass_decode_positions(int32_t B, int32_t *lens, const int32_t *rope_delta,
+                             int32_t advance, int32_t *pos, void *stream);
+
+/* Greedy head: token[r] = the vocabulary id of the largest logit of compass_logits for
+ * row r (the same LayerNorm and logits GEMM, so the same fp32 values; the smallest id
+ * on ties), max_logit[r] (may be NULL) = that logit.
+ *   h: R rows of D elements, row r at h + r * ldh (ldh = 0 means D; e.g. ldh = L * D
+ *   with h pointing at row L - 1 picks the last token of every [L, D] batch row);
+ *   ldh * element size must be a multiple of 16.   token out [R] int32 (device).
+ *   R <= 65535. A NaN logit is never picked (a row of NaN / -inf logits gives id 0).
+ *   workspace: compass_logits_argmax_workspace_size(R, D, V, dtype) bytes, 256-byte
+ *   aligned. Other arguments and errors as compass_logits. */
+size_t compass_logits_argmax_workspace_size(int32_t R, int32_t D, int32_t V, int32_t dtype);
+int compass_logits_argmax(int32_t R, int32_t D, int32_t V, int32_t dtype, const void *h,
+                          int64_t ldh, const void *norm_w, float ln_eps, const void *embed,
+                          float logit_scale, int32_t *token, float *max_logit, void *workspace,
+                          size_t ws_bytes, void *stream);
+
 /* Message of the last failing call on this thread ("" if none). */
 const char *compass_last_error(void);
 

@@ -177,3 +177,44 @@ def test_chunk_argument_errors(b):
     with pytest.raises(b.CompassError) as e:  # capacity 8 < L = 16
         b.compass_layer_prefill_chunk(d, weights(b), x, FakePtr(0x200000), kv, None, None, out, ws, stream=0)
     assert e.value.code == b.COMPASS_E_INVALID
+
+
+def test_front_end_argument_errors(b):
+    """compass_embed / compass_decode_positions / compass_logits_argmax reject bad arguments
+    on the host with the documented codes."""
+    L = b._lib
+    # embed: D not a multiple of 8, NULL table, image pointers missing, misaligned h, h over embed
+    assert L.compass_embed(4, 12, 100, 1, 0x1000, 0x2000, None, None, 0, 0x3000, None, None) == b.COMPASS_E_UNSUPPORTED
+    assert L.compass_embed(4, 64, 100, 1, 0x1000, None, None, None, 0, 0x3000, None, None) == b.COMPASS_E_INVALID
+    assert L.compass_embed(4, 64, 100, 1, 0x1000, 0x2000, None, None, 3, 0x3000, None, None) == b.COMPASS_E_INVALID
+    assert L.compass_embed(4, 64, 100, 1, 0x1000, 0x2000, None, None, 0, 0x3008, None, None) == b.COMPASS_E_ALIGN
+    assert L.compass_embed(4, 64, 100, 1, 0x1000, 0x100000, None, None, 0, 0x100000 + 1024, None,
+                           None) == b.COMPASS_E_INVALID
+    assert L.compass_embed(0, 64, 100, 1, 0x1000, 0x2000, None, None, 0, 0x3000, None, None) == b.COMPASS_E_INVALID
+    assert L.compass_embed(4, 64, 100, 5, 0x1000, 0x2000, None, None, 0, 0x3000, None, None) == b.COMPASS_E_UNSUPPORTED
+    # decode positions: B < 1, advance < 0, NULL lens, pos over lens
+    assert L.compass_decode_positions(0, 0x1000, None, 0, 0x2000, None) == b.COMPASS_E_INVALID
+    assert L.compass_decode_positions(4, 0x1000, None, -1, 0x2000, None) == b.COMPASS_E_INVALID
+    assert L.compass_decode_positions(4, None, None, 0, 0x2000, None) == b.COMPASS_E_INVALID
+    assert L.compass_decode_positions(4, 0x1000, None, 0, 0x1008, None) == b.COMPASS_E_INVALID
+    # logits argmax
+    # LayerNorm rows, fp32 logits, then the per-chunk (value, id) winners of 4096-column chunks
+    assert b.compass_logits_argmax_workspace_size(64, 2048, 256000, 1) == \
+        64 * 2048 * 2 + 64 * 256000 * 4 + 2 * 256 * 63
+    assert b.compass_logits_argmax_workspace_size(64, 2048, 256000, 9) == 0
+    ws = 0x10000000
+    need = b.compass_logits_argmax_workspace_size(8, 2048, 1000, 1)
+
+    def am(R=8, D=2048, V=1000, dt=1, h=0x100000, ldh=0, nw=0x200000, emb=0x400000, tok=0x300000,
+           w=ws, n=need):
+        return L.compass_logits_argmax(R, D, V, dt, h, ldh, nw, 1e-5, emb, 0.0625, tok, None, w, n, None)
+
+    assert am(D=2000) == b.COMPASS_E_UNSUPPORTED
+    assert am(ldh=1000) == b.COMPASS_E_INVALID          # ldh < D
+    assert am(ldh=2052) == b.COMPASS_E_ALIGN            # rows not 16-byte aligned
+    assert am(tok=None) == b.COMPASS_E_INVALID
+    assert am(n=need - 1) == b.COMPASS_E_WORKSPACE
+    assert am(w=ws + 16) == b.COMPASS_E_ALIGN
+    assert am(dt=3) == b.COMPASS_E_UNSUPPORTED
+    assert "ldh" in (am(ldh=1000) and b.compass_last_error())
+    assert am(R=70000, n=1 << 40) == b.COMPASS_E_UNSUPPORTED  # R above the grid limit
