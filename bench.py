@@ -210,12 +210,12 @@ def run_c3(args, b, H, W, torch):
            "kernels_us": {k: round(v["mean_us"], 1) for k, v in stats.items()}}
     if att:
         res["decode_attn_hbm_frac"] = att_bytes_mean / (att["mean_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS
-    lg = stats_g.get("gemm_logits", {})
+    lg = stats_g.get("gemm_logits_argmax", {})
     res["greedy_step"] = {"us_per_step": 1e6 * sec_g,
                           "what": "embed + decode positions + the 4 layers + tied 256000-vocab logits argmax",
                           "kernels_us": {k: round(v["mean_us"], 1) for k, v in stats_g.items()
-                                         if k in ("embed", "decode_positions", "logits_layernorm", "gemm_logits",
-                                                  "argmax")}}
+                                         if k in ("embed", "decode_positions", "logits_layernorm",
+                                                  "gemm_logits_argmax", "argmax")}}
     if lg:
         res["greedy_step"]["logits_hbm_frac"] = V * sh.hidden * 2 / (lg["mean_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS
     return res

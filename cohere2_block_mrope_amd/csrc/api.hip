@@ -553,10 +553,14 @@ int compass_decode_positions(int32_t B, int32_t* lens, const int32_t* rope_delta
   return ok();
 }
 
+static int argmax_parts_bf16(int V) { return 2 * ((V + 255) / 256); }
+
 size_t compass_logits_argmax_workspace_size(int32_t R, int32_t D, int32_t V, int32_t dtype) {
   if (R < 1 || D < 1 || V < 1 || (dtype != COMPASS_F32 && dtype != COMPASS_BF16)) return 0;
-  return up((size_t)R * D * (dtype == COMPASS_BF16 ? 2 : 4)) + up((size_t)R * V * 4) +
-         2 * up((size_t)R * argmax_chunks(V) * 4);
+  if (dtype == COMPASS_BF16)  // LayerNorm rows, then per-row (max, id) partials of 128-column spans
+    return up((size_t)R * D * 2) + 2 * up((size_t)R * argmax_parts_bf16(V) * 4);
+  // fp32: LayerNorm rows, the logits, then per-row (max, id) winners of 4096-column chunks
+  return up((size_t)R * D * 4) + up((size_t)R * V * 4) + 2 * up((size_t)R * argmax_chunks(V) * 4);
 }
 
 int compass_logits_argmax(int32_t R, int32_t D, int32_t V, int32_t dtype, const void* h, int64_t ldh,
@@ -582,22 +586,29 @@ int compass_logits_argmax(int32_t R, int32_t D, int32_t V, int32_t dtype, const 
   if (((uintptr_t)workspace & (kAlign - 1)) != 0) return fail(COMPASS_E_ALIGN, "workspace not 256-byte aligned");
   const hipStream_t s = (hipStream_t)stream;
   void* a = workspace;
-  float* lg = (float*)((char*)workspace + up((size_t)R * D * (dtype == COMPASS_BF16 ? 2 : 4)));
-  float* pv = (float*)((char*)lg + up((size_t)R * V * 4));
-  int* pi = (int*)((char*)pv + up((size_t)R * argmax_chunks(V) * 4));
   BMap eb{};
   eb.kind = 0;
   eb.p[0] = embed;
   eb.ld0 = D;
   (void)hipGetLastError();
-  // Same LayerNorm and logits GEMM as compass_logits (the logits are bitwise those it
-  // returns for the same rows), then one argmax pass over them.
+  // Same LayerNorm and logits arithmetic as compass_logits (the maxima are bitwise those
+  // of the logits it returns for the same rows).
   LAUNCH("logits_layernorm", s, launch_layernorm(dtype, h, norm_w, ln_eps, a, R, D, s, (long long)ldh));
-  if (dtype == COMPASS_BF16)
-    LAUNCH("gemm_logits", s, launch_gemm_bf16_scaled_f32(a, D, R, D, eb, V, logit_scale, lg, (long long)V, s));
-  else
+  if (dtype == COMPASS_BF16) {
+    // The argmax is fused into the logits GEMM: only per-span partials reach memory.
+    float* pv = (float*)((char*)workspace + up((size_t)R * D * 2));
+    int* pi = (int*)((char*)pv + up((size_t)R * argmax_parts_bf16(V) * 4));
+    int parts = 0;
+    hipError_t ge = hipSuccess;
+    LAUNCH("gemm_logits_argmax", s, (parts = gemm_bf16_argmax(a, D, R, D, eb, V, logit_scale, pv, pi, s, &ge), ge));
+    LAUNCH("argmax", s, launch_argmax_partials(pv, pi, R, parts, token, max_logit, s));
+  } else {
+    float* lg = (float*)((char*)workspace + up((size_t)R * D * 4));
+    float* pv = (float*)((char*)lg + up((size_t)R * V * 4));
+    int* pi = (int*)((char*)pv + up((size_t)R * argmax_chunks(V) * 4));
     LAUNCH("gemm_logits", s, launch_gemm_f32_raw(a, D, R, D, eb, V, 1, lg, logit_scale, s));
-  LAUNCH("argmax", s, launch_argmax(lg, R, V, (long long)V, 1.f, pv, pi, token, max_logit, s));
+    LAUNCH("argmax", s, launch_argmax(lg, R, V, (long long)V, 1.f, pv, pi, token, max_logit, s));
+  }
   return ok();
 }
 

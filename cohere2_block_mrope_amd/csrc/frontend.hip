@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void decode_positions_kernel(int32_t* __restri
 
 // Argmax in two passes. Pass 1: workgroup (c, r) scans columns [c * ARG_COLS, +ARG_COLS)
 // of row r (16 coalesced loads in flight per thread) and writes its (value, id) winner;
-// pass 2: one wave per row reduces the row's chunk winners. Larger value wins, equal
+// pass 2: one workgroup per row reduces the row's chunk winners. Larger value wins, equal
 // values go to the smaller id; an all -inf (or NaN) row gives id 0.
 constexpr int ARG_COLS = 4096;
 
@@ -117,15 +117,33 @@ __global__ __launch_bounds__(256) void argmax_chunk_kernel(const float* __restri
   }
 }
 
-__global__ __launch_bounds__(64) void argmax_final_kernel(const float* __restrict__ pv, const int* __restrict__ pi,
-                                                          int nch, int32_t* __restrict__ token,
-                                                          float* __restrict__ max_logit) {
-  const int r = blockIdx.x, lane = threadIdx.x;
+__global__ __launch_bounds__(256) void argmax_final_kernel(const float* __restrict__ pv, const int* __restrict__ pi,
+                                                           int nch, int32_t* __restrict__ token,
+                                                           float* __restrict__ max_logit) {
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const float* rv = pv + (size_t)r * nch;
+  const int* ri = pi + (size_t)r * nch;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int c = lane; c < nch; c += 64) arg_better(bv, bi, pv[(size_t)r * nch + c], pi[(size_t)r * nch + c]);
+  for (int c0 = 0; c0 < nch; c0 += 8 * 256) {
+    float v[8];
+    int id[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {  // all loads first, then the compares
+      const int c = c0 + j * 256 + tid;
+      v[j] = c < nch ? rv[c] : -INFINITY;
+      id[j] = c < nch ? ri[c] : 0x7fffffff;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) arg_better(bv, bi, v[j], id[j]);
+  }
   wave_argmax(bv, bi);
-  if (lane == 0) {
+  __shared__ float s_v[4];
+  __shared__ int s_i[4];
+  if ((tid & 63) == 0) { s_v[tid >> 6] = bv; s_i[tid >> 6] = bi; }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < 4; ++w) arg_better(bv, bi, s_v[w], s_i[w]);
     token[r] = bi == 0x7fffffff ? 0 : bi;
     if (max_logit) max_logit[r] = bv;
   }
@@ -160,7 +178,13 @@ hipError_t launch_argmax(const float* raw, int R, int V, long long ldr, float sc
                          int32_t* token, float* max_logit, hipStream_t s) {
   const int nch = argmax_chunks(V);
   argmax_chunk_kernel<<<dim3(nch, R), 256, 0, s>>>(raw, V, ldr, scale, nch, pv, pi);
-  argmax_final_kernel<<<R, 64, 0, s>>>(pv, pi, nch, token, max_logit);
+  argmax_final_kernel<<<R, 256, 0, s>>>(pv, pi, nch, token, max_logit);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax_partials(const float* pv, const int* pi, int R, int nparts, int32_t* token,
+                                  float* max_logit, hipStream_t s) {
+  argmax_final_kernel<<<R, 256, 0, s>>>(pv, pi, nparts, token, max_logit);
   return hipGetLastError();
 }
 

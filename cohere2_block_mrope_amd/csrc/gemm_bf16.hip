@@ -1,7 +1,7 @@
 // bf16 GEMMs on gfx950 MFMA (v_mfma_f32_32x32x16_bf16, fp32 accumulation):
 //   C[m, n] = sum_k A[m, k] * B[n, k]    (A [M, K] and B [N, K] both K-contiguous)
 //
-// One kernel template serves the four GEMMs of the layer:
+// One kernel template serves the GEMMs of the layer and the head:
 //   PROJ   the fused q/k/v/gate/up projection of "Text decoder forward" (mlxcel
 //          Compass issue). Its epilogue applies interleaved MRoPE to q and k in
 //          registers, scatters q to [B, Hq, L, hd], k/v to the cache [B, Hkv, cap, hd],
@@ -9,6 +9,8 @@
 //   RESID  the output GEMM [o | act] . [Wo | Wd]^T plus the residual x (parallel
 //          block: h + attn + mlp);
 //   SCALED the tied-embedding logits times logit_scale, stored as fp32;
+//   ARGMAX the same logits reduced in registers to per-row (max, id) partials (greedy
+//          decoding without storing the logits);
 //   RAW    fp32 partial sums over a K-slice (split-K for skinny decode GEMMs).
 //
 // Tiling: a 256-thread workgroup (4 waves, 2 x 2) computes a BM x BN tile; each wave
@@ -119,7 +121,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams P) {
           (BKIND == 2 && k0 >= P.bm.ksplit) ? bbase1 + boff1[i] + k0 : bbase0 + boff[i] + k0);
       // Skinny GEMMs (split-K decode projections, logits of at most 128 rows: one row
       // tile) read each weight row once: stream it past the caches.
-      if constexpr (MODE == MODE_RAW || (MODE == MODE_SCALED && BM <= 128)) rb[i] = __builtin_nontemporal_load(src);
+      if constexpr (MODE == MODE_RAW || ((MODE == MODE_SCALED || MODE == MODE_ARGMAX) && BM <= 128))
+        rb[i] = __builtin_nontemporal_load(src);
       else rb[i] = *src;
     }
   };
@@ -209,7 +212,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams P) {
     step(kt, false, false);
   }
 
-  gemm_epilogue<MODE, MB, NB>(P, acc, m0 + wm * WM, n0 + wn * WN, lane, blockIdx.z);
+  if constexpr (MODE == MODE_ARGMAX) argmax_epilogue<MB, NB>(P, acc, m0 + wm * WM, n0 + wn * WN, 2 * tn + wn, lane);
+  else gemm_epilogue<MODE, MB, NB>(P, acc, m0 + wm * WM, n0 + wn * WN, lane, blockIdx.z);
 }
 
 template <int BM, int BN, int MODE, int BKIND>
@@ -334,6 +338,28 @@ hipError_t launch_gemm_bf16_scaled_f32(const void* A, int lda, int M, int K, con
   P.tiles_m = (M + 255) / 256;
   P.tiles_n = (N + 255) / 256;
   return launch<256, 256, MODE_SCALED, 0>(P, dim3(P.tiles_m * P.tiles_n), s);
+}
+
+int gemm_bf16_argmax(const void* A, int lda, int M, int K, const BMap& bm, int N, float scale, float* pv,
+                     int* pi, hipStream_t s, hipError_t* err) {
+  GemmParams P = base_params(A, lda, M, K, bm, N);
+  P.outf = pv;
+  P.outi = pi;
+  P.scale = scale;
+  if (M <= 64) {
+    P.tiles_m = 1;
+    P.tiles_n = (N + 255) / 256;
+    *err = launch<64, 256, MODE_ARGMAX, 0>(P, dim3(P.tiles_n), s);
+  } else if (M <= 128) {
+    P.tiles_m = 1;
+    P.tiles_n = (N + 255) / 256;
+    *err = launch<128, 256, MODE_ARGMAX, 0>(P, dim3(P.tiles_n), s);
+  } else {
+    P.tiles_m = (M + 255) / 256;
+    P.tiles_n = (N + 255) / 256;
+    *err = launch<256, 256, MODE_ARGMAX, 0>(P, dim3(P.tiles_m * P.tiles_n), s);
+  }
+  return 2 * P.tiles_n;
 }
 
 hipError_t launch_gemm_bf16_raw(const void* A, int lda, int M, int K, const BMap& bm, int N,

@@ -8,7 +8,7 @@
 namespace compass {
 namespace gemm {
 
-enum { MODE_PROJ = 0, MODE_RESID = 1, MODE_SCALED = 2, MODE_RAW = 3 };
+enum { MODE_PROJ = 0, MODE_RESID = 1, MODE_SCALED = 2, MODE_RAW = 3, MODE_ARGMAX = 4 };
 
 struct GemmParams {
   const bf16_t* A;
@@ -20,9 +20,10 @@ struct GemmParams {
   const bf16_t* x;   // RESID
   bf16_t* out;
   int ldo;
-  float* outf;       // SCALED
+  float* outf;       // SCALED; ARGMAX: per-row partial maxima [M][2 * tiles_n]
   long long ldof;
-  float scale;
+  float scale;       // SCALED, ARGMAX
+  int* outi;         // ARGMAX: the ids of those maxima
   RowStart rs;       // RESID: rows of batch rows that are not live are not stored
   ProjEpi ep;        // PROJ
   RopeTable rt;
@@ -185,6 +186,42 @@ __device__ __forceinline__ void proj_qkv_epilogue(const GemmParams& P, const f32
         }
       }
   }
+}
+
+// ARGMAX: per row, the largest scale * C over the wave's 128 columns and its column
+// (smallest column on ties; NaN never wins), written as partial 2 tn + wn of the row.
+// Register r of lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4 of each block, column
+// l % 32: the scan runs over the blocks j in column order, then over the 32 lanes of
+// each half-wave (the xor offsets below 32 stay inside a half).
+template <int MB, int NB>
+__device__ __forceinline__ void argmax_epilogue(const GemmParams& P, const f32x16_t (&acc)[MB][NB], int mw0,
+                                                int nw0, int part, int lane) {
+  const int c = lane & 31;
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int n = nw0 + 32 * j + c;
+        const float x = acc[i][j][r] * P.scale;
+        if (n < P.N && x > bv) { bv = x; bi = n; }
+      }
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      }
+      const int m = mw0 + 32 * i + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+      if (c == 0 && m < P.M) {
+        const size_t o = (size_t)m * (2 * P.tiles_n) + part;
+        P.outf[o] = bv;
+        P.outi[o] = bi;
+      }
+    }
 }
 
 // Stores one wave's accumulators (MB x NB blocks of 32 x 32 at rows mw0.., columns nw0..).

@@ -101,6 +101,11 @@ hipError_t launch_gemm_bf16_resid(const void* A, int lda, int M, int K, const BM
 // out[m, n] = C * scale (fp32).
 hipError_t launch_gemm_bf16_scaled_f32(const void* A, int lda, int M, int K, const BMap& bm, int N,
                                        float scale, float* out, long long ldo, hipStream_t s);
+// Greedy head without storing the logits: pv[m][p], pi[m][p] = the largest C * scale over
+// the p-th 128-column span of row m and its column (smallest on ties). Returns the number
+// of spans per row (2 * ceil(N / 256)); *err receives the launch status.
+int gemm_bf16_argmax(const void* A, int lda, int M, int K, const BMap& bm, int N, float scale, float* pv,
+                     int* pi, hipStream_t s, hipError_t* err);
 // raw[z][m][n] = partial C over K-slice z (fp32), splits slices of K (64 x 64 tiles, for
 // skinny decode GEMMs; the _wide variant uses 256 x 256 tiles).
 hipError_t launch_gemm_bf16_raw(const void* A, int lda, int M, int K, const BMap& bm, int N,
@@ -157,6 +162,9 @@ hipError_t launch_decode_positions(int32_t* lens, const int32_t* rope_delta, int
 // token[r] = argmax_v scale * raw[r * ldr + v] (smallest v on ties); max_logit optional.
 // pv / pi: per-row chunk winners, R * argmax_chunks(V) floats / ints of scratch.
 int argmax_chunks(int V);
+// token[r] / max_logit[r] from nparts (value, id) partials per row (smallest id on ties).
+hipError_t launch_argmax_partials(const float* pv, const int* pi, int R, int nparts, int32_t* token,
+                                  float* max_logit, hipStream_t s);
 hipError_t launch_argmax(const float* raw, int R, int V, long long ldr, float scale, float* pv, int* pi,
                          int32_t* token, float* max_logit, hipStream_t s);
 

@@ -198,9 +198,11 @@ def test_front_end_argument_errors(b):
     assert L.compass_decode_positions(4, None, None, 0, 0x2000, None) == b.COMPASS_E_INVALID
     assert L.compass_decode_positions(4, 0x1000, None, 0, 0x1008, None) == b.COMPASS_E_INVALID
     # logits argmax
-    # LayerNorm rows, fp32 logits, then the per-chunk (value, id) winners of 4096-column chunks
-    assert b.compass_logits_argmax_workspace_size(64, 2048, 256000, 1) == \
-        64 * 2048 * 2 + 64 * 256000 * 4 + 2 * 256 * 63
+    # bf16: LayerNorm rows, then (value, id) partials of the 2000 128-column spans per row
+    assert b.compass_logits_argmax_workspace_size(64, 2048, 256000, 1) == 64 * 2048 * 2 + 2 * 64 * 2000 * 4
+    # fp32: LayerNorm rows, the logits, then the winners of 4096-column chunks
+    assert b.compass_logits_argmax_workspace_size(64, 2048, 256000, 0) == \
+        64 * 2048 * 4 + 64 * 256000 * 4 + 2 * 256 * 63
     assert b.compass_logits_argmax_workspace_size(64, 2048, 256000, 9) == 0
     ws = 0x10000000
     need = b.compass_logits_argmax_workspace_size(8, 2048, 1000, 1)
