@@ -105,6 +105,19 @@ def _chunk_start_off_by_one(shape, w, x, pos, k_cache, v_cache, start):
     return _orig_chunk(shape, w, x, pos, k_cache, v_cache, np.maximum(np.asarray(start) - 1, 0))
 
 
+_orig_embed = O.embed
+_orig_greedy = O.greedy_token
+
+
+def _embed_ignores_image_rows(tokens, embed_table, image_rows=None, image_feats=None):
+    return _orig_embed(tokens, embed_table)
+
+
+def _greedy_last_maximum(h_last, norm_w, eps, embed_table, logit_scale):
+    lg = O.logits(h_last, norm_w, eps, embed_table, logit_scale)
+    return lg.shape[1] - 1 - np.argmax(lg[:, ::-1], axis=1)
+
+
 MUTANTS = {
     "rotate_half sign": ("rotate_half", _rotate_half_wrong_sign),
     "pairwise rope": ("rotate_half", _rotate_half_pairwise),
@@ -121,6 +134,8 @@ MUTANTS = {
     "chunk ignores the cache": ("layer_prefill_chunk", _chunk_ignores_cache),
     "chunk start off by one": ("layer_prefill_chunk", _chunk_start_off_by_one),
     "decode positions ignore rope_delta": ("decode_positions", _decode_positions_without_delta),
+    "embed ignores image rows": ("embed", _embed_ignores_image_rows),
+    "greedy ties to the last id": ("greedy_token", _greedy_last_maximum),
 }
 
 PINS = [
@@ -137,6 +152,8 @@ PINS = [
     lambda: P.test_chunked_prefill_equals_one_prefill("sliding", 3),
     lambda: P.test_chunked_prefill_equals_one_prefill("full", 0),
     P.test_greedy_generation_equals_full_recompute,
+    P.test_embed_front_end,
+    P.test_greedy_token_is_first_maximum,
 ]
 
 

@@ -411,6 +411,23 @@ def test_embed_front_end():
     np.testing.assert_array_equal(h, [[12, 13, 14], [9, 9, 9], [6, 7, 8], [8, 8, 8]])
 
 
+def test_greedy_token_is_first_maximum():
+    """Equal largest logits give the smallest id; the chosen id carries the row's largest logit
+    (brute force over the vocabulary)."""
+    r = np.random.default_rng(77)
+    h, nw = r.standard_normal((3, 16)), 1 + 0.1 * r.standard_normal(16)
+    E = r.standard_normal((12, 16))
+    a = O.layer_norm(h, nw, 1e-5)
+    best = int(np.argmax(a[0] @ E.T))
+    E[[2, 9]] = E[best]                       # three equal maxima for row 0
+    tok = O.greedy_token(h, nw, 1e-5, E, 0.5)
+    assert tok[0] == 2
+    lg = O.logits(h, nw, 1e-5, E, 0.5)
+    for i in range(3):
+        assert all(lg[i, tok[i]] >= lg[i, v] for v in range(12))
+        assert all(lg[i, tok[i]] > lg[i, v] for v in range(tok[i]))
+
+
 def test_greedy_generation_equals_full_recompute():
     """Every generated token equals the argmax of the last row of a cache-free stack prefill
     over prompt + the tokens generated so far, with positions recomputed by the position
