@@ -26,6 +26,10 @@ the design notes of the repository):
     keys n - W < j <= n (sliding) or j <= n (full).
   * Chunked prefill: new token i of row b sits at cache index start[b] + i, with
     the same visibility rule as decode.
+  * 4-bit weights (the quantization block of page 1's config section: group size
+    64, 4 bits, affine): a weight is scale * code + bias with one (scale, bias)
+    per 64 consecutive input columns; byte j of a packed row holds column 2j in
+    its low nibble and column 2j + 1 in its high nibble.
 """
 from __future__ import annotations
 
@@ -321,6 +325,49 @@ def layer_decode(shape, w: Dict[str, np.ndarray], x: np.ndarray, pos: np.ndarray
         out = x[b] + (o @ np.asarray(w["wo"], dtype=F64).T)[0] + (act @ np.asarray(w["w_down"], dtype=F64).T)[0]
         outs.append(out); ks.append(kh[:, 0, :]); vs.append(vh[:, 0, :])
     return np.stack(outs), np.stack(ks), np.stack(vs)
+
+
+# ----------------------------------------------------------------------------------------
+# 4-bit affine weights. Page 1, config section: the 4-bit checkpoint carries a quantization
+# block {group_size 64, bits 4, mode affine}. Affine mode: a weight is its group's scale
+# times its 4-bit code plus its group's bias; groups are 64 consecutive input columns of
+# one output row. The nibble order inside a byte is not printed (reading: low nibble first).
+# ----------------------------------------------------------------------------------------
+Q4_GROUP = 64
+
+
+def unpack_q4(packed: np.ndarray) -> np.ndarray:
+    """packed uint8 [rows, cols / 2] -> codes [rows, cols] in 0..15."""
+    p = np.asarray(packed, dtype=np.uint8)
+    codes = np.empty((p.shape[0], 2 * p.shape[1]), dtype=np.int64)
+    codes[:, 0::2] = p & 0x0F
+    codes[:, 1::2] = p >> 4
+    return codes
+
+
+def dequantize_q4(packed: np.ndarray, scales: np.ndarray, biases: np.ndarray) -> np.ndarray:
+    """w[r, c] = scales[r, c // 64] * code[r, c] + biases[r, c // 64], in fp64."""
+    codes = unpack_q4(packed).astype(F64)
+    s = np.repeat(np.asarray(scales, dtype=F64), Q4_GROUP, axis=1)
+    b = np.repeat(np.asarray(biases, dtype=F64), Q4_GROUP, axis=1)
+    return s * codes + b
+
+
+Q4_MATRICES = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
+
+
+def dequantize_layer_q4(wq4: Dict[str, object]) -> Dict[str, np.ndarray]:
+    """wq4: ln_w plus, for each matrix, a (packed, scales, biases) triple."""
+    w = {"ln_w": np.asarray(wq4["ln_w"], dtype=F64)}
+    for name in Q4_MATRICES:
+        w[name] = dequantize_q4(*wq4[name])
+    return w
+
+
+def layer_decode_q4(shape, wq4: Dict[str, object], x: np.ndarray, pos: np.ndarray, k_cache: np.ndarray,
+                    v_cache: np.ndarray, lens: np.ndarray, rows: Optional[Sequence[int]] = None):
+    """The decode step with 4-bit weights: the layer of the dequantized weights."""
+    return layer_decode(shape, dequantize_layer_q4(wq4), x, pos, k_cache, v_cache, lens, rows)
 
 
 # ----------------------------------------------------------------------------------------

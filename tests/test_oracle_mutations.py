@@ -118,6 +118,28 @@ def _greedy_last_maximum(h_last, norm_w, eps, embed_table, logit_scale):
     return lg.shape[1] - 1 - np.argmax(lg[:, ::-1], axis=1)
 
 
+_orig_unpack_q4 = O.unpack_q4
+_orig_dequantize_q4 = O.dequantize_q4
+
+
+def _unpack_q4_high_first(packed):
+    c = _orig_unpack_q4(packed)
+    out = c.copy()
+    out[:, 0::2], out[:, 1::2] = c[:, 1::2], c[:, 0::2]
+    return out
+
+
+def _dequantize_q4_group_32(packed, scales, biases):
+    codes = _orig_unpack_q4(packed).astype(float)
+    s = np.repeat(np.asarray(scales, float), 32, axis=1)[:, :codes.shape[1]]
+    b = np.repeat(np.asarray(biases, float), 32, axis=1)[:, :codes.shape[1]]
+    return s * codes + b
+
+
+def _dequantize_q4_no_bias(packed, scales, biases):
+    return _orig_dequantize_q4(packed, scales, np.zeros_like(np.asarray(biases, float)))
+
+
 MUTANTS = {
     "rotate_half sign": ("rotate_half", _rotate_half_wrong_sign),
     "pairwise rope": ("rotate_half", _rotate_half_pairwise),
@@ -136,6 +158,9 @@ MUTANTS = {
     "decode positions ignore rope_delta": ("decode_positions", _decode_positions_without_delta),
     "embed ignores image rows": ("embed", _embed_ignores_image_rows),
     "greedy ties to the last id": ("greedy_token", _greedy_last_maximum),
+    "q4 nibbles high first": ("unpack_q4", _unpack_q4_high_first),
+    "q4 groups of 32": ("dequantize_q4", _dequantize_q4_group_32),
+    "q4 bias dropped": ("dequantize_q4", _dequantize_q4_no_bias),
 }
 
 PINS = [
@@ -154,6 +179,10 @@ PINS = [
     P.test_greedy_generation_equals_full_recompute,
     P.test_embed_front_end,
     P.test_greedy_token_is_first_maximum,
+    P.test_q4_format_from_page_and_nibble_example,
+    P.test_q4_dequantize_brute_force_and_closed_forms,
+    P.test_q4_round_trip_within_half_step,
+    P.test_q4_decode_is_dense_decode_of_dequantized_weights,
 ]
 
 

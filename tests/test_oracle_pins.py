@@ -459,6 +459,78 @@ def test_greedy_generation_equals_full_recompute():
         np.testing.assert_array_equal(O.greedy_token(h[:, -1], nw, sh.ln_eps, E, 0.25), gen[:, k])
 
 
+# ------------------------------------------------------------------------------ 4-bit weights
+def test_q4_format_from_page_and_nibble_example():
+    g = golden("q4_affine.json")
+    assert (g["group_size"], g["bits"], g["mode"]) == (O.Q4_GROUP, 4, "affine")
+    np.testing.assert_array_equal(O.unpack_q4(np.array(g["packed_example"], np.uint8)), g["codes_example"])
+
+
+def test_q4_dequantize_brute_force_and_closed_forms():
+    """Element by element with explicit bit operations; code 0 gives the bias, code 15 gives
+    15 * scale + bias; columns 63 and 64 take different groups."""
+    r = np.random.default_rng(80)
+    rows, cols = 3, 192
+    packed = r.integers(0, 256, (rows, cols // 2)).astype(np.uint8)
+    sc = r.uniform(0.001, 0.01, (rows, cols // 64))
+    bi = r.uniform(-0.05, 0.05, (rows, cols // 64))
+    got = O.dequantize_q4(packed, sc, bi)
+    for i in range(rows):
+        for c in range(cols):
+            byte = int(packed[i, c // 2])
+            code = (byte >> (4 * (c % 2))) & 15
+            assert got[i, c] == sc[i, c // 64] * code + bi[i, c // 64]
+    zero = np.zeros((1, 64), np.uint8)
+    assert np.all(O.dequantize_q4(zero, [[0.5, 0.25]], [[-1.0, 2.0]])[0, :64] == -1.0)
+    full = np.full((1, 64), 0xFF, np.uint8)
+    out = O.dequantize_q4(full, [[0.5, 0.25]], [[-1.0, 2.0]])[0]
+    assert np.all(out[:64] == 6.5) and np.all(out[64:] == 5.75)
+
+
+def quantize_minmax(w):
+    """Textbook min/max affine quantizer (written here, independent of the oracle)."""
+    rows, cols = w.shape
+    g = w.reshape(rows, cols // 64, 64)
+    lo, hi = g.min(-1), g.max(-1)
+    scale = (hi - lo) / 15.0
+    codes = np.clip(np.rint((g - lo[..., None]) / scale[..., None]), 0, 15).astype(np.uint8).reshape(rows, cols)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, scale, lo
+
+
+def test_q4_round_trip_within_half_step():
+    r = np.random.default_rng(81)
+    w = 0.02 * r.standard_normal((32, 256))
+    packed, scale, lo = quantize_minmax(w)
+    back = O.dequantize_q4(packed, scale, lo)
+    step = np.repeat(scale, 64, axis=1)
+    assert np.all(np.abs(back - w) <= 0.5 * step + 1e-15)
+    assert np.max(np.abs(back - w)) > 0.3 * step.min()   # not a trivial identity
+
+
+def test_q4_decode_is_dense_decode_of_dequantized_weights():
+    sh = tiny_shape("sliding", 3, hd=16, D=64, I=128, section=(4, 2, 2))  # every input width a multiple of 64
+    r = np.random.default_rng(82)
+    dense = rand_weights(sh, seed=83, std=0.2)
+    wq4 = {"ln_w": dense["ln_w"]}
+    deq = {"ln_w": dense["ln_w"]}
+    for name in O.Q4_MATRICES:
+        packed, scale, lo = quantize_minmax(dense[name])
+        wq4[name] = (packed, scale, lo)
+        codes = np.empty(dense[name].shape)
+        codes[:, 0::2], codes[:, 1::2] = packed & 15, packed >> 4
+        deq[name] = np.repeat(scale, 64, axis=1) * codes + np.repeat(lo, 64, axis=1)
+    B, cap = 2, 9
+    x = r.standard_normal((B, 64))
+    kc, vc = r.standard_normal((B, 2, cap, 16)), r.standard_normal((B, 2, cap, 16))
+    lens = np.array([4, 8])
+    pos = O.decode_positions(lens, np.array([0, -3]))
+    got = O.layer_decode_q4(sh, wq4, x, pos, kc, vc, lens)
+    ref = O.layer_decode(sh, deq, x, pos, kc, vc, lens)
+    for a, b in zip(got, ref):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+
+
 # ------------------------------------------------------------------------------ logits
 def test_logits_vs_library_and_scale():
     r = np.random.default_rng(60)
