@@ -199,6 +199,19 @@ def run_c3(args, b, H, W, torch):
 
     sec_g, stats_g = timed(greedy_step, max(5, args.steps), 3, b, torch)
     assert int(est.item()) == 0
+
+    # The same decode step with 4-bit affine weights (group 64) in the four layers.
+    # The ctypes structs hold raw device pointers: q4_dev keeps the tensors alive.
+    q4_dev = [H.q4_to_dev(W.make_layer_weights_q4(dataclasses.replace(sh, kind=layer_kind(i)), 3, i))
+              for i in range(n_layers)]
+    q4 = [b.make_weights_q4(wd) for wd in q4_dev]
+
+    def q4_step():
+        h.copy_(x)
+        for (d, _, _, kc, vc, ws), wq in zip(layers, q4):
+            b.compass_layer_decode_q4(d, wq, h, pos, b.make_kv(kc, vc, lens), h, ws)
+
+    sec_q, stats_q = timed(q4_step, max(5, args.steps), 3, b, torch)
     kv_bytes_slide = Bn * Hkv * sh.window * hd * 2 * 2
     kv_bytes_full = Bn * Hkv * (n + 1) * hd * 2 * 2
     w_bytes = 2 * (sh.hidden * ((sh.n_q_heads + 2 * Hkv) * hd + 2 * sh.intermediate)
@@ -210,6 +223,16 @@ def run_c3(args, b, H, W, torch):
            "kernels_us": {k: round(v["mean_us"], 1) for k, v in stats.items()}}
     if att:
         res["decode_attn_hbm_frac"] = att_bytes_mean / (att["mean_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS
+    q4_bytes_proj = (sh.hidden // 2 + 4 * (sh.hidden // 64)) * ((sh.n_q_heads + 2 * Hkv) * hd + 2 * sh.intermediate)
+    K2 = sh.n_q_heads * hd + sh.intermediate
+    q4_bytes_out = (K2 // 2 + 4 * (K2 // 64)) * sh.hidden
+    res["q4_step"] = {"us_per_step": 1e6 * sec_q,
+                      "what": "the same 4-layer decode step with 4-bit affine weights (group 64)",
+                      "kernels_us": {k: round(v["mean_us"], 1) for k, v in stats_q.items()}}
+    for name, nbytes in (("gemm_proj_decode_q4", q4_bytes_proj), ("gemm_out_decode_q4", q4_bytes_out)):
+        st = stats_q.get(name)
+        if st:
+            res["q4_step"][name + "_weight_hbm_frac"] = nbytes / (st["mean_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS
     lg = stats_g.get("gemm_logits_argmax", {})
     res["greedy_step"] = {"us_per_step": 1e6 * sec_g,
                           "what": "embed + decode positions + the 4 layers + tied 256000-vocab logits argmax",

@@ -55,6 +55,15 @@ class compass_kv(ctypes.Structure):
                 ("lens", ctypes.c_void_p)]
 
 
+class compass_q4_matrix(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p)]
+
+
+class compass_layer_weights_q4(ctypes.Structure):
+    _fields_ = [("ln_w", ctypes.c_void_p)] + [(n, compass_q4_matrix) for n in
+                                              ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")]
+
+
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
 _sig = {
@@ -69,6 +78,9 @@ _sig = {
                                                    ctypes.c_size_t, _P]),
     "compass_layer_decode": (ctypes.c_int, [ctypes.POINTER(compass_layer_desc), ctypes.POINTER(compass_layer_weights),
                                             _I, _P, _P, ctypes.POINTER(compass_kv), _P, _P, ctypes.c_size_t, _P]),
+    "compass_layer_decode_q4": (ctypes.c_int, [ctypes.POINTER(compass_layer_desc),
+                                               ctypes.POINTER(compass_layer_weights_q4), _I, _P, _P,
+                                               ctypes.POINTER(compass_kv), _P, _P, ctypes.c_size_t, _P]),
     "compass_logits_workspace_size": (ctypes.c_size_t, [_I, _I, _I]),
     "compass_logits": (ctypes.c_int, [_I, _I, _I, _I, _P, _P, ctypes.c_float, _P, ctypes.c_float, _P, _P,
                                       ctypes.c_size_t, _P]),
@@ -126,6 +138,16 @@ def make_weights(w: dict) -> compass_layer_weights:
     return s
 
 
+def make_weights_q4(w: dict) -> compass_layer_weights_q4:
+    """w: ln_w tensor, and for each matrix name a (codes, scales, biases) tuple of tensors."""
+    s = compass_layer_weights_q4()
+    s.ln_w = _ptr(w["ln_w"])
+    for name, _ in compass_layer_weights_q4._fields_[1:]:
+        q, sc, bi = w[name]
+        setattr(s, name, compass_q4_matrix(_ptr(q), _ptr(sc), _ptr(bi)))
+    return s
+
+
 def make_kv(k, v, lens=None) -> compass_kv:
     s = compass_kv()
     s.k, s.v = _ptr(k), _ptr(v)
@@ -179,6 +201,14 @@ def compass_layer_decode(desc, weights: compass_layer_weights, x, pos, kv: compa
     _check(_lib.compass_layer_decode(ctypes.byref(desc), ctypes.byref(weights), B, _ptr(x), _ptr(pos),
                                      ctypes.byref(kv), _ptr(out), _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def compass_layer_decode_q4(desc, weights: compass_layer_weights_q4, x, pos, kv: compass_kv, out, workspace,
+                            stream=None) -> None:
+    B = x.shape[0]
+    _check(_lib.compass_layer_decode_q4(ctypes.byref(desc), ctypes.byref(weights), B, _ptr(x), _ptr(pos),
+                                        ctypes.byref(kv), _ptr(out), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def compass_logits_workspace_size(R: int, D: int, dtype: int) -> int:

@@ -254,6 +254,52 @@ BMap out_bmap(const compass_layer_desc* d, const compass_layer_weights* w) {
   return b;
 }
 
+int check_weights_q4(const compass_layer_desc* d, const compass_layer_weights_q4* w) {
+  if (d->dtype != COMPASS_BF16) return fail(COMPASS_E_UNSUPPORTED, "4-bit weights need the bf16 dtype");
+  if (!w->ln_w) return fail(COMPASS_E_INVALID, "weight ln_w is NULL");
+  if (!aligned16(w->ln_w)) return fail(COMPASS_E_ALIGN, "weight ln_w not 16-byte aligned");
+  const compass_q4_matrix* mats[7] = {&w->wq, &w->wk, &w->wv, &w->wo, &w->w_gate, &w->w_up, &w->w_down};
+  const char* n[7] = {"wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"};
+  for (int i = 0; i < 7; ++i) {
+    if (!mats[i]->q || !mats[i]->scales || !mats[i]->biases)
+      return fail(COMPASS_E_INVALID, "4-bit weight %s has a NULL pointer", n[i]);
+    if (!aligned16(mats[i]->q)) return fail(COMPASS_E_ALIGN, "codes of %s not 16-byte aligned", n[i]);
+    if (((uintptr_t)mats[i]->scales & 1) || ((uintptr_t)mats[i]->biases & 1))
+      return fail(COMPASS_E_ALIGN, "scales/biases of %s not 2-byte aligned", n[i]);
+  }
+  const Dims m = dims(d);
+  if (m.qd % 64) return fail(COMPASS_E_UNSUPPORTED, "n_q_heads * head_dim must be a multiple of 64 for 4-bit weights");
+  return COMPASS_OK;
+}
+
+Q4Map proj_q4map(const compass_layer_desc* d, const compass_layer_weights_q4* w) {
+  const Dims m = dims(d);
+  Q4Map b{};
+  b.kind = 1;
+  const compass_q4_matrix* mats[5] = {&w->wq, &w->wk, &w->wv, &w->w_gate, &w->w_up};
+  for (int i = 0; i < 5; ++i) {
+    b.q[i] = mats[i]->q;
+    b.s[i] = mats[i]->scales;
+    b.b[i] = mats[i]->biases;
+  }
+  b.cols0 = (int)m.D;
+  b.nq64 = (int)(m.qd / 64);
+  b.nk64 = (int)(m.Hkv * m.hd / 64);
+  return b;
+}
+
+Q4Map out_q4map(const compass_layer_desc* d, const compass_layer_weights_q4* w) {
+  const Dims m = dims(d);
+  Q4Map b{};
+  b.kind = 2;
+  b.q[0] = w->wo.q; b.s[0] = w->wo.scales; b.b[0] = w->wo.biases;
+  b.q[1] = w->w_down.q; b.s[1] = w->w_down.scales; b.b[1] = w->w_down.biases;
+  b.cols0 = (int)m.qd;
+  b.cols1 = (int)m.I;
+  b.ksplit = (int)m.qd;
+  return b;
+}
+
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
   return x < y + nb && y < x + na;
@@ -405,12 +451,17 @@ int compass_layer_prefill_chunk(const compass_layer_desc* d, const compass_layer
   return prefill_impl(d, w, B, L, x, pos, kv, kv->lens, ds_rows, ds, n_ds, out, workspace, ws_bytes, stream);
 }
 
-int compass_layer_decode(const compass_layer_desc* d, const compass_layer_weights* w, int32_t B,
-                         const void* x, const int32_t* pos, const compass_kv* kv, void* out,
-                         void* workspace, size_t ws_bytes, void* stream) {
+// One decode step; the GEMM weights are either bf16/fp32 (w) or 4-bit affine (wq).
+static int decode_impl(const compass_layer_desc* d, const compass_layer_weights* w,
+                       const compass_layer_weights_q4* wq, int32_t B, const void* x, const int32_t* pos,
+                       const compass_kv* kv, void* out, void* workspace, size_t ws_bytes, void* stream) {
   int rc = check_desc(d);
   if (rc) return rc;
-  if ((rc = check_weights(w))) return rc;
+  if (wq) {
+    if ((rc = check_weights_q4(d, wq))) return rc;
+  } else if ((rc = check_weights(w))) {
+    return rc;
+  }
   if (B < 1) return fail(COMPASS_E_INVALID, "B=%d must be >= 1", B);
   const Dims m = dims(d);
   if ((long long)B * (m.K2 > m.Nv ? m.K2 : m.Nv) > (1LL << 31) - 1)
@@ -457,27 +508,51 @@ int compass_layer_decode(const compass_layer_desc* d, const compass_layer_weight
   ep.nq64 = (int)(m.qd / 64); ep.nk64 = (int)(m.Hkv * m.hd / 64);
   ep.I = (int)m.I;
   const RopeTable rt = rope_table(d);
-  const BMap pb = proj_bmap(d, w), ob = out_bmap(d, w);
 
   (void)hipGetLastError();
-  LAUNCH("layernorm", s, launch_layernorm(dt, x, w->ln_w, d->ln_eps, a, B, (int)m.D, s));
-  if (dt == COMPASS_BF16)
-    LAUNCH("gemm_proj_decode", s, launch_gemm_bf16_raw(a, (int)m.D, B, (int)m.D, pb, (int)m.Nv, ws.s1, raw1, s));
+  LAUNCH("layernorm", s, launch_layernorm(dt, x, wq ? wq->ln_w : w->ln_w, d->ln_eps, a, B, (int)m.D, s));
+  const int s1 = ws.s1, s2 = ws.s2;
+  if (wq)
+    LAUNCH("gemm_proj_decode_q4", s, launch_gemm_q4_raw(a, (int)m.D, B, (int)m.D, proj_q4map(d, wq), (int)m.Nv, s1,
+                                                        raw1, s));
+  else if (dt == COMPASS_BF16)
+    LAUNCH("gemm_proj_decode", s, launch_gemm_bf16_raw(a, (int)m.D, B, (int)m.D, proj_bmap(d, w), (int)m.Nv, s1,
+                                                       raw1, s));
   else
-    LAUNCH("gemm_proj_decode", s, launch_gemm_f32_raw(a, (int)m.D, B, (int)m.D, pb, (int)m.Nv, ws.s1, raw1, 1.f, s));
-  LAUNCH("proj_epilogue", s, launch_proj_epilogue(dt, raw1, ws.s1, B, (int)m.Nv, ep, rt, s));
+    LAUNCH("gemm_proj_decode", s, launch_gemm_f32_raw(a, (int)m.D, B, (int)m.D, proj_bmap(d, w), (int)m.Nv, ws.s1,
+                                                      raw1, 1.f, s));
+  LAUNCH("proj_epilogue", s, launch_proj_epilogue(dt, raw1, s1, B, (int)m.Nv, ep, rt, s));
   LAUNCH("decode_attn", s, launch_decode_attention(dt, q, kv->k, kv->v, kv->lens, B, (int)m.Hq, (int)m.Hkv,
                                                    kv->capacity, (int)m.hd, sliding, d->window,
                                                    ws.n_chunks, part, s));
   LAUNCH("decode_combine", s, launch_decode_combine(dt, part, kv->lens, B, (int)m.Hq, kv->capacity,
                                                     (int)m.hd, ws.n_chunks, a2, (int)m.K2, s));
-  if (dt == COMPASS_BF16)
-    LAUNCH("gemm_out_decode", s, launch_gemm_bf16_raw(a2, (int)m.K2, B, (int)m.K2, ob, (int)m.D, ws.s2, raw2, s));
+  if (wq)
+    LAUNCH("gemm_out_decode_q4", s, launch_gemm_q4_raw(a2, (int)m.K2, B, (int)m.K2, out_q4map(d, wq), (int)m.D, s2,
+                                                       raw2, s));
+  else if (dt == COMPASS_BF16)
+    LAUNCH("gemm_out_decode", s, launch_gemm_bf16_raw(a2, (int)m.K2, B, (int)m.K2, out_bmap(d, w), (int)m.D, s2,
+                                                      raw2, s));
   else
-    LAUNCH("gemm_out_decode", s, launch_gemm_f32_raw(a2, (int)m.K2, B, (int)m.K2, ob, (int)m.D, ws.s2, raw2, 1.f, s));
-  LAUNCH("splitk_resid", s, launch_splitk_resid(dt, raw2, ws.s2, B, (int)m.D, x, out,
+    LAUNCH("gemm_out_decode", s, launch_gemm_f32_raw(a2, (int)m.K2, B, (int)m.K2, out_bmap(d, w), (int)m.D, ws.s2,
+                                                     raw2, 1.f, s));
+  LAUNCH("splitk_resid", s, launch_splitk_resid(dt, raw2, s2, B, (int)m.D, x, out,
                                                 RowStart{kv->lens, 1, kv->capacity}, s));
   return ok();
+}
+
+int compass_layer_decode(const compass_layer_desc* d, const compass_layer_weights* w, int32_t B,
+                         const void* x, const int32_t* pos, const compass_kv* kv, void* out,
+                         void* workspace, size_t ws_bytes, void* stream) {
+  if (!w) return fail(COMPASS_E_INVALID, "weights struct is NULL");
+  return decode_impl(d, w, nullptr, B, x, pos, kv, out, workspace, ws_bytes, stream);
+}
+
+int compass_layer_decode_q4(const compass_layer_desc* d, const compass_layer_weights_q4* w, int32_t B,
+                            const void* x, const int32_t* pos, const compass_kv* kv, void* out,
+                            void* workspace, size_t ws_bytes, void* stream) {
+  if (!w) return fail(COMPASS_E_INVALID, "weights struct is NULL");
+  return decode_impl(d, nullptr, w, B, x, pos, kv, out, workspace, ws_bytes, stream);
 }
 
 size_t compass_logits_workspace_size(int32_t R, int32_t D, int32_t dtype) {

@@ -41,6 +41,20 @@ struct BMap {
   int nq64, nk64;
 };
 
+// 4-bit affine B operand (rows of codes packed two per byte, column 2j in the low nibble;
+// bf16 scale and bias per 64 columns). kind 1: the projection's virtual N layout of BMap
+// kind 1 (matrices 0..4 = q, k, v, gate, up; all cols0 columns wide). kind 2: concatenation
+// along K (matrix 0, cols0 columns, for k < ksplit; matrix 1, cols1 columns, after).
+struct Q4Map {
+  int kind;
+  const void* q[5];
+  const void* s[5];
+  const void* b[5];
+  int cols0, cols1;
+  int ksplit;
+  int nq64, nk64;
+};
+
 // Destinations of the projection epilogue (q/k/v with MRoPE, KV write, SwiGLU).
 struct ProjEpi {
   int decode;           // 0: row m is (b = m / L, l = m % L); 1: row m is b = m, l = lens[b]
@@ -115,6 +129,11 @@ hipError_t launch_gemm_bf16_raw_wide(const void* A, int lda, int M, int K, const
 // K splits for the residual output GEMM: 1 when 128 x 256 tiles fill the CUs, else enough
 // 256 x 256 split-K workgroups to (the partials then go through launch_splitk_resid).
 int gemm_bf16_resid_splits(int M, int N, int K);
+
+// Same contract as launch_gemm_bf16_raw with the B operand in 4-bit affine form (64 x 64
+// tiles; K, N, ksplit and the matrices' widths multiples of 64).
+hipError_t launch_gemm_q4_raw(const void* A, int lda, int M, int K, const Q4Map& bm, int N, int splits, float* raw,
+                              hipStream_t s);
 
 // fp32 GEMM (VALU), same contract as launch_gemm_bf16_raw with fp32 operands; every
 // stored sum is multiplied by `scale` (1 for raw partials).

@@ -183,6 +183,33 @@ int compass_layer_decode(const compass_layer_desc *d, const compass_layer_weight
                          int32_t B, const void *x, const int32_t *pos, const compass_kv *kv,
                          void *out, void *workspace, size_t ws_bytes, void *stream);
 
+/* 4-bit affine weights: the quantization block of the 4-bit checkpoint in the mlxcel
+ * Compass issue's config section (group size 64, 4 bits, affine mode). For a matrix of
+ * [rows, cols] (cols a multiple of 64):
+ *   W[r][c] = scale[r][c / 64] * code[r][c] + bias[r][c / 64],  code in 0..15.
+ * The caller owns all buffers (device memory). */
+typedef struct {
+  const void *q;       /* uint8 [rows, cols / 2]: byte j of a row holds column 2j in its low
+                          nibble and column 2j + 1 in its high nibble; 16-byte aligned */
+  const void *scales;  /* bf16 [rows, cols / 64] */
+  const void *biases;  /* bf16 [rows, cols / 64] */
+} compass_q4_matrix;
+
+typedef struct {
+  const void *ln_w;    /* bf16 [D] */
+  compass_q4_matrix wq, wk, wv, wo, w_gate, w_up, w_down;  /* shapes of compass_layer_weights */
+} compass_layer_weights_q4;
+
+/* One decode step of one layer with 4-bit affine weights: compass_layer_decode's
+ * arguments, workspace (compass_workspace_size(d, B, 1, kv->capacity, 1)), outputs and
+ * errors, with every weight matrix read in the 4-bit form above. The result is the layer of
+ * the dequantized weights; each dequantized weight is rounded once to bf16 before the
+ * bf16 MFMA products (fp32 accumulation). Requires d->dtype == COMPASS_BF16 (else
+ * COMPASS_E_UNSUPPORTED) and n_q_heads * head_dim a multiple of 64. */
+int compass_layer_decode_q4(const compass_layer_desc *d, const compass_layer_weights_q4 *w,
+                            int32_t B, const void *x, const int32_t *pos, const compass_kv *kv,
+                            void *out, void *workspace, size_t ws_bytes, void *stream);
+
 /* Tied-embedding head ("Text decoder forward": h = LayerNorm(h); logits =
  * embed_tokens.as_linear(h) * logit_scale), with the scale applied as the last fp32
  * operation on each logit (the in-place fp32 footer of the C-Kernel-Engine page,

@@ -151,6 +151,31 @@ def make_layer_weights(shape: LayerShape, workload: int, layer: int) -> Dict[str
     return out
 
 
+Q4_STREAM = 100  # tensor-id offset of the scale (+100) and bias (+200) streams of 4-bit weights
+
+
+def make_layer_weights_q4(shape: LayerShape, workload: int, layer: int) -> Dict[str, object]:
+    """4-bit affine weights in their stored form: ln_w as make_layer_weights, and per matrix
+    [out, in] a tuple (codes uint8 [out, in / 2] of uniform random bytes, scales [out, in / 64],
+    biases [out, in / 64]), scales |N(0.0067, 0.0012)| and biases -7.5 * scale + N(0, 0.002),
+    both bf16-exact, so that the weights they stand for spread like the dense N(0, 0.02) ones."""
+    D, Hq, Hkv, hd, I = shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.intermediate
+    specs = [("wq", TensorId.WQ, (Hq * hd, D)), ("wk", TensorId.WK, (Hkv * hd, D)),
+             ("wv", TensorId.WV, (Hkv * hd, D)), ("wo", TensorId.WO, (D, Hq * hd)), ("w_gate", TensorId.WG, (I, D)),
+             ("w_up", TensorId.WU, (I, D)), ("w_down", TensorId.WD, (D, I))]
+    out = {"ln_w": bf16_round(normal(stream_seed(workload, layer, TensorId.LN_W), D, std=0.02, mean=1.0))}
+    for name, tid, (rows, cols) in specs:
+        assert cols % 64 == 0
+        codes = _uniform_ints(stream_seed(workload, layer, tid), rows * cols // 2, 0, 256).astype(np.uint8)
+        ng = rows * (cols // 64)
+        scale = bf16_round(np.abs(normal(stream_seed(workload, layer, tid + Q4_STREAM), ng, std=0.0012,
+                                         mean=0.0067)))
+        bias = bf16_round(-7.5 * scale + normal(stream_seed(workload, layer, tid + 2 * Q4_STREAM), ng, std=0.002))
+        out[name] = (codes.reshape(rows, cols // 2), scale.reshape(rows, cols // 64),
+                     bias.reshape(rows, cols // 64))
+    return out
+
+
 def make_layer_input(shape: LayerShape, workload: int, rows: int, tensor_id: int = TensorId.X,
                      layer: int = 0, std: float = 1.0) -> np.ndarray:
     """[rows, D] N(0, std^2) hidden states (bf16-exact for bf16 shapes)."""

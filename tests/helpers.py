@@ -84,6 +84,27 @@ def run_decode(shape: LayerShape, wdev: dict, x: torch.Tensor, pos, kc, vc, lens
     return out
 
 
+def q4_to_dev(wq4: dict) -> dict:
+    """4-bit weights (codes uint8, bf16-exact scales / biases) as device tensors."""
+    out = {"ln_w": to_dev(wq4["ln_w"], torch.bfloat16)}
+    for k, v in wq4.items():
+        if k != "ln_w":
+            q, sc, bi = v
+            out[k] = (torch.from_numpy(np.ascontiguousarray(q)).to(DEV), to_dev(sc, torch.bfloat16),
+                      to_dev(bi, torch.bfloat16))
+    return out
+
+
+def run_decode_q4(shape: LayerShape, wq4dev: dict, x: torch.Tensor, pos, kc, vc, lens, out=None, stream=None):
+    b = B()
+    d = desc(shape)
+    Bn = x.shape[0]
+    ws = workspace(b.compass_workspace_size(d, Bn, 1, kc.shape[2], 1))
+    out = torch.empty_like(x) if out is None else out
+    b.compass_layer_decode_q4(d, b.make_weights_q4(wq4dev), x, pos, b.make_kv(kc, vc, lens), out, ws, stream)
+    return out
+
+
 def run_logits(h: torch.Tensor, norm_w, eps: float, embed, scale: float, dtype: int, logits=None):
     b = B()
     R, D = h.shape

@@ -220,3 +220,31 @@ def test_front_end_argument_errors(b):
     assert am(dt=3) == b.COMPASS_E_UNSUPPORTED
     assert "ldh" in (am(ldh=1000) and b.compass_last_error())
     assert am(R=70000, n=1 << 40) == b.COMPASS_E_UNSUPPORTED  # R above the grid limit
+
+
+def test_q4_decode_argument_errors(b):
+    """compass_layer_decode_q4: bf16 only, every matrix pointer set, codes 16-byte aligned."""
+    def wq4(p=0x10000, bad=None, misalign=None):
+        w = b.compass_layer_weights_q4()
+        w.ln_w = p
+        for i, (name, _) in enumerate(b.compass_layer_weights_q4._fields_[1:]):
+            base = p + 0x100000 * (i + 1)
+            m = b.compass_q4_matrix(base, base + 0x40000, base + 0x80000)
+            if name == bad:
+                m.scales = None
+            if name == misalign:
+                m.q = base + 8
+            setattr(w, name, m)
+        return w
+    kv = b.compass_kv()
+    kv.k, kv.v, kv.capacity, kv.lens = 0x5000000, 0x6000000, 64, 0x7000000
+    x, pos, out, ws = FakePtr(0x100000, shape=(4, 2048)), FakePtr(0x200000), FakePtr(0x300000), FakePtr(0x400000)
+    for d, w, code in [(compass_shape(b, dtype=b.COMPASS_F32), wq4(), b.COMPASS_E_UNSUPPORTED),
+                       (compass_shape(b), wq4(bad="w_up"), b.COMPASS_E_INVALID),
+                       (compass_shape(b), wq4(misalign="wo"), b.COMPASS_E_ALIGN)]:
+        with pytest.raises(b.CompassError) as e:
+            b.compass_layer_decode_q4(d, w, x, pos, kv, out, ws, stream=0)
+        assert e.value.code == code
+    with pytest.raises(b.CompassError) as e:  # workspace too small
+        b.compass_layer_decode_q4(compass_shape(b), wq4(), x, pos, kv, out, FakePtr(0x400000, n=64), stream=0)
+    assert e.value.code == b.COMPASS_E_WORKSPACE

@@ -1,0 +1,109 @@
+"""GPU parity of the decode step with 4-bit affine weights (compass_layer_decode_q4)
+against oracle.layer_decode_q4 (the fp64 decode of the dequantized weights).
+
+Gates as for the bf16 decode: max relative error 2e-2 on the output and on the branch sum
+out - x (after allowing for the bf16 rounding of out), and on the new K / V rows; every
+other cache row untouched. The kernel rounds each dequantized weight once to bf16 (a
+relative 2^-9 per weight, like bf16 weight storage), which the gate covers.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import compass_oracle as O
+from synth import stream_seed
+from synth import workloads as W
+from synth.workloads import WORKLOADS
+import synth.rng_torch as RT
+from tests import helpers as H
+from tests.test_gpu_small import check_layer_out
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # kind, hd, Hq, Hkv, D, I, window, B
+    ("sliding", 128, 4, 1, 256, 512, 48, 8),
+    ("full", 128, 4, 1, 256, 512, 0, 8),
+    ("sliding", 64, 8, 2, 512, 1024, 100, 70),   # two row tiles, ragged
+    ("full", 64, 4, 4, 256, 256, 0, 3),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-hd{c[1]}-{c[2]}x{c[3]}-D{c[4]}-B{c[7]}" for c in CASES])
+def test_q4_decode_parity(case):
+    kind, hd, Hq, Hkv, D, I, win, Bn = case
+    sh = H.small_shape("bf16", kind, hd, Hq, Hkv, D, I, win)
+    wq4 = W.make_layer_weights_q4(sh, 50, hd + Hq)
+    r = np.random.default_rng(Bn)
+    cap = 1003
+    lens = r.integers(0, cap, Bn).astype(np.int32)
+    lens[0] = 0
+    lens[-1] = cap - 1
+    x = H.rand_np(5, (Bn, D))
+    kc = H.rand_np(6, (Bn, Hkv, cap, hd))
+    vc = H.rand_np(7, (Bn, Hkv, cap, hd))
+    delta = r.integers(-500, 20, Bn)
+    pos = O.decode_positions(lens, delta)
+    ref, knew, vnew = O.layer_decode_q4(sh, wq4, x, pos, kc, vc, lens)
+    kd, vd = H.to_dev(kc, torch.bfloat16), H.to_dev(vc, torch.bfloat16)
+    out = H.run_decode_q4(sh, H.q4_to_dev(wq4), H.to_dev(x, torch.bfloat16), H.ints_to_dev(pos), kd, vd,
+                          H.ints_to_dev(lens))
+    torch.cuda.synchronize()
+    check_layer_out(sh, out, x, ref, "q4 decode")
+    kg, vg = H.np64(kd), H.np64(vd)
+    for i, n in enumerate(lens):
+        assert H.rel_err(kg[i, :, n], knew[i]) <= 2e-2
+        assert H.rel_err(vg[i, :, n], vnew[i]) <= 2e-2
+    mask = np.ones((Bn, cap), bool)
+    mask[np.arange(Bn), lens] = False
+    assert np.array_equal(kg.transpose(0, 2, 1, 3)[mask], kc.transpose(0, 2, 1, 3)[mask])
+
+
+def test_q4_decode_skips_rows_and_aliases():
+    """A row whose lens is at capacity is skipped (output and cache untouched); out may alias x."""
+    sh = H.small_shape("bf16", "sliding", 128, 4, 1, 256, 512, 40)
+    wq4 = W.make_layer_weights_q4(sh, 51, 0)
+    lens = np.array([5, 64, 63], np.int32)
+    Bn, cap = 3, 64
+    x = H.rand_np(8, (Bn, sh.hidden))
+    kc = H.rand_np(9, (Bn, 1, cap, 128))
+    vc = H.rand_np(10, (Bn, 1, cap, 128))
+    pos = O.decode_positions(lens, np.zeros(Bn, np.int64))
+    xd = H.to_dev(x, torch.bfloat16)
+    kd, vd = H.to_dev(kc, torch.bfloat16), H.to_dev(vc, torch.bfloat16)
+    H.run_decode_q4(sh, H.q4_to_dev(wq4), xd, H.ints_to_dev(pos), kd, vd, H.ints_to_dev(lens), out=xd)
+    torch.cuda.synchronize()
+    got = H.np64(xd)
+    assert np.array_equal(got[1], x[1])
+    assert np.array_equal(H.np64(kd[1]), kc[1])
+    ref, _, _ = O.layer_decode_q4(sh, wq4, x, pos, kc, vc, lens, rows=[0, 2])
+    assert H.rel_err(got[[0, 2]], ref) <= 2e-2
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("layer", [0, 3])
+def test_q4_decode_full_size(layer):
+    """The batched-decode workload's widths (hidden 2048, 16/4 heads, hd 128, I 8192), B = 64 over
+    a cache of 8192 tokens (window 4096 on the sliding layer), sampled rows against the oracle."""
+    cfg = WORKLOADS[3]
+    sh = dataclasses.replace(cfg["shape"], kind=W.layer_kind(layer))
+    Bn, n = cfg["B"], cfg["cache_len"]
+    cap = n + 8
+    Hkv, hd = sh.n_kv_heads, sh.head_dim
+    wq4 = W.make_layer_weights_q4(sh, 3, layer)
+    kc = RT.normal(stream_seed(3, layer, W.TensorId.K_CACHE), Bn * Hkv * cap * hd).to(torch.bfloat16).view(Bn, Hkv, cap, hd)
+    vc = RT.normal(stream_seed(3, layer, W.TensorId.V_CACHE), Bn * Hkv * cap * hd).to(torch.bfloat16).view(Bn, Hkv, cap, hd)
+    rows = [0, 31, 63]
+    kh = H.np64(kc[rows])
+    vh = H.np64(vc[rows])
+    x = H.rand_np(11, (Bn, sh.hidden))
+    lens = np.full(Bn, n, np.int32)
+    pos = O.decode_positions(lens, np.zeros(Bn, np.int64))
+    out = H.run_decode_q4(sh, H.q4_to_dev(wq4), H.to_dev(x, torch.bfloat16), H.ints_to_dev(pos), kc, vc,
+                          H.ints_to_dev(lens))
+    torch.cuda.synchronize()
+    ref, knew, _ = O.layer_decode_q4(sh, wq4, x[rows], pos[:, rows], kh, vh, lens[rows])
+    check_layer_out(sh, out[rows], x[rows], ref, "q4 decode full size")
+    assert H.rel_err(H.np64(kc[rows][:, :, n]), knew) <= 2e-2
