@@ -26,6 +26,11 @@ the design notes of the repository):
     keys n - W < j <= n (sliding) or j <= n (full).
   * Chunked prefill: new token i of row b sits at cache index start[b] + i, with
     the same visibility rule as decode.
+  * The corrected rotary layout ("sections", page 1's correction under "Acceptance
+    criteria"): contiguous H, W, T sections, each carrying the frequency indices the
+    interleave gives its axis, in increasing order. PARITY UNPINNED against the real
+    rotary class, whose permutation the page does not print; pinned only to the axis
+    sets the page prints and to the structure of this reading.
   * 4-bit weights (the quantization block of page 1's config section: group size
     64, 4 bits, affine): a weight is scale * code + bias with one (scale, bias)
     per 64 consecutive input columns; byte j of a packed row holds column 2j in
@@ -147,13 +152,39 @@ def inv_freq(theta: float, head_dim: int) -> np.ndarray:
     return float(theta) ** (-2.0 * j / head_dim)
 
 
-def mrope_angles(pos3: np.ndarray, section: Sequence[int], theta: float, head_dim: int) -> np.ndarray:
-    """pos3 [3, N] -> angles [N, hd/2]: freqs[n, j] = pos[axis(j), n] * inv_freq[j]."""
-    half = head_dim // 2
+def mrope_section_layout(section: Sequence[int], half: int) -> Tuple[np.ndarray, np.ndarray]:
+    """The corrected Compass layout (page 1, the correction under "Acceptance criteria": the
+    real rotary class pre-permutes inv_freq and gives the axes contiguous [H, W, T] sections).
+    The permutation is not printed. Reading (parity unpinned against the real class): each
+    axis keeps the frequency indices the interleave gives it, in increasing order, and the
+    sections are laid out H, then W, then T. Returns (axis[f], freq_index[f]) for f < half."""
     ax = mrope_axis_map(section, half)
-    f = inv_freq(theta, head_dim)
+    order = (1, 2, 0)
+    fidx = np.concatenate([np.flatnonzero(ax == a) for a in order])
+    axis = np.concatenate([np.full(int((ax == a).sum()), a, dtype=np.int64) for a in order])
+    return axis, fidx
+
+
+def mrope_angles(pos3: np.ndarray, section: Sequence[int], theta: float, head_dim: int,
+                 layout: str = "interleaved") -> np.ndarray:
+    """pos3 [3, N] -> angles [N, hd/2]: freqs[n, j] = pos[axis(j), n] * inv_freq[j]
+    (layout "interleaved"); with layout "sections", column f carries frequency index
+    freq_index[f] on axis axis[f] of mrope_section_layout."""
+    half = head_dim // 2
     pos3 = np.asarray(pos3, dtype=F64)
+    f = inv_freq(theta, head_dim)
+    if layout == "sections":
+        axis, fidx = mrope_section_layout(section, half)
+        return pos3[axis, :].T * f[fidx][None, :]
+    if layout != "interleaved":
+        raise ValueError(f"unknown rope layout {layout!r}")
+    ax = mrope_axis_map(section, half)
     return pos3[ax, :].T * f[None, :]
+
+
+def _angles(shape, pos3: np.ndarray) -> np.ndarray:
+    return mrope_angles(pos3, shape.mrope_section, shape.rope_theta, shape.head_dim,
+                        getattr(shape, "rope_layout", "interleaved"))
 
 
 def rotate_half(x: np.ndarray) -> np.ndarray:
@@ -239,7 +270,7 @@ def layer_prefill(shape, w: Dict[str, np.ndarray], x: np.ndarray, pos: Optional[
         q, k, v, g, u = projections(a, w)
         qh, kh, vh = _heads(q, Hq, hd), _heads(k, Hkv, hd), _heads(v, Hkv, hd)
         if shape.kind == "sliding":
-            ang = mrope_angles(pos[:, b, :], shape.mrope_section, shape.rope_theta, hd)
+            ang = _angles(shape, pos[:, b, :])
             qh, kh = apply_rope(qh, ang), apply_rope(kh, ang)
         o = attention(qh, kh, vh, shape.kind, shape.window)
         act = silu(g) * u
@@ -278,8 +309,8 @@ def layer_prefill_rows(shape, w: Dict[str, np.ndarray], x: np.ndarray, pos: Opti
     q = a_rows @ np.asarray(w["wq"], dtype=F64).T
     qh = _heads(q, Hq, hd)
     if shape.kind == "sliding":
-        kh = apply_rope(kh, mrope_angles(pos[:, b, lo:hi], shape.mrope_section, shape.rope_theta, hd))
-        qh = apply_rope(qh, mrope_angles(pos[:, b, rows], shape.mrope_section, shape.rope_theta, hd))
+        kh = apply_rope(kh, _angles(shape, pos[:, b, lo:hi]))
+        qh = apply_rope(qh, _angles(shape, pos[:, b, rows]))
     o = attention(qh, kh, vh, shape.kind, shape.window, q_index=rows, k_index=span)
     g = a_rows @ np.asarray(w["w_gate"], dtype=F64).T
     u = a_rows @ np.asarray(w["w_up"], dtype=F64).T
@@ -312,7 +343,7 @@ def layer_decode(shape, w: Dict[str, np.ndarray], x: np.ndarray, pos: np.ndarray
         q, k, v, g, u = projections(a, w)
         qh, kh, vh = _heads(q, Hq, hd), _heads(k, Hkv, hd), _heads(v, Hkv, hd)
         if shape.kind == "sliding":
-            ang = mrope_angles(pos[:, b:b + 1], shape.mrope_section, shape.rope_theta, hd)
+            ang = _angles(shape, pos[:, b:b + 1])
             qh, kh = apply_rope(qh, ang), apply_rope(kh, ang)
         lo = 0 if shape.kind == "full" else max(0, n - shape.window + 1)
         kc = np.asarray(k_cache[b, :, lo:n, :], dtype=F64)
@@ -399,7 +430,7 @@ def layer_prefill_chunk(shape, w: Dict[str, np.ndarray], x: np.ndarray, pos: Opt
         q, k, v, g, u = projections(a, w)
         qh, kh, vh = _heads(q, Hq, hd), _heads(k, Hkv, hd), _heads(v, Hkv, hd)
         if shape.kind == "sliding":
-            ang = mrope_angles(pos[:, b, :], shape.mrope_section, shape.rope_theta, hd)
+            ang = _angles(shape, pos[:, b, :])
             qh, kh = apply_rope(qh, ang), apply_rope(kh, ang)
         kk = np.concatenate([np.asarray(k_cache[b, :, :s0, :], dtype=F64), kh], axis=1)
         vv = np.concatenate([np.asarray(v_cache[b, :, :s0, :], dtype=F64), vh], axis=1)

@@ -53,6 +53,7 @@ class LayerShape:
     dtype: str  # "f32" | "bf16"
     rope_theta: float = 50000.0
     ln_eps: float = 1e-5
+    rope_layout: str = "interleaved"  # "interleaved" | "sections"
 
     def with_kind(self, kind: str) -> "LayerShape":
         return dataclasses.replace(self, kind=kind)

@@ -140,6 +140,20 @@ def _dequantize_q4_no_bias(packed, scales, biases):
     return _orig_dequantize_q4(packed, scales, np.zeros_like(np.asarray(biases, float)))
 
 
+_orig_section_layout = O.mrope_section_layout
+
+
+def _sections_t_first(section, half):
+    axis, fidx = _orig_section_layout(section, half)
+    n_t = int(section[0])
+    return np.roll(axis, n_t), np.roll(fidx, n_t)
+
+
+def _sections_unpermuted(section, half):
+    axis, _ = _orig_section_layout(section, half)
+    return axis, np.arange(half)
+
+
 MUTANTS = {
     "rotate_half sign": ("rotate_half", _rotate_half_wrong_sign),
     "pairwise rope": ("rotate_half", _rotate_half_pairwise),
@@ -161,6 +175,8 @@ MUTANTS = {
     "q4 nibbles high first": ("unpack_q4", _unpack_q4_high_first),
     "q4 groups of 32": ("dequantize_q4", _dequantize_q4_group_32),
     "q4 bias dropped": ("dequantize_q4", _dequantize_q4_no_bias),
+    "sections ordered T, H, W": ("mrope_section_layout", _sections_t_first),
+    "sections without the frequency permutation": ("mrope_section_layout", _sections_unpermuted),
 }
 
 PINS = [
@@ -183,6 +199,10 @@ PINS = [
     P.test_q4_dequantize_brute_force_and_closed_forms,
     P.test_q4_round_trip_within_half_step,
     P.test_q4_decode_is_dense_decode_of_dequantized_weights,
+    P.test_sections_layout_carries_the_page_axis_sets,
+    P.test_sections_rope_is_a_pair_permutation_of_the_interleave,
+    P.test_sections_with_equal_axes_is_1d_rope_on_permuted_frequencies,
+    P.test_sections_layer_equals_interleaved_layer_with_permuted_qk_rows,
 ]
 
 

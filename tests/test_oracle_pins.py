@@ -132,6 +132,71 @@ def test_relative_position_property():
     assert abs(dot(0) - dot(1234)) < 1e-9
 
 
+# ------------------------------------------------------------------------------ corrected layout
+# The "sections" layout is a reading of the correction under "Acceptance criteria" (the real
+# rotary class's permutation is not printed): parity unpinned against that class; these pins
+# tie it to the axis sets the page prints and to the structure of the reading.
+def test_sections_layout_carries_the_page_axis_sets():
+    g = golden("axis_sets_24_20_20.json")
+    axis, fidx = O.mrope_section_layout(g["section"], g["n_freq"])
+    h = list(range(g["h_first"], g["h_last"] + 1, g["h_step"]))
+    w = list(range(g["w_first"], g["w_last"] + 1, g["w_step"]))
+    assert fidx[:len(h)].tolist() == h and set(axis[:len(h)].tolist()) == {1}
+    assert fidx[len(h):len(h) + len(w)].tolist() == w and set(axis[len(h):len(h) + len(w)].tolist()) == {2}
+    t = sorted(set(range(64)) - set(h) - set(w))
+    assert fidx[len(h) + len(w):].tolist() == t and set(axis[len(h) + len(w):].tolist()) == {0}
+    assert all(j in fidx[len(h) + len(w):] for j in g["t_tail"])
+
+
+def test_sections_rope_is_a_pair_permutation_of_the_interleave():
+    """Rotating x in the sections layout equals rotating, in the interleaved layout, the
+    vector whose pair fidx[f] holds x's pair f, read back at those pairs."""
+    r = np.random.default_rng(90)
+    for hd, section in ((128, (24, 20, 20)), (64, (12, 10, 10)), (64, (14, 8, 10))):
+        half = hd // 2
+        _, fidx = O.mrope_section_layout(section, half)
+        x = r.standard_normal((9, hd))
+        pos = r.integers(0, 5000, (3, 9))
+        ys = O.apply_rope(x, O.mrope_angles(pos, section, 50000.0, hd, "sections"))
+        xi = np.empty_like(x)
+        xi[:, fidx], xi[:, fidx + half] = x[:, :half], x[:, half:]
+        yi = O.apply_rope(xi, O.mrope_angles(pos, section, 50000.0, hd))
+        np.testing.assert_allclose(ys, np.concatenate([yi[:, fidx], yi[:, fidx + half]], axis=1), atol=1e-12)
+
+
+def test_sections_with_equal_axes_is_1d_rope_on_permuted_frequencies():
+    r = np.random.default_rng(91)
+    hd, section = 128, (24, 20, 20)
+    _, fidx = O.mrope_section_layout(section, hd // 2)
+    x = r.standard_normal((11, hd))
+    p = r.integers(0, 9000, 11)
+    got = O.apply_rope(x, O.mrope_angles(np.stack([p, p, p]), section, 50000.0, hd, "sections"))
+    inv = 50000.0 ** (-2.0 * fidx / hd)   # RoFormer rotation of (x_f, x_{f + 64}) at frequency inv[f]
+    c, s_ = np.cos(p[:, None] * inv), np.sin(p[:, None] * inv)
+    ref = np.concatenate([x[:, :64] * c - x[:, 64:] * s_, x[:, 64:] * c + x[:, :64] * s_], axis=1)
+    np.testing.assert_allclose(got, ref, atol=1e-9)
+
+
+def test_sections_layer_equals_interleaved_layer_with_permuted_qk_rows():
+    """q.k is invariant under a common permutation of head dimensions: the layer in the
+    sections layout equals the interleaved layer whose Wq / Wk rows are permuted to match."""
+    import dataclasses
+    sh_i = tiny_shape("sliding", 4, hd=16, D=64, I=128, section=(4, 2, 2))
+    sh_s = dataclasses.replace(sh_i, rope_layout="sections")
+    half = 8
+    _, fidx = O.mrope_section_layout(sh_i.mrope_section, half)
+    perm = np.concatenate([fidx, fidx + half])   # sections dim d <- interleaved dim perm[d]
+    w_i = rand_weights(sh_i, seed=92, std=0.3)
+    w_s = dict(w_i)
+    for name, nh in (("wq", sh_i.n_q_heads), ("wk", sh_i.n_kv_heads)):
+        m = w_i[name].reshape(nh, 16, -1)
+        w_s[name] = m[:, perm, :].reshape(nh * 16, -1)
+    r = np.random.default_rng(93)
+    x = r.standard_normal((2, 7, 64))
+    pos = mixed_pos(2, 7, seed=94)
+    np.testing.assert_allclose(O.layer_prefill(sh_s, w_s, x, pos), O.layer_prefill(sh_i, w_i, x, pos), atol=1e-12)
+
+
 # ------------------------------------------------------------------------------ LayerNorm
 def test_layer_norm_vs_torch_and_invariants():
     r = np.random.default_rng(5)
