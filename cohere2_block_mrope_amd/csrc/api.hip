@@ -111,6 +111,8 @@ int check_desc(const compass_layer_desc* d) {
     return fail(COMPASS_E_UNSUPPORTED, "(Hq + 2 Hkv) * head_dim must be a multiple of 128");
   if ((long long)(d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim + 2LL * d->intermediate > (1LL << 30))
     return fail(COMPASS_E_UNSUPPORTED, "projection width too large");
+  if (d->rope_layout != COMPASS_ROPE_INTERLEAVED && d->rope_layout != COMPASS_ROPE_SECTIONS)
+    return fail(COMPASS_E_INVALID, "rope_layout %d is neither INTERLEAVED nor SECTIONS", d->rope_layout);
   if (!(d->ln_eps >= 0.f) || !isfinite(d->ln_eps))
     return fail(COMPASS_E_INVALID, "ln_eps must be finite and >= 0");
   if (d->kind == COMPASS_SLIDING) {
@@ -151,6 +153,7 @@ RopeTable rope_table(const compass_layer_desc* d) {
   t.theta = d->rope_theta;
   t.sh3 = 3 * d->mrope_section[1];
   t.sw3 = 3 * d->mrope_section[2];
+  t.layout = d->rope_layout;
   return t;
 }
 

@@ -104,7 +104,8 @@ __device__ __forceinline__ void proj_qkv_epilogue(const GemmParams& P, const f32
   // frequency 32 jj + col4 + t of the first half.
   float invr[PB][4];
   int axis[PB][4];
-  {
+  if (!P.rt.layout) {
+    // Interleaved layout: consecutive pairs have consecutive frequency indices.
     const double th = (double)P.rt.theta;
     const double r1 = pow(th, -2.0 / HD), r32 = pow(th, -64.0 / HD);
     double f0 = pow(th, -2.0 * col4 / HD) * 0.15915494309189535;  // / (2 pi)
@@ -119,6 +120,16 @@ __device__ __forceinline__ void proj_qkv_epilogue(const GemmParams& P, const f32
       }
       f0 *= r32;
     }
+  } else {
+    const double l2t = log2((double)P.rt.theta);
+#pragma unroll
+    for (int jj = 0; jj < PB; ++jj)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int f = 32 * jj + col4 + t;
+        invr[jj][t] = (float)(exp2(-2.0 * rope_freq_index(P.rt, f) / HD * l2t) * 0.15915494309189535);
+        axis[jj][t] = rope_axis(P.rt, f);
+      }
   }
 
 #pragma unroll

@@ -6,20 +6,43 @@
 
 namespace compass {
 
-// MRoPE parameters. Frequency j < head_dim / 2 has inverse frequency
-// theta^(-2j / head_dim) (evaluated in double, rounded once to fp32) and uses axis
-// h when j % 3 == 1 and j < sh3 (= 3 * s_h), axis w when j % 3 == 2 and j < sw3
-// (= 3 * s_w), axis t otherwise.
+// MRoPE parameters. Interleaved layout (layout 0): rotation pair f < head_dim / 2 uses
+// frequency index j = f, inverse frequency theta^(-2j / head_dim) (evaluated in double,
+// rounded once to fp32), and axis h when j % 3 == 1 and j < sh3 (= 3 * s_h), axis w when
+// j % 3 == 2 and j < sw3 (= 3 * s_w), axis t otherwise. Sections layout (layout 1): pairs
+// f < s_h use axis h, the next s_w axis w, the rest axis t, and each section carries, in
+// increasing order, the frequency indices the interleaved layout gives its axis.
 struct RopeTable {
   float theta;
   int sh3, sw3;
+  int layout;
 };
 
 #ifdef __HIPCC__
+__device__ __forceinline__ int rope_freq_index(const RopeTable& rt, int f) {
+  if (!rt.layout) return f;
+  const int sh = rt.sh3 / 3, sw = rt.sw3 / 3;
+  if (f < sh) return 3 * f + 1;
+  if (f < sh + sw) return 3 * (f - sh) + 2;
+  // t section: below 3 min(s_h, s_w) the t indices are the multiples of 3; up to
+  // 3 max(s_h, s_w) also the residue of the shorter axis; beyond that every index.
+  const int k = f - sh - sw, a = min(sh, sw), bm = max(sh, sw);
+  if (k < a) return 3 * k;
+  const int mid = 2 * (bm - a);
+  if (k < a + mid) {
+    const int i = k - a;
+    return 3 * (a + i / 2) + ((i & 1) ? (sh < sw ? 1 : 2) : 0);
+  }
+  return 3 * bm + (k - a - mid);
+}
 __device__ __forceinline__ float rope_inv_freq(const RopeTable& rt, int f, int hd) {
-  return (float)pow((double)rt.theta, -2.0 * (double)f / (double)hd);
+  return (float)pow((double)rt.theta, -2.0 * (double)rope_freq_index(rt, f) / (double)hd);
 }
 __device__ __forceinline__ int rope_axis(const RopeTable& rt, int f) {
+  if (rt.layout) {
+    const int sh = rt.sh3 / 3, sw = rt.sw3 / 3;
+    return f < sh ? 1 : (f < sh + sw ? 2 : 0);
+  }
   const int r = f % 3;
   return (r == 1 && f < rt.sh3) ? 1 : (r == 2 && f < rt.sw3) ? 2 : 0;
 }

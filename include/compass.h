@@ -49,6 +49,7 @@ typedef enum {
 
 typedef enum { COMPASS_F32 = 0, COMPASS_BF16 = 1 } compass_dtype;
 typedef enum { COMPASS_SLIDING = 0, COMPASS_FULL = 1 } compass_kind;
+typedef enum { COMPASS_ROPE_INTERLEAVED = 0, COMPASS_ROPE_SECTIONS = 1 } compass_rope_layout;
 
 /* Status words written by compass_mrope_positions (device, one per call). */
 enum {
@@ -71,7 +72,13 @@ enum {
  *   uses axis h when j % 3 == 1 and j < 3*s_h, axis w when j % 3 == 2 and j < 3*s_w,
  *   axis t otherwise ("Interleaved MRoPE"; [24, 20, 20] on the real model).
  * rope_theta: MRoPE base (50000 on the real model); inv_freq[j] = theta^(-2j/head_dim).
- * ln_eps: LayerNorm epsilon (the value is not printed by the page; callers pass it). */
+ * ln_eps: LayerNorm epsilon (the value is not printed by the page; callers pass it).
+ * rope_layout: COMPASS_ROPE_INTERLEAVED (0), the layout above; or COMPASS_ROPE_SECTIONS
+ *   (1), the correction under the issue's "Acceptance criteria" (contiguous [H, W, T]
+ *   sections over a permuted inv_freq). Its permutation is not printed; this library
+ *   reads it as: rotation pairs f < s_h use axis h, the next s_w axis w, the rest axis t,
+ *   and each section carries, in increasing order, the frequency indices j the
+ *   interleaved layout gives its axis (unverified against the real rotary class). */
 typedef struct {
   int32_t hidden;        /* D */
   int32_t n_q_heads;     /* Hq */
@@ -84,6 +91,7 @@ typedef struct {
   float rope_theta;
   float ln_eps;
   int32_t dtype;         /* compass_dtype */
+  int32_t rope_layout;   /* compass_rope_layout; 0 = interleaved */
 } compass_layer_desc;
 
 /* Weights of one layer, nn.Linear layout [out, in], no biases (section "Weight keys":

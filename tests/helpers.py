@@ -29,7 +29,8 @@ def desc(shape: LayerShape):
     return b.make_desc(shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.intermediate,
                        b.COMPASS_SLIDING if shape.kind == "sliding" else b.COMPASS_FULL,
                        shape.window if shape.kind == "sliding" else 0, shape.mrope_section, shape.rope_theta,
-                       shape.ln_eps, cdtype(shape))
+                       shape.ln_eps, cdtype(shape),
+                       b.COMPASS_ROPE_SECTIONS if shape.rope_layout == "sections" else b.COMPASS_ROPE_INTERLEAVED)
 
 
 def to_dev(a: np.ndarray, dtype) -> torch.Tensor:

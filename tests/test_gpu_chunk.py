@@ -20,6 +20,8 @@ CHUNK_CASES = [
     ("bf16", "sliding", 128, 4, 1, 256, 512, 48, (0, 37, 130), 70),
     ("bf16", "full", 128, 4, 2, 256, 512, 0, (0, 64, 200), 130),
     ("bf16", "sliding", 64, 8, 2, 256, 256, 100, (5, 260), 33),
+    ("bf16", "sliding", 128, 4, 1, 256, 512, 300, (0, 200, 90), 520),   # chunks of >= 512 queries
+    ("bf16", "full", 64, 4, 2, 256, 256, 0, (70, 0), 600),
     ("f32", "sliding", 64, 4, 1, 256, 512, 32, (0, 17, 90), 40),
     ("f32", "full", 128, 2, 1, 256, 256, 0, (3, 50), 25),
 ]

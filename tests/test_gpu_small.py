@@ -129,6 +129,9 @@ PREFILL_CASES = [
     ("bf16", "sliding", 128, 2, 2, 256, 256, 5000, 1, 257),  # window >= L
     ("bf16", "sliding", 128, 4, 2, 256, 256, 300, 1, 700),   # window spans several key tiles
     ("bf16", "full", 128, 2, 1, 256, 256, 0, 1, 600),        # several 256-query blocks, ragged tail
+    ("bf16", "sliding", 64, 4, 2, 256, 256, 200, 2, 530),    # head_dim 64 with 64-query waves
+    ("bf16", "full", 64, 8, 1, 256, 256, 0, 1, 1100),
+    ("bf16", "sliding", 128, 4, 1, 256, 256, 64, 1, 777),    # window shorter than a wave's 64 queries
 ]
 
 
