@@ -293,3 +293,24 @@ def test_logits_parity_and_scale(dt, R, D, V):
     ref = O.logits(h, nw, 1e-5, E, 0.0625)
     assert H.rel_err(H.np64(lg), ref) <= (2e-2 if bf else 1e-4)
     assert torch.equal(lg, l1 * 0.0625)
+
+
+def test_tiny_fp32_workload_against_both_oracles():
+    """The fp32 parity workload exactly (hidden 256, 4/1 heads, hd 64, I 1024, MRoPE [12,10,10],
+    window 32, 128 text tokens with t = h = w = index, N(0, 0.02) weights): the GPU layer against
+    the fp64 numpy oracle and against the plain fp32 C++ reference, 1e-4 each."""
+    from oracle import ref as R
+    cfg = W.WORKLOADS[0]
+    sh, L = cfg["shape"], cfg["L"]
+    w = W.make_layer_weights(sh, 0, 0)
+    x = W.make_layer_input(sh, 0, L).reshape(1, L, sh.hidden)
+    p = np.arange(L)
+    pos = np.stack([p, p, p])[:, None, :]
+    out = H.run_prefill(sh, H.weights_to_dev(sh, w), H.to_dev(x, torch.float32), H.ints_to_dev(pos))
+    torch.cuda.synchronize()
+    got = H.np64(out)
+    ref64 = O.layer_prefill(sh, w, x, pos)
+    ref32, _, _ = R.layer_forward(sh, w, x, pos)
+    assert H.rel_err(got, ref64) <= 1e-4
+    assert H.rel_err(got, ref32) <= 1e-4
+    check_layer_out(sh, out, x, ref64, "fp32 workload")
