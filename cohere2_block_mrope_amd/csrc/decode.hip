@@ -206,11 +206,14 @@ __global__ __launch_bounds__(256) void decode_attn_mfma_kernel(const bf16_t* __r
   constexpr int LPK = HD / 8;          // lanes per K / V row (16-byte chunks per row)
   constexpr int KPS = 64 / LPK;        // rows per wave load instruction
   constexpr int STEPS = 64 / KPS;      // load instructions for the wave's 64 rows
-  // Per-wave K tiles; reused for the per-wave output partials once every wave is done.
-  __shared__ __align__(16) u32x4_t s_kbuf[4 * 64 * LPK];
+  // Per-wave K tiles of 32 keys (the wave's 64 keys are staged in two rounds, which keeps
+  // the workgroup at about 36 KB of LDS: three workgroups per CU stream at once); reused
+  // for the per-wave output partials once every wave is done.
+  __shared__ __align__(16) u32x4_t s_kbuf[4 * 32 * LPK];
   __shared__ float s_p[G][CHUNK];
   __shared__ float s_red[G][4];
-  static_assert(sizeof(float) * 4 * G * HD <= sizeof(u32x4_t) * 4 * 64 * LPK, "s_o must fit in the K tiles");
+  __shared__ __align__(16) u32x4_t s_q[G * LPK];
+  static_assert(sizeof(float) * 4 * G * HD <= sizeof(u32x4_t) * 4 * 32 * LPK, "s_o must fit in the K tiles");
   float (*s_o)[G][HD] = reinterpret_cast<float (*)[G][HD]>(s_kbuf);
 
   const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -247,31 +250,28 @@ __global__ __launch_bounds__(256) void decode_attn_mfma_kernel(const bf16_t* __r
     const int key = min(kbeg + 64 * wave + st * KPS + kin, kend - 1);
     vr[st] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vb + (size_t)key * HD + 8 * sub));
   }
-  // Q^T operand: column `col` is head col (zero beyond G).
-  bf16x8_t qf[KS];
-  {
-    const bool live = col < G;
-    const bf16_t* qp = q + ((size_t)b * Hq + kvh * G + (live ? col : 0)) * HD + 8 * half;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4_t w = *reinterpret_cast<const u32x4_t*>(qp + 16 * ks);
-      if (!live) w = u32x4_t{0u, 0u, 0u, 0u};
-      qf[ks] = __builtin_bit_cast(bf16x8_t, w);
-    }
-  }
-  u32x4_t* kt = s_kbuf + 64 * LPK * wave;
-#pragma unroll
-  for (int st = 0; st < STEPS; ++st) kt[dk_swz<HD>(st * KPS + kin, sub)] = kr[st];
-  __syncthreads();
+  // The G query rows (the Q^T operand, column `col` = head col, zero beyond G) go through
+  // LDS, read per MFMA: holding them in registers for the whole kernel would cost the
+  // occupancy that keeps three workgroups' loads in flight per CU.
+  if (tid < G * LPK) s_q[tid] = *reinterpret_cast<const u32x4_t*>(q + ((size_t)b * Hq + kvh * G) * HD + 8 * tid);
+  u32x4_t* kt = s_kbuf + 32 * LPK * wave;
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2) {
+    // Stage keys 32 kb2 .. + 32 of this wave (load steps STEPS / 2 * kb2 ..). The previous
+    // round's fragment reads were consumed by its MFMAs before this point.
+#pragma unroll
+    for (int st = 0; st < STEPS / 2; ++st)
+      kt[dk_swz<HD>(st * KPS + kin, sub)] = kr[(STEPS / 2) * kb2 + st];
+    __syncthreads();
     f32x16_t sacc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const u32x4_t kf = kt[dk_swz<HD>(32 * kb2 + col, 2 * ks + half)];
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf), qf[ks], sacc, 0, 0, 0);
+      const u32x4_t kf = kt[dk_swz<HD>(col, 2 * ks + half)];
+      const u32x4_t qw = col < G ? s_q[col * LPK + 2 * ks + half] : u32x4_t{0u, 0u, 0u, 0u};
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf),
+                                                     __builtin_bit_cast(bf16x8_t, qw), sacc, 0, 0, 0);
     }
     if (col < G) {
 #pragma unroll
