@@ -303,12 +303,27 @@ Q4Map out_q4map(const compass_layer_desc* d, const compass_layer_weights_q4* w) 
   return b;
 }
 
+std::mutex g_lds_mu;
+std::vector<std::pair<int, const void*>> g_lds_done;  // (device, kernel) pairs already raised
+
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
   return x < y + nb && y < x + na;
 }
 
 }  // namespace
+
+hipError_t compass::ensure_dynamic_lds(const void* kernel, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_lds_mu);
+  for (const auto& d : g_lds_done)
+    if (d.first == dev && d.second == kernel) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) g_lds_done.emplace_back(dev, kernel);
+  return e;
+}
 
 extern "C" {
 

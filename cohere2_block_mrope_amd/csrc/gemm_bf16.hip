@@ -219,13 +219,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams P) {
 template <int BM, int BN, int MODE, int BKIND>
 hipError_t launch(const GemmParams& P, dim3 grid, hipStream_t s) {
   constexpr size_t lds = (size_t)2 * (BM + BN) * BK * sizeof(bf16_t);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<BM, BN, MODE, BKIND>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  const hipError_t e = ensure_dynamic_lds((const void*)gemm_bf16_kernel<BM, BN, MODE, BKIND>, (int)lds);
+  if (e != hipSuccess) return e;
   gemm_bf16_kernel<BM, BN, MODE, BKIND><<<grid, 256, lds, s>>>(P);
   return hipGetLastError();
 }

@@ -117,6 +117,10 @@ __device__ __forceinline__ bool row_live(const RowStart& r, int b) {
 }
 #endif
 
+// Raise `kernel`'s dynamic LDS limit to `bytes` on the current device, once per (device,
+// kernel); thread-safe (defined in api.hip).
+hipError_t ensure_dynamic_lds(const void* kernel, int bytes);
+
 // ---------------------------------------------------------------- launchers
 hipError_t launch_positions(const int32_t* tok, int B, int L, int image_id, const int32_t* grid,
                             const int32_t* img_off, int merge, int32_t* pos, int32_t* delta,

@@ -165,14 +165,9 @@ hipError_t launch_positions(const int32_t* tok, int B, int L, int image_id, cons
                             const int32_t* img_off, int merge, int32_t* pos, int32_t* delta,
                             int32_t* status, hipStream_t s) {
   const size_t lds = sizeof(int) * ((size_t)kRecInts + ((size_t)L + 31) / 32);
-  static bool attr_set = false;
-  if (!attr_set) {
-    const size_t max_lds = sizeof(int) * ((size_t)kRecInts + COMPASS_MAX_TOKENS_PER_ROW / 32);
-    hipError_t e = hipFuncSetAttribute((const void*)positions_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)max_lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  const size_t max_lds = sizeof(int) * ((size_t)kRecInts + COMPASS_MAX_TOKENS_PER_ROW / 32);
+  const hipError_t e = ensure_dynamic_lds((const void*)positions_kernel, (int)max_lds);
+  if (e != hipSuccess) return e;
   positions_kernel<<<B, kThreads, lds, s>>>(tok, L, image_id, grid, img_off, merge, pos, delta, status, B);
   return hipGetLastError();
 }
