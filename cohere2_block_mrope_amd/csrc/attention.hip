@@ -20,6 +20,8 @@
 // most tiles skip the rescale. O / l is unchanged by the choice of m.
 //
 // fp32 kernel: one wave per query, keys in 64-lane chunks with an online softmax.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -85,46 +87,31 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
 
   const bf16_t* kbase = P.k + ((size_t)b * P.Hkv + kvh) * P.cap * HD;
   const bf16_t* vbase = P.v + ((size_t)b * P.Hkv + kvh) * P.cap * HD;
+  // Software pipeline over key tiles: S^T of tile t + 1 is computed while the softmax of
+  // tile t runs (independent MFMA and VALU work in one instruction stream). Tile t sits in
+  // K buffer (t - kt0) & 1 and V buffer (t - kt0) & 1; K runs one tile ahead of V, so during
+  // iteration t the registers hold K(t + 2) and V(t + 1) on their way to LDS.
   u32x4_t rk[LD_PER_T], rv[LD_PER_T];
-  auto gload = [&](int kt) __attribute__((always_inline)) {
+  // Keys past the chunk's last row are clamped to it (valid data; those keys are masked).
+  const int last_key = s0 + L - 1;
+  auto gload = [&](u32x4_t* r, const bf16_t* base, int kt) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < LD_PER_T; ++i) {
       const int c = tid + 256 * i;
-      const int key = min(kt * KB + c / CH, s0 + L - 1);
-      const size_t off = (size_t)key * HD + 8 * (c % CH);
-      rk[i] = *reinterpret_cast<const u32x4_t*>(kbase + off);
-      rv[i] = *reinterpret_cast<const u32x4_t*>(vbase + off);
+      const uint32_t key = (uint32_t)min(kt * KB + c / CH, last_key);
+      r[i] = *reinterpret_cast<const u32x4_t*>(base + (key * HD + 8 * (c % CH)));
     }
   };
-  auto sstore = [&](int buf) __attribute__((always_inline)) {
+  auto sstore = [&](const u32x4_t* r, bf16_t* tile, int stride) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < LD_PER_T; ++i) {
       const int c = tid + 256 * i;
-      const int key = c / CH, ch = c % CH;
-      *reinterpret_cast<u32x4_t*>(&Ks[buf][key * KS + 8 * ch]) = rk[i];
-      *reinterpret_cast<u32x4_t*>(&Vs[buf][key * VS + 8 * ch]) = rv[i];
+      *reinterpret_cast<u32x4_t*>(&tile[(c / CH) * stride + 8 * (c % CH)]) = r[i];
     }
   };
-
-  f32x16_t O[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) O[i][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-
-  gload(kt0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = kt0; kt <= kt1; ++kt) {
-    const int cur = (kt - kt0) & 1;
-    if (kt < kt1) gload(kt + 1);
-    const bf16_t* ks_ = Ks[cur];
-    const bf16_t* vs_ = Vs[cur];
-    const int k0 = kt * KB;
-
-    // S^T for 64 keys x 32 queries: two 32-key blocks.
-    f32x16_t S[2];
+  // S^T for 64 keys x 32 queries (two 32-key blocks) from the K tile in buffer kbuf.
+  auto qk = [&](int kbuf, f32x16_t (&S)[2]) __attribute__((always_inline)) {  // kbuf: constant
+    const bf16_t* ks_ = Ks[kbuf];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -136,6 +123,19 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
         S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], S[kb], 0, 0, 0);
       }
     }
+  };
+
+  f32x16_t O[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) O[i][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // Tile kt, scores in S: mask, row maximum, lazy raise of the reference (rescaling O).
+  // Returns -m_run (0 while a row has seen no visible key).
+  auto softmax_max = [&](int kt, f32x16_t (&S)[2]) __attribute__((always_inline)) -> float {
+    const int k0 = kt * KB;
     // Mask only tiles that are not entirely visible to every query of the workgroup.
     // The maximum is taken on raw scores (the scale is positive) and the scale folded
     // into the exponent's FMA.
@@ -173,44 +173,129 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) O[i][r] *= alpha;
     }
+    l_run *= alpha;
     // Rows with no visible key yet keep m_run = -inf and get p = 0 (their scores are -inf).
-    const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
+    return (m_run == -INFINITY) ? 0.f : -m_run;
+  };
+  // Probabilities of tile kt, with S^T of the next tile (K buffer PAR ^ 1) issued in the
+  // same straight-line block when NEXT, then O^T += V^T P^T from V buffer PAR.
+  auto exp_pv = [&](auto par, f32x16_t (&S)[2], float neg_m, auto next, f32x16_t (&Sn)[2])
+      __attribute__((always_inline)) {
+    constexpr int PAR = decltype(par)::value;
+    // The 32 exponentials are spread over NQ chunks, one MFMA of the next tile's S^T each
+    // (K fragments read two chunks ahead); sched_barrier keeps the chunks in order so the
+    // MFMAs run under the VALU work.
+    constexpr bool NEXT = decltype(next)::value;
+    constexpr int NQ = 2 * QK;
+    constexpr int EPC = 32 / NQ;
+    const bf16_t* kn = Ks[PAR ^ 1];
+    auto kfrag = [&](int c) __attribute__((always_inline)) {
+      return *reinterpret_cast<const bf16x8_t*>(kn + (32 * (c / QK) + (lane & 31)) * KS + 16 * (c % QK) + 8 * half);
+    };
     float rs = 0.f;
     bf16x8_t pf[2][2];
+    bf16x8_t kf[3];
+    if constexpr (NEXT) {
+      kf[0] = kfrag(0);
+      kf[1] = kfrag(1);
+    }
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int c = 0; c < NQ; ++c) {
+      if constexpr (NEXT) {
+        if (c + 2 < NQ) kf[(c + 2) % 3] = kfrag(c + 2);
+        const int kb = c / QK, ks = c % QK;
+        if (ks == 0) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(S[kb][8 * st + t], P.scale_log2, neg_m));
-          rs += p;
-          pf[kb][st][t] = (__bf16)p;
+          for (int r = 0; r < 16; ++r) Sn[kb][r] = 0.f;
         }
-    l_run = l_run * alpha + pair32_sum(rs);
+        Sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c % 3], qf[ks], Sn[kb], 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = c * EPC; e < (c + 1) * EPC; ++e) {
+        const int kb = e / 16, r = e % 16;
+        float pe = __builtin_amdgcn_exp2f(fmaf(S[kb][r], P.scale_log2, neg_m));
+        asm volatile("" : "+v"(pe));  // keeps the exponential in its chunk (no sinking to the PV)
+        rs += pe;
+        pf[kb][r / 8][r % 8] = (__bf16)pe;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run += pair32_sum(rs);
 
     // O^T[d, q] += sum_key V[key, d] P[q, key]. The V^T operand comes from two
     // transpose reads: lane m of each 16-lane group addresses row key0 + m / 4,
     // columns d0 + 4 (m % 4) .. + 4, and receives V[key0 + j][d0 + lane % 16], j < 4.
+    // MFMA c takes 16-key step c / DB and d block c % DB (consecutive MFMAs feed
+    // different accumulators); its V^T fragment is read three MFMAs ahead.
+    const bf16_t* vs_ = Vs[PAR];
     const int grp = lane >> 4, m16 = lane & 15;
+    constexpr int NP = 4 * DB;
+    auto vfrag = [&](int c) __attribute__((always_inline)) {
+      const int kst = c / DB, db = c % DB;
+      const int key0 = 16 * kst + 4 * half;
+      const bf16_t* v0 = vs_ + (key0 + (m16 >> 2)) * VS + 32 * db + 16 * (grp & 1) + 4 * (m16 & 3);
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4_t))v0);
+      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4_t))(v0 + 8 * VS));
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8_t vf[4];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int d0 = 32 * db + 16 * (grp & 1);
+    for (int c = 0; c < 3; ++c) vf[c] = vfrag(c);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const int key0 = 32 * kb + 16 * st + 4 * half;
-          const bf16_t* a0 = vs_ + (key0 + (m16 >> 2)) * VS + d0 + 4 * (m16 & 3);
-          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4_t))a0);
-          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4_t))(a0 + 8 * VS));
-          const bf16x8_t vf = __builtin_bit_cast(
-              bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][st], O[db], 0, 0, 0);
-        }
+    for (int c = 0; c < NP; ++c) {
+      if (c + 3 < NP) vf[(c + 3) % 4] = vfrag(c + 3);
+      const int kst = c / DB, db = c % DB;
+      O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[c % 4], pf[kst / 2][kst % 2], O[db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt < kt1) sstore(cur ^ 1);
+  };
+
+  // Prologue: K(kt0), V(kt0), K(kt0 + 1) in LDS, S of tile kt0, then K(kt0 + 2) and
+  // V(kt0 + 1) into registers.
+  gload(rk, kbase, kt0);
+  gload(rv, vbase, kt0);
+  sstore(rk, Ks[0], KS);
+  sstore(rv, Vs[0], VS);
+  if (kt0 < kt1) {
+    gload(rk, kbase, kt0 + 1);
+    sstore(rk, Ks[1], KS);
+  }
+  __syncthreads();
+  f32x16_t Sa[2], Sb[2];
+  qk(0, Sa);
+  if (kt0 + 2 <= kt1) gload(rk, kbase, kt0 + 2);
+  if (kt0 + 1 <= kt1) gload(rv, vbase, kt0 + 1);
+  // Iteration t (PAR = (t - kt0) & 1, a constant of the unrolled loop, so every LDS address
+  // is a base plus an immediate): S of tile t + 1 from K buffer PAR ^ 1, softmax and PV of
+  // tile t from V buffer PAR, then K(t + 2) into K buffer PAR (K(t) was last read in
+  // iteration t - 1) and V(t + 1) into V buffer PAR ^ 1 (V(t - 1) was last read in
+  // iteration t - 1), one barrier.
+  auto iter = [&](int t, auto par, f32x16_t (&Sc)[2], f32x16_t (&Sn)[2], auto next)
+      __attribute__((always_inline)) {
+    constexpr int PAR = decltype(par)::value;
+    const float neg_m = softmax_max(t, Sc);
+    exp_pv(par, Sc, neg_m, next, Sn);
+    if (t + 2 <= kt1) sstore(rk, Ks[PAR], KS);
+    if (t + 1 <= kt1) sstore(rv, Vs[PAR ^ 1], VS);
+    if (t + 3 <= kt1) gload(rk, kbase, t + 3);
+    if (t + 2 <= kt1) gload(rv, vbase, t + 2);
     __syncthreads();
+  };
+  using more = std::true_type;
+  using last = std::false_type;
+  using even = std::integral_constant<int, 0>;
+  using odd = std::integral_constant<int, 1>;
+  int t = kt0;
+  for (; t + 2 <= kt1; t += 2) {
+    iter(t, even{}, Sa, Sb, more{});
+    iter(t + 1, odd{}, Sb, Sa, more{});
+  }
+  if (t < kt1) {
+    iter(t, even{}, Sa, Sb, more{});
+    iter(t + 1, odd{}, Sb, Sa, last{});
+  } else {
+    iter(t, even{}, Sa, Sb, last{});
   }
 
   if (qw >= L) return;
