@@ -43,6 +43,8 @@ struct AttnParams {
 
 constexpr int QB = 128, KB = 64;
 constexpr float kLazyMax = 8.0f;  // log2 headroom before the reference max is raised
+// Fourth dword of a raw (unstrided) buffer resource: 32-bit data format, range-checked.
+constexpr int kBufferDword3 = 0x00020000;
 
 template <int HD>
 __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
@@ -93,13 +95,30 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
   // iteration t the registers hold K(t + 2) and V(t + 1) on their way to LDS.
   u32x4_t rk[LD_PER_T], rv[LD_PER_T];
   // Keys past the chunk's last row are clamped to it (valid data; those keys are masked).
+  // K and V are read with buffer loads: the tile's start is a uniform byte offset in an
+  // SGPR, so tiles that lie wholly before that row (all but the last) need no per-tile
+  // address arithmetic, only this thread's fixed offsets.
   const int last_key = s0 + L - 1;
-  auto gload = [&](u32x4_t* r, const bf16_t* base, int kt) __attribute__((always_inline)) {
+  const int slice_bytes = P.cap * HD * 2;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, slice_bytes, kBufferDword3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, slice_bytes, kBufferDword3);
+  int toff[LD_PER_T];
 #pragma unroll
-    for (int i = 0; i < LD_PER_T; ++i) {
-      const int c = tid + 256 * i;
-      const uint32_t key = (uint32_t)min(kt * KB + c / CH, last_key);
-      r[i] = *reinterpret_cast<const u32x4_t*>(base + (key * HD + 8 * (c % CH)));
+  for (int i = 0; i < LD_PER_T; ++i) {
+    const int c = tid + 256 * i;
+    toff[i] = ((c / CH) * HD + 8 * (c % CH)) * 2;
+  }
+  auto gload = [&](u32x4_t* r, __amdgpu_buffer_rsrc_t rs, int kt) __attribute__((always_inline)) {
+    if (kt * KB + KB - 1 <= last_key) {
+#pragma unroll
+      for (int i = 0; i < LD_PER_T; ++i) r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, toff[i], kt * KB * HD * 2, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < LD_PER_T; ++i) {
+        const int c = tid + 256 * i;
+        const int key = min(kt * KB + c / CH, last_key);
+        r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (key * HD + 8 * (c % CH)) * 2, 0, 0);
+      }
     }
   };
   auto sstore = [&](const u32x4_t* r, bf16_t* tile, int stride) __attribute__((always_inline)) {
@@ -253,19 +272,19 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
 
   // Prologue: K(kt0), V(kt0), K(kt0 + 1) in LDS, S of tile kt0, then K(kt0 + 2) and
   // V(kt0 + 1) into registers.
-  gload(rk, kbase, kt0);
-  gload(rv, vbase, kt0);
+  gload(rk, krs, kt0);
+  gload(rv, vrs, kt0);
   sstore(rk, Ks[0], KS);
   sstore(rv, Vs[0], VS);
   if (kt0 < kt1) {
-    gload(rk, kbase, kt0 + 1);
+    gload(rk, krs, kt0 + 1);
     sstore(rk, Ks[1], KS);
   }
   __syncthreads();
   f32x16_t Sa[2], Sb[2];
   qk(0, Sa);
-  if (kt0 + 2 <= kt1) gload(rk, kbase, kt0 + 2);
-  if (kt0 + 1 <= kt1) gload(rv, vbase, kt0 + 1);
+  if (kt0 + 2 <= kt1) gload(rk, krs, kt0 + 2);
+  if (kt0 + 1 <= kt1) gload(rv, vrs, kt0 + 1);
   // Iteration t (PAR = (t - kt0) & 1, a constant of the unrolled loop, so every LDS address
   // is a base plus an immediate): S of tile t + 1 from K buffer PAR ^ 1, softmax and PV of
   // tile t from V buffer PAR, then K(t + 2) into K buffer PAR (K(t) was last read in
@@ -278,8 +297,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
     exp_pv(par, Sc, neg_m, next, Sn);
     if (t + 2 <= kt1) sstore(rk, Ks[PAR], KS);
     if (t + 1 <= kt1) sstore(rv, Vs[PAR ^ 1], VS);
-    if (t + 3 <= kt1) gload(rk, kbase, t + 3);
-    if (t + 2 <= kt1) gload(rv, vbase, t + 2);
+    if (t + 3 <= kt1) gload(rk, krs, t + 3);
+    if (t + 2 <= kt1) gload(rv, vrs, t + 2);
     __syncthreads();
   };
   using more = std::true_type;
