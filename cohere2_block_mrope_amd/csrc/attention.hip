@@ -211,8 +211,12 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
     auto kfrag = [&](int c) __attribute__((always_inline)) {
       return *reinterpret_cast<const bf16x8_t*>(kn + (32 * (c / QK) + (lane & 31)) * KS + 16 * (c % QK) + 8 * half);
     };
+    // Row sum of the bf16-rounded probabilities (the values the PV MFMA multiplies), two
+    // per dot2 against (1, 1).
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
     float rs = 0.f;
-    bf16x8_t pf[2][2];
+    uint32_t pw[2][2][4];
     bf16x8_t kf[3];
     if constexpr (NEXT) {
       kf[0] = kfrag(0);
@@ -230,16 +234,26 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
         Sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c % 3], qf[ks], Sn[kb], 0, 0, 0);
       }
 #pragma unroll
-      for (int e = c * EPC; e < (c + 1) * EPC; ++e) {
+      for (int e = c * EPC; e < (c + 1) * EPC; e += 2) {
         const int kb = e / 16, r = e % 16;
-        float pe = __builtin_amdgcn_exp2f(fmaf(S[kb][r], P.scale_log2, neg_m));
-        asm volatile("" : "+v"(pe));  // keeps the exponential in its chunk (no sinking to the PV)
-        rs += pe;
-        pf[kb][r / 8][r % 8] = (__bf16)pe;
+        float p0 = __builtin_amdgcn_exp2f(fmaf(S[kb][r], P.scale_log2, neg_m));
+        float p1 = __builtin_amdgcn_exp2f(fmaf(S[kb][r + 1], P.scale_log2, neg_m));
+        asm volatile("" : "+v"(p0), "+v"(p1));  // keeps the exponentials in their chunk
+        const uint32_t w = pack_bf2(p0, p1);
+        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), ones, rs, false);
+        pw[kb][r / 8][(r % 8) / 2] = w;
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     l_run += pair32_sum(rs);
+    bf16x8_t pf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const u32x4_t q4 = {pw[kb][st][0], pw[kb][st][1], pw[kb][st][2], pw[kb][st][3]};
+        pf[kb][st] = __builtin_bit_cast(bf16x8_t, q4);
+      }
 
     // O^T[d, q] += sum_key V[key, d] P[q, key]. The V^T operand comes from two
     // transpose reads: lane m of each 16-lane group addresses row key0 + m / 4,
