@@ -340,15 +340,18 @@ def cpu_baseline(sh, w, x, tok, grid, off):
     from oracle import compass_oracle as O
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
-    t0 = time.perf_counter()
     from synth.workloads import IMAGE_TOKEN_ID
-    pos, _ = O.mrope_positions(tok, IMAGE_TOKEN_ID, grid, off, 2)
-    O.layer_prefill(sh, w, x, pos)
+    # Whole passes (positions + layer) until at least 10 s have run, at most 8.
+    runs, t0 = 0, time.perf_counter()
+    while runs < 8 and (runs == 0 or time.perf_counter() - t0 < 10.0):
+        pos, _ = O.mrope_positions(tok, IMAGE_TOKEN_ID, grid, off, 2)
+        O.layer_prefill(sh, w, x, pos)
+        runs += 1
     sec = time.perf_counter() - t0
     L = x.shape[1]
-    return {"value": L / sec, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"one full sliding-layer prefill of the headline workload ({L} tokens, positions + layer) in "
-                      f"fp64 numpy on {threads} BLAS threads, {sec:.1f} s"}
+    return {"value": runs * L / sec, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{runs} full sliding-layer prefills of the headline workload ({L} tokens each, positions + "
+                      f"layer) in fp64 numpy on {threads} BLAS threads, {sec:.1f} s"}
 
 
 GEMM_SOURCES = ["gemm_bf16.hip", "gemm_common.h", "common.h", "launch.h"]
