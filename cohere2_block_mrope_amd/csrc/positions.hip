@@ -20,7 +20,8 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kMaxImg = COMPASS_MAX_IMAGES_PER_ROW;
-constexpr int kRecInts = 6 * kMaxImg;  // per-image records in dynamic LDS, then the mask
+constexpr int kRecInts = 9 * kMaxImg;  // per-image records and grids in dynamic LDS, then the mask
+constexpr int kUnroll = 4;             // token loads in flight per lane while building the mask
 
 __global__ __launch_bounds__(kThreads) void positions_kernel(
     const int32_t* __restrict__ tok, int L, int image_id, const int32_t* __restrict__ grid,
@@ -33,6 +34,7 @@ __global__ __launch_bounds__(kThreads) void positions_kernel(
   int* s_after = smem + 3 * kMaxImg;    // text offset (position - index) after the image
   int* s_gh = smem + 4 * kMaxImg;
   int* s_gw = smem + 5 * kMaxImg;
+  int* s_grid = smem + 6 * kMaxImg;     // the row's image grids (t, h, w), prefetched
   uint32_t* s_mask = reinterpret_cast<uint32_t*>(smem + kRecInts);  // bit l: token l is a pad
   __shared__ int s_found;
   __shared__ int s_bad;
@@ -51,13 +53,26 @@ __global__ __launch_bounds__(kThreads) void positions_kernel(
     if (tid == 0) status[b] = COMPASS_POS_TOO_MANY_IMAGES;
     return;
   }
-  // Pad bitmask: wave w covers tokens 64 i .. 64 i + 63 for i = w, w + 16, ...
-  for (int base = 64 * wave; base < L; base += 64 * (kThreads / 64)) {
-    const int idx = base + lane;
-    const uint64_t bal = __ballot(idx < L && row[idx] == image_id);
-    if (lane == 0) {
-      s_mask[base >> 5] = (uint32_t)bal;
-      if ((base >> 5) + 1 < nw) s_mask[(base >> 5) + 1] = (uint32_t)(bal >> 32);
+  // The row's grids go to LDS while the tokens are read.
+  for (int i = tid; i < 3 * nimg; i += kThreads) s_grid[i] = grid[(size_t)k0 * 3 + i];
+  // Pad bitmask: wave w covers tokens 64 i .. 64 i + 63 for i = w, w + 16, ...; kUnroll
+  // chunks of a lane are loaded before any is tested, so their latencies overlap.
+  constexpr int kStride = 64 * (kThreads / 64);
+  for (int base0 = 64 * wave; base0 < L; base0 += kUnroll * kStride) {
+    int v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int idx = base0 + u * kStride + lane;
+      v[u] = idx < L ? row[idx] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int base = base0 + u * kStride;
+      const uint64_t bal = __ballot(base + lane < L && v[u] == image_id);
+      if (lane == 0 && base < L) {
+        s_mask[base >> 5] = (uint32_t)bal;
+        if ((base >> 5) + 1 < nw) s_mask[(base >> 5) + 1] = (uint32_t)(bal >> 32);
+      }
     }
   }
   __syncthreads();
@@ -83,9 +98,9 @@ __global__ __launch_bounds__(kThreads) void positions_kernel(
       if (tid == 0) s_err = COMPASS_POS_UNUSED_IMAGES;
       break;
     }
-    const int t = grid[(size_t)(k0 + k) * 3 + 0];
-    const int h = grid[(size_t)(k0 + k) * 3 + 1];
-    const int w = grid[(size_t)(k0 + k) * 3 + 2];
+    const int t = s_grid[3 * k + 0];
+    const int h = s_grid[3 * k + 1];
+    const int w = s_grid[3 * k + 2];
     if (t < 1 || h < 1 || w < 1 || h % merge || w % merge) {
       if (tid == 0) s_err = COMPASS_POS_BAD_GRID;
       break;
