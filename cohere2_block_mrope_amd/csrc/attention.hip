@@ -14,12 +14,10 @@
 // K/V tiles of 64 keys are double-buffered in LDS (rows padded against bank
 // conflicts); tiles outside the causal/window range are skipped, and only tiles that
 // straddle the diagonal or the window edge are masked.
-// Online softmax in the log2 domain with a lazily moved reference: Q is pre-scaled by
-// log2(e) / sqrt(hd) and one extra MFMA step per 32-key block subtracts the row's
-// reference m, so p = 2^(s - m) is a single exp2 per score. m is only raised (rescaling
-// O and l by 2^(m_old - m_new)) when a tile's maximum exceeds it by more than 8, so
-// probabilities stay below 256 and most tiles skip the rescale. O / l is unchanged by
-// the choice of m.
+// Online softmax in the log2 domain with a lazily moved reference: a row's running
+// maximum m is only raised (rescaling O and l by 2^(m_old - m_new)) when a tile's
+// maximum exceeds it by more than 2^8, so probabilities 2^(s - m) stay below 256 and
+// most tiles skip the rescale. O / l is unchanged by the choice of m.
 //
 // fp32 kernel: one wave per query, keys in 64-lane chunks with an online softmax.
 #include <type_traits>
@@ -77,27 +75,12 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
   const int aw = s0 + qw;   // cache index of this lane's query
   const int half = lane >> 5;
 
-  // Q fragments (B operand of S^T): lane holds query qw, d = 16 ks + 8 half .. + 8, scaled
-  // by log2(e) / sqrt(hd) (rounded to bf16 again), so the MFMA yields scores in log2 units.
+  // Q fragments (B operand of S^T): lane holds query qw, d = 16 ks + 8 half .. + 8.
   bf16x8_t qf[QK];
   {
     const bf16_t* qp = P.q + (((size_t)b * P.Hq + h) * L + min(qw, L - 1)) * HD + 8 * half;
 #pragma unroll
-    for (int ks = 0; ks < QK; ++ks) {
-      const bf16x8_t raw = *reinterpret_cast<const bf16x8_t*>(qp + 16 * ks);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)((float)raw[e] * P.scale_log2);
-    }
-  }
-  // The running reference m of the lane's query enters every score through one extra MFMA
-  // step per 32-key block: A[key][0] = 1 and B[0][query] = -m (k = 0 lives in lanes 0..31,
-  // element 0; every other k is 0) give S' = S - m with no per-score VALU. m is kept
-  // bf16-representable so the operand holds it exactly.
-  bf16x8_t kones, mfrag;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    kones[e] = (__bf16)((e == 0 && half == 0) ? 1.0f : 0.0f);
-    mfrag[e] = (__bf16)0.0f;
+    for (int ks = 0; ks < QK; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * ks);
   }
 
   const int q_hi = s0 + min(q0 + QB - 1, L - 1);
@@ -152,7 +135,6 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) S[kb][r] = 0.f;
-      S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kones, mfrag, S[kb], 0, 0, 0);
 #pragma unroll
       for (int ks = 0; ks < QK; ++ks) {
         const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
@@ -167,17 +149,15 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
   for (int i = 0; i < DB; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) O[i][r] = 0.f;
-  // m_run: the reference (log2 units, bf16-representable); l_run = 0 until the row's first
-  // visible key.
-  float m_run = 0.f, l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
 
-  // Tile kt, scores S' = S - m in S: mask, row maximum, lazy raise of the reference. m is
-  // raised (rescaling O and l by alpha = 2^(m_old - m_new) and shifting the tile's scores)
-  // only when the tile's maximum exceeds it by more than kLazyMax, or on the row's first
-  // visible tile (l = 0, alpha = 0). O / l is unchanged by the choice of m.
-  auto softmax_max = [&](int kt, f32x16_t (&S)[2]) __attribute__((always_inline)) {
+  // Tile kt, scores in S: mask, row maximum, lazy raise of the reference (rescaling O).
+  // Returns -m_run (0 while a row has seen no visible key).
+  auto softmax_max = [&](int kt, f32x16_t (&S)[2]) __attribute__((always_inline)) -> float {
     const int k0 = kt * KB;
     // Mask only tiles that are not entirely visible to every query of the workgroup.
+    // The maximum is taken on raw scores (the scale is positive) and the scale folded
+    // into the exponent's FMA.
     const bool full_vis = (k0 + KB - 1 <= a0) && (!P.sliding || k0 >= a0 + QB - P.window);
     float mx = -INFINITY;
     if (full_vis) {
@@ -199,29 +179,26 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
           mx = fmaxf(mx, sc);
         }
     }
-    mx = pair32_max(mx);
-    const bool first = l_run == 0.f;
-    const bool raise = mx > kLazyMax || (first && mx > -INFINITY);
+    mx = pair32_max(mx) * P.scale_log2;
+    // Raise the reference only when this tile's maximum is more than kLazyMax above it
+    // (always on a row's first visible tile, where m_run = -inf). alpha = 2^(m_old - m_new)
+    // is 1 when the reference stays and 0 on the first raise.
+    const bool raise = mx > m_run + kLazyMax;
+    const float alpha = __builtin_amdgcn_exp2f(raise ? m_run - mx : 0.f);
+    m_run = raise ? mx : m_run;
     if (__builtin_amdgcn_ballot_w64(raise)) {
-      const float m_new = raise ? (float)(__bf16)(m_run + mx) : m_run;
-      const float shift = m_new - m_run;
-      const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(-shift);
 #pragma unroll
       for (int i = 0; i < DB; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) O[i][r] *= alpha;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) S[kb][r] -= shift;
-      l_run *= alpha;
-      m_run = m_new;
-      mfrag[0] = (__bf16)(half == 0 ? -m_run : 0.0f);
     }
+    l_run *= alpha;
+    // Rows with no visible key yet keep m_run = -inf and get p = 0 (their scores are -inf).
+    return (m_run == -INFINITY) ? 0.f : -m_run;
   };
   // Probabilities of tile kt, with S^T of the next tile (K buffer PAR ^ 1) issued in the
   // same straight-line block when NEXT, then O^T += V^T P^T from V buffer PAR.
-  auto exp_pv = [&](auto par, f32x16_t (&S)[2], auto next, f32x16_t (&Sn)[2])
+  auto exp_pv = [&](auto par, f32x16_t (&S)[2], float neg_m, auto next, f32x16_t (&Sn)[2])
       __attribute__((always_inline)) {
     constexpr int PAR = decltype(par)::value;
     // The 32 exponentials are spread over NQ chunks, one MFMA of the next tile's S^T each
@@ -253,15 +230,14 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
         if (ks == 0) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) Sn[kb][r] = 0.f;
-          Sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kones, mfrag, Sn[kb], 0, 0, 0);
         }
         Sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c % 3], qf[ks], Sn[kb], 0, 0, 0);
       }
 #pragma unroll
       for (int e = c * EPC; e < (c + 1) * EPC; e += 2) {
         const int kb = e / 16, r = e % 16;
-        float p0 = __builtin_amdgcn_exp2f(S[kb][r]);
-        float p1 = __builtin_amdgcn_exp2f(S[kb][r + 1]);
+        float p0 = __builtin_amdgcn_exp2f(fmaf(S[kb][r], P.scale_log2, neg_m));
+        float p1 = __builtin_amdgcn_exp2f(fmaf(S[kb][r + 1], P.scale_log2, neg_m));
         asm volatile("" : "+v"(p0), "+v"(p1));  // keeps the exponentials in their chunk
         const uint32_t w = pack_bf2(p0, p1);
         rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), ones, rs, false);
@@ -331,8 +307,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
   auto iter = [&](int t, auto par, f32x16_t (&Sc)[2], f32x16_t (&Sn)[2], auto next)
       __attribute__((always_inline)) {
     constexpr int PAR = decltype(par)::value;
-    softmax_max(t, Sc);
-    exp_pv(par, Sc, next, Sn);
+    const float neg_m = softmax_max(t, Sc);
+    exp_pv(par, Sc, neg_m, next, Sn);
     if (t + 2 <= kt1) sstore(rk, Ks[PAR], KS);
     if (t + 1 <= kt1) sstore(rv, Vs[PAR ^ 1], VS);
     if (t + 3 <= kt1) gload(rk, krs, t + 3);

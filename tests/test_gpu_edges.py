@@ -129,3 +129,43 @@ def test_positions_longest_row():
     with pytest.raises(b.CompassError) as e:
         b.compass_mrope_positions(longer, img, H.ints_to_dev(grid), H.ints_to_dev(np.array([0, 0])), 2, out, d1, d1)
     assert e.value.code == b.COMPASS_E_UNSUPPORTED
+
+
+def test_prefill_large_logits():
+    """Scores spread over ~33 log2 units (q and k weights x5, gate / up x0.1 so attention
+    dominates the branch sum): near one-hot rows and repeated raises of the softmax reference.
+
+    At this spread the storage roundings decide the result by percents: the layer feeds the
+    bf16-rounded LayerNorm output to the projection and stores q / k / v in bf16, and that
+    alone moves the fp64 oracle's output by 2.2e-2 here. So the reference follows the same
+    storage steps: a = bf16(LN(x)), q = bf16(a Wq^T), the kernel's own K / V (read back from
+    the cache), act = bf16(silu(a Wg^T) * (a Wu^T)), then the oracle's attention in fp64 and
+    the bf16-rounded attention output through Wo. What remains is the softmax arithmetic
+    (bf16 P) plus rare one-ulp differences: about 1e-3. A softmax that loses precision fails
+    the 8e-3 gate (re-rounding q * log2(e) / sqrt(hd) to bf16, for one, gives 2.5e-2 here in a
+    CPU emulation). A full-attention (NoPE) layer, so no rotation angle enters q."""
+    sh = H.small_shape("bf16", "full", 128, 4, 1, 256, 512, 0)
+    Bn, L, Hq, hd = 1, 400, 4, 128
+    w, x, pos = layer_case(sh, Bn, L, seed=77)
+    w = dict(w)
+    for name, f in (("wq", 5.0), ("wk", 5.0), ("w_gate", 0.1), ("w_up", 0.1)):
+        w[name] = H.bf16_round(w[name] * f)
+    td = H.tdtype(sh)
+    kc = torch.zeros((Bn, sh.n_kv_heads, L, hd), dtype=td, device="cuda")
+    vc = torch.zeros_like(kc)
+    out = H.run_prefill(sh, H.weights_to_dev(sh, w), H.to_dev(x, td), H.ints_to_dev(pos), kv=(kc, vc))
+    torch.cuda.synchronize()
+    f64 = lambda n: w[n].astype(np.float64)
+    a = H.bf16_round(O.layer_norm(x[0], w["ln_w"], sh.ln_eps))
+    q = H.bf16_round(a @ f64("wq").T).reshape(L, Hq, hd).transpose(1, 0, 2)
+    k, v = H.np64(kc)[0], H.np64(vc)[0]
+    s = np.einsum("hqd,hkd->hqk", q, np.repeat(k, Hq // sh.n_kv_heads, axis=0)) / np.sqrt(hd)
+    spread = np.log2(np.e) * float(np.std(s[:, np.tril(np.ones((L, L), bool))]))
+    assert spread > 25.0, f"score spread {spread:.1f} log2 units: the case is not large-logit"
+    o_flat = H.bf16_round(O.attention(q, k, v, sh.kind, sh.window))   # [L, Hq * hd]
+    act = H.bf16_round(O.silu(a @ f64("w_gate").T) * (a @ f64("w_up").T))
+    d_ref = o_flat @ f64("wo").T + act @ f64("w_down").T
+    ref = x[0].astype(np.float64) + d_ref
+    d_gpu = H.np64(out)[0] - x[0]
+    e_branch = float(np.max(np.abs(d_gpu - d_ref) - 2.0 ** -8 * np.abs(ref)) / np.max(np.abs(d_ref)))
+    assert e_branch <= 8e-3, f"branch-sum rel err {e_branch:.3e} at score spread {spread:.1f}"
