@@ -385,6 +385,11 @@ static int prefill_impl(const compass_layer_desc* d, const compass_layer_weights
     if (!kv->k || !kv->v) return fail(COMPASS_E_INVALID, "kv->k or kv->v is NULL");
     if (!aligned16(kv->k) || !aligned16(kv->v)) return fail(COMPASS_E_ALIGN, "kv not 16-byte aligned");
     if (kv->capacity < L) return fail(COMPASS_E_INVALID, "kv capacity %d < L=%d", kv->capacity, L);
+    // The attention kernels address one (row, kv head) slice of the cache with 32-bit byte
+    // offsets.
+    if ((long long)kv->capacity * m.hd * m.esz > (1LL << 31) - 1)
+      return fail(COMPASS_E_UNSUPPORTED, "kv capacity %d x head_dim %lld: a (row, kv head) cache slice of 2 GiB or more",
+                  kv->capacity, (long long)m.hd);
   }
   if (n_ds < 0) return fail(COMPASS_E_INVALID, "n_ds < 0");
   if (n_ds > 0) {

@@ -114,7 +114,8 @@ typedef struct {
 typedef struct {
   void *k;              /* [B, Hkv, capacity, hd] */
   void *v;              /* [B, Hkv, capacity, hd] */
-  int32_t capacity;
+  int32_t capacity;     /* rows per (row, kv head) slice; prefill requires capacity * hd * element
+                           size < 2^31 bytes (COMPASS_E_UNSUPPORTED otherwise) */
   const int32_t *lens;  /* device [B]: tokens already cached (decode only; prefill ignores it) */
 } compass_kv;
 

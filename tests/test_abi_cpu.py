@@ -126,6 +126,10 @@ def test_argument_errors(b):
     with pytest.raises(b.CompassError) as e:
         call(kv=kv)  # capacity 8 < L = 16
     assert e.value.code == b.COMPASS_E_INVALID
+    kv.capacity = 1 << 23  # 2^23 rows x 128 x 2 bytes = a 2 GiB (row, kv head) slice
+    with pytest.raises(b.CompassError) as e:
+        call(kv=kv)
+    assert e.value.code == b.COMPASS_E_UNSUPPORTED
 
 
 def test_decode_and_logits_argument_errors(b):
