@@ -81,6 +81,14 @@ __device__ __forceinline__ void store_bf16x4(bf16_t* dst, const float (&v)[4]) {
   o.y = pack_bf2(v[2], v[3]);
   *reinterpret_cast<u32x2_t*>(dst) = o;
 }
+// The same with a streaming hint: for outputs no later kernel reads while they could still
+// be in this XCD's L2, so they leave no dirty lines for the write-back at the kernel's end.
+__device__ __forceinline__ void store_bf16x4_nt(bf16_t* dst, const float (&v)[4]) {
+  u32x2_t o;
+  o.x = pack_bf2(v[0], v[1]);
+  o.y = pack_bf2(v[2], v[3]);
+  __builtin_nontemporal_store(o, reinterpret_cast<u32x2_t*>(dst));
+}
 
 // q / k / v part of the fused projection epilogue for head_dim HD. For HD = 128 the
 // wave's 128 columns are one head (first half blocks 0, 1, second half 2, 3); for
@@ -269,7 +277,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& P, f32x16_t (&ac
             v[1] += __uint_as_float(xv.x & 0xffff0000u);
             v[2] += __uint_as_float(xv.y << 16);
             v[3] += __uint_as_float(xv.y & 0xffff0000u);
-            store_bf16x4(P.out + o, v);
+            store_bf16x4_nt(P.out + o, v);
           } else {
             float* d = P.outf + (size_t)m * P.ldof + n;
             if (vec) {
@@ -302,7 +310,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& P, f32x16_t (&ac
 #pragma unroll
             for (int t = 0; t < 4; ++t) v[t] = silu_f(acc[i][j][4 * g + t]) * acc[i][j + 2][4 * g + t];
             quad_transpose(v, lane);
-            if (m < P.M) store_bf16x4(act + (size_t)m * E.ldact + 32 * j, v);
+            if (m < P.M) store_bf16x4_nt(act + (size_t)m * E.ldact + 32 * j, v);
           }
         }
       return;

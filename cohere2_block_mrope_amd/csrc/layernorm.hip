@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const T* __restrict__ x,
         o4[j] = pack_bf2((v[i * V + 2 * j] - mean) * rstd * w0,
                          (v[i * V + 2 * j + 1] - mean) * rstd * w1);
       }
-      *reinterpret_cast<u32x4_t*>(ar + e) = u32x4_t{o4[0], o4[1], o4[2], o4[3]};
+      __builtin_nontemporal_store(u32x4_t{o4[0], o4[1], o4[2], o4[3]}, reinterpret_cast<u32x4_t*>(ar + e));
     } else {
       float4 wr = *reinterpret_cast<const float4*>(w + e);
       float4 o;
