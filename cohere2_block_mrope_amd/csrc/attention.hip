@@ -16,8 +16,11 @@
 // straddle the diagonal or the window edge are masked.
 // Online softmax in the log2 domain with a lazily moved reference: a row's running
 // maximum m is only raised (rescaling O and l by 2^(m_old - m_new)) when a tile's
-// maximum exceeds it by more than 2^8, so probabilities 2^(s - m) stay below 256 and
-// most tiles skip the rescale. O / l is unchanged by the choice of m.
+// maximum exceeds it by more than 8, so probabilities 2^(s - m) stay below 256 and
+// most tiles skip the rescale. O / l is unchanged by the choice of m. Row sums are taken
+// over the bf16-rounded probabilities the PV MFMA multiplies.
+// Each wave runs a software pipeline over key tiles: the next tile's S^T MFMAs are issued
+// among the current tile's exponentials (see the loop below).
 //
 // fp32 kernel: one wave per query, keys in 64-lane chunks with an online softmax.
 #include <type_traits>
