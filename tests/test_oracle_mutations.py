@@ -5,11 +5,27 @@ dropped term, a flipped sign, an off-by-one index, a transposed operand), then
 runs the pins that should catch it. CPU only; the oracle module is restored
 after every case by monkeypatch.
 """
+import inspect
+import textwrap
+
 import numpy as np
 import pytest
 
 from oracle import compass_oracle as O
 import tests.test_oracle_pins as P
+
+
+def _edited(name, *edits):
+    """The oracle function `name` recompiled from its own source with each (old, new) text edit
+    applied once: a one-token mistake planted in the real code, not a rewrite. It runs with a
+    copy of the oracle's globals, so it calls the unmutated helpers."""
+    src = textwrap.dedent(inspect.getsource(getattr(O, name)))
+    for old, new in edits:
+        assert src.count(old) == 1, (name, old)
+        src = src.replace(old, new)
+    g = dict(O.__dict__)
+    exec(compile(src, f"<mutant of {name}>", "exec"), g)
+    return g[name]
 
 
 def _rotate_half_wrong_sign(x):
@@ -177,6 +193,19 @@ MUTANTS = {
     "q4 bias dropped": ("dequantize_q4", _dequantize_q4_no_bias),
     "sections ordered T, H, W": ("mrope_section_layout", _sections_t_first),
     "sections without the frequency permutation": ("mrope_section_layout", _sections_unpermuted),
+    "image advances positions by t only": ("mrope_positions", _edited(
+        "mrope_positions", ("st += max(t, gh, gw)", "st += t"))),
+    "rope_delta without the + 1": ("mrope_positions", _edited(
+        "mrope_positions", ("delta[b] = st - L", "delta[b] = st - 1 - L"))),
+    "image h and w axes swapped": ("mrope_positions", _edited(
+        "mrope_positions", ("pos[1, b, l + r] = st + (r // gw) % gh", "pos[1, b, l + r] = st + r % gw"),
+        ("pos[2, b, l + r] = st + r % gw", "pos[2, b, l + r] = st + (r // gw) % gh"))),
+    "full layers at i % 4 == 0": ("layer_kind", _edited("layer_kind", ("i % 4 == 3", "i % 4 == 0"))),
+    "logit scale dropped": ("logits", _edited("logits", ("* float(logit_scale)", "* 1.0"))),
+    "deepstack rows shifted by one": ("layer_prefill", _edited(
+        "layer_prefill", ("flat[np.asarray(ds_rows)] +=", "flat[np.asarray(ds_rows) + 1] +="))),
+    "deepstack after every layer": ("stack_prefill", _edited(
+        "stack_prefill", ("i < 3 and i < len(ds)", "i < len(ds)"))),
 }
 
 PINS = [
@@ -203,6 +232,13 @@ PINS = [
     P.test_sections_rope_is_a_pair_permutation_of_the_interleave,
     P.test_sections_with_equal_axes_is_1d_rope_on_permuted_frequencies,
     P.test_sections_layer_equals_interleaved_layer_with_permuted_qk_rows,
+    P.test_positions_image_448_page_example,
+    P.test_positions_c1_layout_hand_derived,
+    P.test_positions_video_like_and_multi_image,
+    P.test_layer_pattern_page_example,
+    P.test_deepstack_adds_at_rows_only,
+    P.test_stack_deepstack_first_three_layers_only,
+    P.test_prefill_decode_consistency,
 ]
 
 
