@@ -15,7 +15,7 @@ headline row prefilled as 4 chunks continuing the KV cache.
 GEMM): algorithmic flops per launch / its mean launch time from HIP events recorded
 around every launch while the timed steps are repeated (the throughput itself is timed
 without the events). "traffic" is its HBM bytes per launch from committed rocprofv3
-counter passes (profiles/gemm_proj_c1_traffic.json) while they match the current kernel
+counter passes (profiles/gemm_proj_sliding_prefill_traffic.json) while they match the current kernel
 sources. "cpu_baseline" is the fp64 oracle timed on this host on one full layer of the
 same workload.
 """
@@ -43,7 +43,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-extra", action="store_true", help="headline workload only")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--only", default=None, help="run one workload: c1|c2|c3|c4|c5 (for profiling)")
+    p.add_argument("--only", default=None, help="run one workload: sliding_prefill|full_prefill|decode_stack|stack_logits|chunked_prefill (for profiling)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run plain 512 MiB copies (reference launches for the HBM byte counters)")
     return p.parse_args()
@@ -86,19 +86,19 @@ def timed(fn, steps, warmup, b, torch):
 
 
 # ------------------------------------------------------------------------ workloads
-def setup_c1(H, W, torch):
+def setup_sliding_prefill(H, W, torch):
     from synth.workloads import WORKLOADS
-    cfg = WORKLOADS[1]
+    cfg = WORKLOADS["sliding_prefill"]
     sh = cfg["shape"]
     L = cfg["L"]
-    w = W.make_layer_weights(sh, 1, 0)
-    x = W.make_layer_input(sh, 1, L).reshape(1, L, sh.hidden)
-    tok, grid, off = W.c1_tokens(W.stream_seed(1, 0, W.TensorId.TOKENS))
+    w = W.make_layer_weights(sh, W.Stream.SLIDING_PREFILL, 0)
+    x = W.make_layer_input(sh, W.Stream.SLIDING_PREFILL, L).reshape(1, L, sh.hidden)
+    tok, grid, off = W.image_text_row(W.stream_seed(W.Stream.SLIDING_PREFILL, 0, W.TensorId.TOKENS))
     return sh, w, x, tok, grid, off
 
 
-def run_c1(args, b, H, W, torch):
-    sh, w, x, tok, grid, off = setup_c1(H, W, torch)
+def run_sliding_prefill(args, b, H, W, torch):
+    sh, w, x, tok, grid, off = setup_sliding_prefill(H, W, torch)
     L = x.shape[1]
     wd = H.weights_to_dev(sh, w)
     xd = H.to_dev(x, torch.bfloat16)
@@ -120,7 +120,7 @@ def run_c1(args, b, H, W, torch):
     return sh, w, x, tok, grid, off, sec, stats
 
 
-def c1_flops(sh, L):
+def layer_flops(sh, L):
     D, Hq, Hkv, hd, I = sh.hidden, sh.n_q_heads, sh.n_kv_heads, sh.head_dim, sh.intermediate
     nv = (Hq + 2 * Hkv) * hd + 2 * I
     proj = 2.0 * L * D * nv
@@ -130,13 +130,13 @@ def c1_flops(sh, L):
     return proj, out, attn
 
 
-def run_c2(args, b, H, W, torch):
+def run_full_prefill(args, b, H, W, torch):
     from synth.workloads import WORKLOADS
-    cfg = WORKLOADS[2]
+    cfg = WORKLOADS["full_prefill"]
     sh, Bn, L = cfg["shape"], cfg["B"], cfg["L"]
-    w = W.make_layer_weights(sh, 2, 0)
+    w = W.make_layer_weights(sh, W.Stream.FULL_PREFILL, 0)
     import synth.rng_torch as RT
-    x = RT.normal(W.stream_seed(2, 0, W.TensorId.X), Bn * L * sh.hidden).to(torch.bfloat16).view(Bn, L, sh.hidden)
+    x = RT.normal(W.stream_seed(W.Stream.FULL_PREFILL, 0, W.TensorId.X), Bn * L * sh.hidden).to(torch.bfloat16).view(Bn, L, sh.hidden)
     wd = H.weights_to_dev(sh, w)
     d = H.desc(sh)
     ws = H.workspace(b.compass_workspace_size(d, Bn, L, 0, 0))
@@ -144,30 +144,30 @@ def run_c2(args, b, H, W, torch):
     wts = b.make_weights(wd)
     step = lambda: b.compass_layer_prefill(d, wts, x, None, None, None, None, out, ws)
     sec, stats = timed(step, max(3, args.steps // 4), 2, b, torch)
-    proj, outf, attn = [Bn * f for f in c1_flops(sh, L)]
+    proj, outf, attn = [Bn * f for f in layer_flops(sh, L)]
     return {"workload": cfg["name"], "tokens_per_s_per_layer": Bn * L / sec, "ms_per_layer": 1e3 * sec,
             "mfma_frac_layer": (proj + outf + attn) / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             "kernels_us": {k: round(v["mean_us"], 1) for k, v in stats.items()}}
 
 
-def run_c3(args, b, H, W, torch):
+def run_decode_stack(args, b, H, W, torch):
     from synth.workloads import WORKLOADS, layer_kind
     import dataclasses
     import synth.rng_torch as RT
-    cfg = WORKLOADS[3]
+    cfg = WORKLOADS["decode_stack"]
     sh, Bn, n_layers, n = cfg["shape"], cfg["B"], cfg["layers"], cfg["cache_len"]
     cap = n + 8
     Hkv, hd = sh.n_kv_heads, sh.head_dim
     layers = []
     for i in range(n_layers):
         shi = dataclasses.replace(sh, kind=layer_kind(i))
-        wd = H.weights_to_dev(shi, W.make_layer_weights(shi, 3, i))
-        kc = RT.normal(W.stream_seed(3, i, W.TensorId.K_CACHE), Bn * Hkv * cap * hd).to(torch.bfloat16).view(Bn, Hkv, cap, hd)
-        vc = RT.normal(W.stream_seed(3, i, W.TensorId.V_CACHE), Bn * Hkv * cap * hd).to(torch.bfloat16).view(Bn, Hkv, cap, hd)
+        wd = H.weights_to_dev(shi, W.make_layer_weights(shi, W.Stream.DECODE_STACK, i))
+        kc = RT.normal(W.stream_seed(W.Stream.DECODE_STACK, i, W.TensorId.K_CACHE), Bn * Hkv * cap * hd).to(torch.bfloat16).view(Bn, Hkv, cap, hd)
+        vc = RT.normal(W.stream_seed(W.Stream.DECODE_STACK, i, W.TensorId.V_CACHE), Bn * Hkv * cap * hd).to(torch.bfloat16).view(Bn, Hkv, cap, hd)
         d = H.desc(shi)
         ws = H.workspace(b.compass_workspace_size(d, Bn, 1, cap, 1))
         layers.append((d, b.make_weights(wd), wd, kc, vc, ws))
-    x = RT.normal(W.stream_seed(3, 0, W.TensorId.X), Bn * sh.hidden).to(torch.bfloat16).view(Bn, sh.hidden)
+    x = RT.normal(W.stream_seed(W.Stream.DECODE_STACK, 0, W.TensorId.X), Bn * sh.hidden).to(torch.bfloat16).view(Bn, sh.hidden)
     lens = torch.full((Bn,), n, dtype=torch.int32, device="cuda")
     pos = torch.full((3, Bn), n, dtype=torch.int32, device="cuda")
     h = torch.empty_like(x)
@@ -182,9 +182,9 @@ def run_c3(args, b, H, W, torch):
     # A whole greedy decode step: embed the 64 tokens, decode positions, the 4 layers, then
     # the tied 256000-vocab head reduced to the next token ids, which feed the next step.
     # lens is not advanced (advance 0), so every timed step does the same work.
-    V = WORKLOADS[4]["vocab"]
-    E = RT.normal(W.stream_seed(3, 0, W.TensorId.EMBED), V * sh.hidden, std=0.02).to(torch.bfloat16).view(V, sh.hidden)
-    nw = RT.normal(W.stream_seed(3, 0, W.TensorId.FINAL_LN), sh.hidden, std=0.02, mean=1.0).to(torch.bfloat16)
+    V = WORKLOADS["stack_logits"]["vocab"]
+    E = RT.normal(W.stream_seed(W.Stream.DECODE_STACK, 0, W.TensorId.EMBED), V * sh.hidden, std=0.02).to(torch.bfloat16).view(V, sh.hidden)
+    nw = RT.normal(W.stream_seed(W.Stream.DECODE_STACK, 0, W.TensorId.FINAL_LN), sh.hidden, std=0.02, mean=1.0).to(torch.bfloat16)
     tok = torch.arange(Bn, dtype=torch.int32, device="cuda") * 17
     delta = torch.zeros((Bn,), dtype=torch.int32, device="cuda")
     gws = H.workspace(b.compass_logits_argmax_workspace_size(Bn, sh.hidden, V, 1))
@@ -195,14 +195,14 @@ def run_c3(args, b, H, W, torch):
         b.compass_decode_positions(lens, delta, 0, pos)
         for d, wts, _, kc, vc, ws in layers:
             b.compass_layer_decode(d, wts, h, pos, b.make_kv(kc, vc, lens), h, ws)
-        b.compass_logits_argmax(h, nw, sh.ln_eps, E, WORKLOADS[4]["logit_scale"], tok, None, gws, 1)
+        b.compass_logits_argmax(h, nw, sh.ln_eps, E, WORKLOADS["stack_logits"]["logit_scale"], tok, None, gws, 1)
 
     sec_g, stats_g = timed(greedy_step, max(5, args.steps), 3, b, torch)
     assert int(est.item()) == 0
 
     # The same decode step with 4-bit affine weights (group 64) in the four layers.
     # The ctypes structs hold raw device pointers: q4_dev keeps the tensors alive.
-    q4_dev = [H.q4_to_dev(W.make_layer_weights_q4(dataclasses.replace(sh, kind=layer_kind(i)), 3, i))
+    q4_dev = [H.q4_to_dev(W.make_layer_weights_q4(dataclasses.replace(sh, kind=layer_kind(i)), W.Stream.DECODE_STACK, i))
               for i in range(n_layers)]
     q4 = [b.make_weights_q4(wd) for wd in q4_dev]
 
@@ -244,13 +244,13 @@ def run_c3(args, b, H, W, torch):
     return res
 
 
-def run_c4(args, b, H, W, torch):
+def run_stack_logits(args, b, H, W, torch):
     from synth.workloads import WORKLOADS, layer_kind
     import dataclasses
     import synth.rng_torch as RT
-    cfg = WORKLOADS[4]
+    cfg = WORKLOADS["stack_logits"]
     sh, L, n_layers, V, scale = cfg["shape"], cfg["L"], cfg["layers"], cfg["vocab"], cfg["logit_scale"]
-    tok, grid, off = W.c1_tokens(W.stream_seed(4, 0, W.TensorId.TOKENS))
+    tok, grid, off = W.image_text_row(W.stream_seed(W.Stream.STACK_LOGITS, 0, W.TensorId.TOKENS))
     pos = torch.empty((3, 1, L), dtype=torch.int32, device="cuda")
     delta = torch.empty((1,), dtype=torch.int32, device="cuda")
     status = torch.empty((1,), dtype=torch.int32, device="cuda")
@@ -260,14 +260,14 @@ def run_c4(args, b, H, W, torch):
     layers = []
     for i in range(n_layers):
         shi = dataclasses.replace(sh, kind=layer_kind(i))
-        wd = H.weights_to_dev(shi, W.make_layer_weights(shi, 4, i))
+        wd = H.weights_to_dev(shi, W.make_layer_weights(shi, W.Stream.STACK_LOGITS, i))
         layers.append((H.desc(shi), b.make_weights(wd), wd))
-    x = RT.normal(W.stream_seed(4, 0, W.TensorId.X), L * sh.hidden).to(torch.bfloat16).view(1, L, sh.hidden)
-    ds = [RT.normal(W.stream_seed(4, i, W.TensorId.DS + i), 1024 * sh.hidden).to(torch.bfloat16).view(1024, sh.hidden)
+    x = RT.normal(W.stream_seed(W.Stream.STACK_LOGITS, 0, W.TensorId.X), L * sh.hidden).to(torch.bfloat16).view(1, L, sh.hidden)
+    ds = [RT.normal(W.stream_seed(W.Stream.STACK_LOGITS, i, W.TensorId.DS + i), 1024 * sh.hidden).to(torch.bfloat16).view(1024, sh.hidden)
           for i in range(3)]
     ds_rows = torch.arange(64, 64 + 1024, dtype=torch.int32, device="cuda")
-    E = RT.normal(W.stream_seed(4, 0, W.TensorId.EMBED), V * sh.hidden, std=0.02).to(torch.bfloat16).view(V, sh.hidden)
-    nw = RT.normal(W.stream_seed(4, 0, W.TensorId.FINAL_LN), sh.hidden, std=0.02, mean=1.0).to(torch.bfloat16)
+    E = RT.normal(W.stream_seed(W.Stream.STACK_LOGITS, 0, W.TensorId.EMBED), V * sh.hidden, std=0.02).to(torch.bfloat16).view(V, sh.hidden)
+    nw = RT.normal(W.stream_seed(W.Stream.STACK_LOGITS, 0, W.TensorId.FINAL_LN), sh.hidden, std=0.02, mean=1.0).to(torch.bfloat16)
     ws = H.workspace(max(b.compass_workspace_size(layers[0][0], 1, L, 0, 0),
                          b.compass_logits_workspace_size(L, sh.hidden, 1)))
     h = torch.empty_like(x)
@@ -289,11 +289,11 @@ def run_c4(args, b, H, W, torch):
     return res
 
 
-def run_c5(args, b, H, W, torch):
+def run_chunked_prefill(args, b, H, W, torch):
     """The headline row prefilled as 4 chunks of 1024 tokens, each continuing the dense cache
     (compass_layer_prefill_chunk; positions from the whole row), against one prefill of the
     row writing the same cache."""
-    sh, w, x, tok, grid, off = setup_c1(H, W, torch)
+    sh, w, x, tok, grid, off = setup_sliding_prefill(H, W, torch)
     L = x.shape[1]
     n_chunks, Lc = 4, L // 4
     wd = H.weights_to_dev(sh, w)
@@ -384,7 +384,7 @@ def copy_calibration(torch, nbytes=512 << 20, copies=3):
     return {"bytes_read": nbytes, "bytes_written": nbytes, "copies": copies}
 
 
-def c1_proj_bytes(sh, L):
+def proj_bytes(sh, L):
     """Algorithmic HBM bytes of one fused-projection launch: the normalized activations and
     the five weight matrices read once, q / k / v / SwiGLU output written once (bf16)."""
     D, Hq, Hkv, hd, I = sh.hidden, sh.n_q_heads, sh.n_kv_heads, sh.head_dim, sh.intermediate
@@ -405,11 +405,11 @@ def main():
     torch.cuda.set_device(0)
 
     res_extra = {}
-    if args.only in (None, "c1"):
-        log("c1: generating inputs")
-        sh, w, x, tok, grid, off, sec, stats = run_c1(args, b, H, W, torch)
+    if args.only in (None, "sliding_prefill"):
+        log("sliding_prefill: generating inputs")
+        sh, w, x, tok, grid, off, sec, stats = run_sliding_prefill(args, b, H, W, torch)
         L = x.shape[1]
-        proj, outf, attn = c1_flops(sh, L)
+        proj, outf, attn = layer_flops(sh, L)
         gp = stats["gemm_proj"]
         achieved = proj / (gp["mean_us"] * 1e-6) / 1e12
         line = {
@@ -427,19 +427,19 @@ def main():
             "roofline": {"kernel": "gemm_proj (fused LN-input q/k/v/gate/up projection + MRoPE/SwiGLU epilogue)",
                          "bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                         "traffic": traffic_for("gemm_proj_c1", GEMM_SOURCES),
+                         "traffic": traffic_for("gemm_proj_sliding_prefill", GEMM_SOURCES),
                          "flops_per_launch": proj, "mean_launch_us": gp["mean_us"],
-                         "algorithmic_bytes": c1_proj_bytes(sh, L)},
+                         "algorithmic_bytes": proj_bytes(sh, L)},
         }
         if not args.no_cpu:
-            log("c1: timing the CPU oracle")
+            log("sliding_prefill: timing the CPU oracle")
             line["cpu_baseline"] = cpu_baseline(sh, w, x, tok, grid, off)
         else:
             line["cpu_baseline"] = None
     else:
         line = None
     if not args.no_extra:
-        for key, fn in (("c2", run_c2), ("c3", run_c3), ("c4", run_c4), ("c5", run_c5)):
+        for key, fn in (("full_prefill", run_full_prefill), ("decode_stack", run_decode_stack), ("stack_logits", run_stack_logits), ("chunked_prefill", run_chunked_prefill)):
             if args.only in (None, key):
                 log(f"{key}: running")
                 res_extra[key] = fn(args, b, H, W, torch)

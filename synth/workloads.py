@@ -64,21 +64,30 @@ def _compass(kind: str, window: int) -> LayerShape:
                       kind=kind, window=window, mrope_section=(24, 20, 20), dtype="bf16")
 
 
-# The five workloads. Index 0 is the small fp32 parity case; 1 is the sliding-layer
-# prefill the headline throughput is quoted on; 2 the full-attention prefill; 3 batched
-# decode over a 4-layer stack; 4 the 4-layer stack prefill with deepstack and logits.
-WORKLOADS: Dict[int, dict] = {
-    0: dict(name="tiny sliding layer fp32 (D=256, 4/1 heads, hd=64, I=1024, W=32, L=128)",
+class Stream:
+    """Seed-stream ids (the `workload` argument of stream_seed) of the named workloads."""
+    TINY_SLIDING_F32 = 0
+    SLIDING_PREFILL = 1
+    FULL_PREFILL = 2
+    DECODE_STACK = 3
+    STACK_LOGITS = 4
+
+
+# The workloads, by name: the small fp32 parity case; the sliding-layer prefill the headline
+# throughput is quoted on; the full-attention prefill; batched decode over a 4-layer stack;
+# the 4-layer stack prefill with deepstack and logits. `stream` seeds each one's inputs.
+WORKLOADS: Dict[str, dict] = {
+    "tiny_sliding_f32": dict(stream=Stream.TINY_SLIDING_F32, name="tiny sliding layer fp32 (D=256, 4/1 heads, hd=64, I=1024, W=32, L=128)",
             shape=LayerShape(hidden=256, n_q_heads=4, n_kv_heads=1, head_dim=64, intermediate=1024,
                              kind="sliding", window=32, mrope_section=(12, 10, 10), dtype="f32"),
             B=1, L=128, layers=1),
-    1: dict(name="sliding-layer prefill bf16 (D=2048, 16/4 heads, hd=128, I=8192, W=1024, L=4096 = 64 text + 1024 image + 3008 text)",
+    "sliding_prefill": dict(stream=Stream.SLIDING_PREFILL, name="sliding-layer prefill bf16 (D=2048, 16/4 heads, hd=128, I=8192, W=1024, L=4096 = 64 text + 1024 image + 3008 text)",
             shape=_compass("sliding", 1024), B=1, L=4096, layers=1),
-    2: dict(name="full-attention prefill bf16 (D=2048, 16/4 heads, NoPE, causal, B=2, L=8192)",
+    "full_prefill": dict(stream=Stream.FULL_PREFILL, name="full-attention prefill bf16 (D=2048, 16/4 heads, NoPE, causal, B=2, L=8192)",
             shape=_compass("full", 0), B=2, L=8192, layers=1),
-    3: dict(name="batched decode bf16, 4-layer 3:1 stack, B=64, KV cache 8192, W=4096",
+    "decode_stack": dict(stream=Stream.DECODE_STACK, name="batched decode bf16, 4-layer 3:1 stack, B=64, KV cache 8192, W=4096",
             shape=_compass("sliding", 4096), B=64, L=1, layers=4, cache_len=8192),
-    4: dict(name="4-layer 3:1 stack prefill bf16, L=4096 mixed image+text, deepstack x3, tied 256000-vocab logits x 0.0625",
+    "stack_logits": dict(stream=Stream.STACK_LOGITS, name="4-layer 3:1 stack prefill bf16, L=4096 mixed image+text, deepstack x3, tied 256000-vocab logits x 0.0625",
             shape=_compass("sliding", 1024), B=1, L=4096, layers=4, vocab=256000, logit_scale=0.0625),
 }
 
@@ -103,7 +112,7 @@ def text_tokens(seed: int, n: int) -> np.ndarray:
     return _uniform_ints(seed, n, 1, 255000)
 
 
-def c1_tokens(seed: int, L: int = 4096, n_text_before: int = 64, grid=(1, 64, 64), merge: int = 2):
+def image_text_row(seed: int, L: int = 4096, n_text_before: int = 64, grid=(1, 64, 64), merge: int = 2):
     """One row: text, one image-pad span for `grid` (patch units), then text up to L.
 
     Returns (tokens [1, L] int32, grid_thw [1, 3] int32, img_offset [2] int32).

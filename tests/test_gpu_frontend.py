@@ -174,8 +174,8 @@ def test_logits_argmax_ties_and_strided_rows():
 def test_logits_argmax_decode_batch_full_vocab():
     """Decode-batch greedy head: 64 rows, hidden 2048, tied 256000-vocab table, logit_scale 0.0625."""
     R, D, V, scale = 64, 2048, 256000, 0.0625
-    h = RT.normal(stream_seed(3, 0, W.TensorId.X), R * D).to(torch.bfloat16).view(R, D)
-    E = RT.normal(stream_seed(4, 0, W.TensorId.EMBED), V * D, std=0.02).to(torch.bfloat16).view(V, D)
+    h = RT.normal(stream_seed(W.Stream.DECODE_STACK, 0, W.TensorId.X), R * D).to(torch.bfloat16).view(R, D)
+    E = RT.normal(stream_seed(W.Stream.STACK_LOGITS, 0, W.TensorId.EMBED), V * D, std=0.02).to(torch.bfloat16).view(V, D)
     nw = torch.ones(D, dtype=torch.bfloat16, device="cuda")
     tok, mx = argmax_dev(h, nw, 1e-5, E, scale, 1)
     lg = H.run_logits(h, nw, 1e-5, E, scale, 1)

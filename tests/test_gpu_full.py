@@ -38,11 +38,11 @@ def gpu_positions(tok, grid, off):
 
 def test_sliding_prefill_full_size():
     """hidden 2048, 16/4 heads, hd 128, I 8192, window 1024, L = 4096 (64 text + 1024 image + 3008 text)."""
-    cfg = WORKLOADS[1]
+    cfg = WORKLOADS["sliding_prefill"]
     sh, L = cfg["shape"], cfg["L"]
-    w = W.make_layer_weights(sh, 1, 0)
-    x = W.make_layer_input(sh, 1, L).reshape(1, L, sh.hidden)
-    tok, grid, off = W.c1_tokens(stream_seed(1, 0, W.TensorId.TOKENS))
+    w = W.make_layer_weights(sh, W.Stream.SLIDING_PREFILL, 0)
+    x = W.make_layer_input(sh, W.Stream.SLIDING_PREFILL, L).reshape(1, L, sh.hidden)
+    tok, grid, off = W.image_text_row(stream_seed(W.Stream.SLIDING_PREFILL, 0, W.TensorId.TOKENS))
     ref_pos, ref_delta = O.mrope_positions(tok, W.IMAGE_TOKEN_ID, grid, off, 2)
     pos, delta, status = gpu_positions(tok, grid, off)
     out = H.run_prefill(sh, H.weights_to_dev(sh, w), H.to_dev(x, torch.bfloat16), pos)
@@ -61,13 +61,13 @@ def got_t(a):
 
 def test_full_attention_prefill_full_size_and_relabel_invariance():
     """Full (NoPE) layer, B = 2, L = 8192; also bitwise invariance to permuted position ids."""
-    cfg = WORKLOADS[2]
+    cfg = WORKLOADS["full_prefill"]
     sh, Bn, L = cfg["shape"], cfg["B"], cfg["L"]
-    w = W.make_layer_weights(sh, 2, 0)
-    x = W.make_layer_input(sh, 2, Bn * L).reshape(Bn, L, sh.hidden)
+    w = W.make_layer_weights(sh, W.Stream.FULL_PREFILL, 0)
+    x = W.make_layer_input(sh, W.Stream.FULL_PREFILL, Bn * L).reshape(Bn, L, sh.hidden)
     wd, xd = H.weights_to_dev(sh, w), H.to_dev(x, torch.bfloat16)
     ar = np.broadcast_to(np.arange(L, dtype=np.int32), (3, Bn, L)).copy()
-    perm = np.stack([np.stack([W.permutation(stream_seed(2, 3 * b + a, W.TensorId.PERM), L) for b in range(Bn)])
+    perm = np.stack([np.stack([W.permutation(stream_seed(W.Stream.FULL_PREFILL, 3 * b + a, W.TensorId.PERM), L) for b in range(Bn)])
                      for a in range(3)]).astype(np.int32)
     o1 = H.run_prefill(sh, wd, xd, H.ints_to_dev(ar))
     o2 = H.run_prefill(sh, wd, xd, H.ints_to_dev(perm))
@@ -80,12 +80,12 @@ def test_full_attention_prefill_full_size_and_relabel_invariance():
 
 def test_batched_decode_stack_full_size():
     """4 layers [S, S, S, F], B = 64, cache 8192, window 4096: one decode step."""
-    cfg = WORKLOADS[3]
+    cfg = WORKLOADS["decode_stack"]
     sh, Bn, n_layers, n = cfg["shape"], cfg["B"], cfg["layers"], cfg["cache_len"]
     cap = n + 8
     Hkv, hd = sh.n_kv_heads, sh.head_dim
     rows = [0, 17, 42, 63]
-    x = W.make_layer_input(sh, 3, Bn)
+    x = W.make_layer_input(sh, W.Stream.DECODE_STACK, Bn)
     lens_np = np.full(Bn, n, np.int32)
     pos_np = O.decode_positions(lens_np, np.zeros(Bn, np.int64)).astype(np.int32)
     h = H.to_dev(x, torch.bfloat16)
@@ -93,9 +93,9 @@ def test_batched_decode_stack_full_size():
     layers = []
     for i in range(n_layers):
         shi = dataclasses.replace(sh, kind=layer_kind(i))
-        w = W.make_layer_weights(shi, 3, i)
-        kc = RT.normal(stream_seed(3, i, W.TensorId.K_CACHE), Bn * Hkv * cap * hd).to(torch.bfloat16).view(Bn, Hkv, cap, hd)
-        vc = RT.normal(stream_seed(3, i, W.TensorId.V_CACHE), Bn * Hkv * cap * hd).to(torch.bfloat16).view(Bn, Hkv, cap, hd)
+        w = W.make_layer_weights(shi, W.Stream.DECODE_STACK, i)
+        kc = RT.normal(stream_seed(W.Stream.DECODE_STACK, i, W.TensorId.K_CACHE), Bn * Hkv * cap * hd).to(torch.bfloat16).view(Bn, Hkv, cap, hd)
+        vc = RT.normal(stream_seed(W.Stream.DECODE_STACK, i, W.TensorId.V_CACHE), Bn * Hkv * cap * hd).to(torch.bfloat16).view(Bn, Hkv, cap, hd)
         kc_host = H.np64(kc[rows, :, :n])  # cache contents before the step (inputs)
         vc_host = H.np64(vc[rows, :, :n])
         H.run_decode(shi, H.weights_to_dev(shi, w), h, pos, kc, vc, lens, out=h)
@@ -117,17 +117,17 @@ def test_batched_decode_stack_full_size():
 
 def test_stack_prefill_deepstack_logits_full_size():
     """4-layer [S, S, S, F] prefill, L = 4096, deepstack after layers 0-2, 256000-vocab logits x 0.0625."""
-    cfg = WORKLOADS[4]
+    cfg = WORKLOADS["stack_logits"]
     sh, L, n_layers, V, scale = cfg["shape"], cfg["L"], cfg["layers"], cfg["vocab"], cfg["logit_scale"]
     D = sh.hidden
-    tok, grid, off = W.c1_tokens(stream_seed(4, 0, W.TensorId.TOKENS))
+    tok, grid, off = W.image_text_row(stream_seed(W.Stream.STACK_LOGITS, 0, W.TensorId.TOKENS))
     pos_np, _ = O.mrope_positions(tok, W.IMAGE_TOKEN_ID, grid, off, 2)
-    x = W.make_layer_input(sh, 4, L).reshape(1, L, D)
+    x = W.make_layer_input(sh, W.Stream.STACK_LOGITS, L).reshape(1, L, D)
     ds = [W.make_tensor(sh, 4, i, W.TensorId.DS + i, (1024, D)) for i in range(3)]
     ds_rows = np.arange(64, 64 + 1024, dtype=np.int32)
-    ws = [W.make_layer_weights(dataclasses.replace(sh, kind=layer_kind(i)), 4, i) for i in range(n_layers)]
+    ws = [W.make_layer_weights(dataclasses.replace(sh, kind=layer_kind(i)), W.Stream.STACK_LOGITS, i) for i in range(n_layers)]
     nw = W.make_tensor(sh, 4, 0, W.TensorId.FINAL_LN, (D,), std=0.02, mean=1.0)
-    E = RT.normal(stream_seed(4, 0, W.TensorId.EMBED), V * D, std=0.02).to(torch.bfloat16).view(V, D)
+    E = RT.normal(stream_seed(W.Stream.STACK_LOGITS, 0, W.TensorId.EMBED), V * D, std=0.02).to(torch.bfloat16).view(V, D)
     pos = H.ints_to_dev(pos_np)
     h = H.to_dev(x, torch.bfloat16)
     rows_d = H.ints_to_dev(ds_rows)

@@ -87,14 +87,14 @@ def test_q4_decode_skips_rows_and_aliases():
 def test_q4_decode_full_size(layer):
     """The batched-decode workload's widths (hidden 2048, 16/4 heads, hd 128, I 8192), B = 64 over
     a cache of 8192 tokens (window 4096 on the sliding layer), sampled rows against the oracle."""
-    cfg = WORKLOADS[3]
+    cfg = WORKLOADS["decode_stack"]
     sh = dataclasses.replace(cfg["shape"], kind=W.layer_kind(layer))
     Bn, n = cfg["B"], cfg["cache_len"]
     cap = n + 8
     Hkv, hd = sh.n_kv_heads, sh.head_dim
-    wq4 = W.make_layer_weights_q4(sh, 3, layer)
-    kc = RT.normal(stream_seed(3, layer, W.TensorId.K_CACHE), Bn * Hkv * cap * hd).to(torch.bfloat16).view(Bn, Hkv, cap, hd)
-    vc = RT.normal(stream_seed(3, layer, W.TensorId.V_CACHE), Bn * Hkv * cap * hd).to(torch.bfloat16).view(Bn, Hkv, cap, hd)
+    wq4 = W.make_layer_weights_q4(sh, W.Stream.DECODE_STACK, layer)
+    kc = RT.normal(stream_seed(W.Stream.DECODE_STACK, layer, W.TensorId.K_CACHE), Bn * Hkv * cap * hd).to(torch.bfloat16).view(Bn, Hkv, cap, hd)
+    vc = RT.normal(stream_seed(W.Stream.DECODE_STACK, layer, W.TensorId.V_CACHE), Bn * Hkv * cap * hd).to(torch.bfloat16).view(Bn, Hkv, cap, hd)
     rows = [0, 31, 63]
     kh = H.np64(kc[rows])
     vh = H.np64(vc[rows])

@@ -60,7 +60,7 @@ def test_positions_bit_exact(B, L):
 
 
 def test_positions_c1_layout_bit_exact():
-    tok, grid, off = W.c1_tokens(seed=5)
+    tok, grid, off = W.image_text_row(seed=5)
     pos, delta, status = gpu_positions(tok, grid, off)
     ref_pos, ref_delta = O.mrope_positions(tok, W.IMAGE_TOKEN_ID, grid, off, 2)
     assert status.tolist() == [0]
@@ -300,10 +300,10 @@ def test_tiny_fp32_workload_against_both_oracles():
     window 32, 128 text tokens with t = h = w = index, N(0, 0.02) weights): the GPU layer against
     the fp64 numpy oracle and against the plain fp32 C++ reference, 1e-4 each."""
     from oracle import ref as R
-    cfg = W.WORKLOADS[0]
+    cfg = W.WORKLOADS["tiny_sliding_f32"]
     sh, L = cfg["shape"], cfg["L"]
-    w = W.make_layer_weights(sh, 0, 0)
-    x = W.make_layer_input(sh, 0, L).reshape(1, L, sh.hidden)
+    w = W.make_layer_weights(sh, W.Stream.TINY_SLIDING_F32, 0)
+    x = W.make_layer_input(sh, W.Stream.TINY_SLIDING_F32, L).reshape(1, L, sh.hidden)
     p = np.arange(L)
     pos = np.stack([p, p, p])[:, None, :]
     out = H.run_prefill(sh, H.weights_to_dev(sh, w), H.to_dev(x, torch.float32), H.ints_to_dev(pos))

@@ -52,7 +52,7 @@ def test_positions_bit_exact():
     assert code == 0
     np.testing.assert_array_equal(pos, ref_pos)
     np.testing.assert_array_equal(delta, ref_delta)
-    tok, grid, off = W.c1_tokens(seed=5, L=4096)
+    tok, grid, off = W.image_text_row(seed=5, L=4096)
     code, pos, delta = R.mrope_positions(tok, W.IMAGE_TOKEN_ID, grid, off, 2)
     ref_pos, ref_delta = O.mrope_positions(tok, W.IMAGE_TOKEN_ID, grid, off, 2)
     assert code == 0 and int(delta[0]) == -992

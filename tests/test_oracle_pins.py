@@ -637,8 +637,8 @@ def test_positions_image_448_page_example():
 
 def test_positions_c1_layout_hand_derived():
     """64 text, one 1x64x64 (patch) image = 32x32 merged tokens, 3008 text."""
-    from synth.workloads import c1_tokens
-    tok, grid, off = c1_tokens(seed=1)
+    from synth.workloads import image_text_row
+    tok, grid, off = image_text_row(seed=1)
     pos, d = O.mrope_positions(tok, 255031, grid, off, 2)
     assert np.array_equal(pos[:, 0, :64], np.stack([np.arange(64)] * 3))
     r = np.arange(1024)
