@@ -141,7 +141,7 @@ def test_prefill_large_logits():
     storage steps: a = bf16(LN(x)), q = bf16(a Wq^T), the kernel's own K / V (read back from
     the cache), act = bf16(silu(a Wg^T) * (a Wu^T)), then the oracle's attention in fp64 and
     the bf16-rounded attention output through Wo. What remains is the softmax arithmetic
-    (bf16 P) plus rare one-ulp differences: about 1e-3. A softmax that loses precision fails
+    (bf16 P) plus rare one-ulp differences: 3.2e-3 measured. A softmax that loses precision fails
     the 8e-3 gate (re-rounding q * log2(e) / sqrt(hd) to bf16, for one, gives 2.5e-2 here in a
     CPU emulation). A full-attention (NoPE) layer, so no rotation angle enters q."""
     sh = H.small_shape("bf16", "full", 128, 4, 1, 256, 512, 0)
@@ -168,4 +168,5 @@ def test_prefill_large_logits():
     ref = x[0].astype(np.float64) + d_ref
     d_gpu = H.np64(out)[0] - x[0]
     e_branch = float(np.max(np.abs(d_gpu - d_ref) - 2.0 ** -8 * np.abs(ref)) / np.max(np.abs(d_ref)))
+    print(f"large-logit layer: branch-sum rel err {e_branch:.3e} at score spread {spread:.1f}")
     assert e_branch <= 8e-3, f"branch-sum rel err {e_branch:.3e} at score spread {spread:.1f}"
