@@ -6,6 +6,8 @@
 // registers (16-byte loads), mean and variance are two passes over registers with
 // wave reductions, and the normalized row is written in the input's dtype: bf16
 // rows become the bf16 A operand of the projection GEMM.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -27,6 +29,18 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const T* __restrict__ x,
   constexpr int V = (sizeof(T) == 2) ? 8 : 4;  // elements per 16-byte vector
   constexpr int NV = (VPL + V - 1) / V;        // vectors per lane
   float v[NV * V];
+  // Small rows also fetch the weight up front, so its loads overlap the row's instead of
+  // following the two reductions.
+  using W16 = typename std::conditional<sizeof(T) == 2, u32x4_t, float4>::type;
+  constexpr bool kEarlyW = NV <= 8;
+  W16 wpre[kEarlyW ? NV : 1];
+  if constexpr (kEarlyW) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = (i * 64 + lane) * V;
+      if (e < D) wpre[i] = *reinterpret_cast<const W16*>(w + e);
+    }
+  }
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -69,8 +83,10 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const T* __restrict__ x,
   for (int i = 0; i < NV; ++i) {
     const int e = (i * 64 + lane) * V;
     if (e >= D) continue;
+    W16 wr;
+    if constexpr (kEarlyW) wr = wpre[i];
+    else wr = *reinterpret_cast<const W16*>(w + e);
     if constexpr (sizeof(T) == 2) {
-      u32x4_t wr = *reinterpret_cast<const u32x4_t*>(w + e);
       const uint32_t w4[4] = {wr.x, wr.y, wr.z, wr.w};
       uint32_t o4[4];
 #pragma unroll
@@ -81,7 +97,6 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const T* __restrict__ x,
       }
       __builtin_nontemporal_store(u32x4_t{o4[0], o4[1], o4[2], o4[3]}, reinterpret_cast<u32x4_t*>(ar + e));
     } else {
-      float4 wr = *reinterpret_cast<const float4*>(w + e);
       float4 o;
       o.x = (v[i * V + 0] - mean) * rstd * wr.x;
       o.y = (v[i * V + 1] - mean) * rstd * wr.y;
