@@ -59,6 +59,40 @@ def got_t(a):
     return torch.from_numpy(a)
 
 
+def test_chunked_prefill_full_size():
+    """The same row as 4 chunks of 1024 tokens, each continuing the dense cache (the chunked
+    workload bench.py times): sampled rows against the fp64 oracle, the cache against the one
+    a single prefill of the row writes (the projection's arithmetic per element does not depend
+    on the rows in the launch, so bitwise), and every output row within the bf16 gate of that
+    prefill's (the chunks' output GEMM splits K, so not bitwise)."""
+    cfg = WORKLOADS["sliding_prefill"]
+    sh, L = cfg["shape"], cfg["L"]
+    w = W.make_layer_weights(sh, W.Stream.SLIDING_PREFILL, 0)
+    x = W.make_layer_input(sh, W.Stream.SLIDING_PREFILL, L).reshape(1, L, sh.hidden)
+    tok, grid, off = W.image_text_row(stream_seed(W.Stream.SLIDING_PREFILL, 0, W.TensorId.TOKENS))
+    ref_pos, _ = O.mrope_positions(tok, W.IMAGE_TOKEN_ID, grid, off, 2)
+    pos, _, status = gpu_positions(tok, grid, off)
+    wd, xd = H.weights_to_dev(sh, w), H.to_dev(x, torch.bfloat16)
+    n_chunks, Lc = 4, L // 4
+    kc = torch.full((1, sh.n_kv_heads, L, sh.head_dim), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vc = torch.full_like(kc, float("nan"))
+    outs = []
+    for i in range(n_chunks):
+        lens = H.ints_to_dev(np.array([i * Lc], dtype=np.int32))
+        outs.append(H.run_prefill_chunk(sh, wd, xd[:, i * Lc:(i + 1) * Lc].contiguous(),
+                                        pos[:, :, i * Lc:(i + 1) * Lc].contiguous(), kc, vc, lens))
+    got = torch.cat(outs, dim=1)
+    kf, vf = torch.empty_like(kc), torch.empty_like(vc)
+    whole = H.run_prefill(sh, wd, xd, pos, kv=(kf, vf))
+    torch.cuda.synchronize()
+    assert status.item() == 0
+    assert torch.equal(kc, kf) and torch.equal(vc, vf)
+    rows = [0, 63, 64, 1023, 1024, 1025, 1087, 1088, 2047, 2048, 3071, 3072, 4095]
+    ref = O.layer_prefill_rows(sh, w, x, ref_pos, 0, rows)
+    check_layer_out(sh, got_t(H.np64(got[0, rows])), x[0, rows], ref)
+    assert H.rel_err(H.np64(got), H.np64(whole)) <= H.tol(sh)
+
+
 def test_full_attention_prefill_full_size_and_relabel_invariance():
     """Full (NoPE) layer, B = 2, L = 8192; also bitwise invariance to permuted position ids."""
     cfg = WORKLOADS["full_prefill"]
