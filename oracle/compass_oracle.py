@@ -60,10 +60,11 @@ class PositionError(ValueError):
 
 
 # ----------------------------------------------------------------------------------------
-# Position ids. Page 1, "Position ids (get_rope_index)": text tokens advance t/h/w by one;
-# the t*(h/2)*(w/2) pads of an image take (t_idx, h_idx, w_idx) on the merged grid plus the
-# running text offset; the next text token starts at max(previous positions) + 1;
-# rope_delta = max_position + 1 - L.
+# Position ids. Page 1, "Position ids (get_rope_index)". A running counter st gives every
+# ordinary token the triple (st, st, st) and then moves on by one. An image spans one pad per
+# cell of its merged grid (frames x rows/merge x cols/merge); each pad gets st plus its own
+# (frame, row, col) index, and afterwards st moves past the largest of the three extents.
+# The row's offset for later tokens is the final counter minus the row length.
 # ----------------------------------------------------------------------------------------
 def mrope_positions(tokens: np.ndarray, image_token_id: int, grid_thw: np.ndarray,
                     img_offset: np.ndarray, spatial_merge: int) -> Tuple[np.ndarray, np.ndarray]:
@@ -292,12 +293,13 @@ def layer_prefill_rows(shape, w: Dict[str, np.ndarray], x: np.ndarray, pos: Opti
                        b: int, rows: Sequence[int]) -> np.ndarray:
     """Outputs of selected rows of batch row b, computed one by one from the definition.
 
-    Only the keys each selected query can see are projected. Returns [len(rows), D]
-    (no deepstack term).
+    Only the keys each selected query can see are projected: the span from the earliest
+    key visible to the smallest selected row up to the largest selected row. Returns
+    [len(rows), D] in the order of `rows` (no deepstack term).
     """
     x = np.asarray(x, dtype=F64)
     Hq, Hkv, hd = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
-    rows = np.asarray(sorted(rows))
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1)
     lo = 0 if shape.kind == "full" else max(0, int(rows.min()) - shape.window + 1)
     hi = int(rows.max()) + 1
     span = np.arange(lo, hi)

@@ -204,6 +204,10 @@ MUTANTS = {
     "logit scale dropped": ("logits", _edited("logits", ("* float(logit_scale)", "* 1.0"))),
     "deepstack rows shifted by one": ("layer_prefill", _edited(
         "layer_prefill", ("flat[np.asarray(ds_rows)] +=", "flat[np.asarray(ds_rows) + 1] +="))),
+    "row sampler key span starts one late": ("layer_prefill_rows", _edited(
+        "layer_prefill_rows", ("int(rows.min()) - shape.window + 1", "int(rows.min()) - shape.window + 2"))),
+    "row sampler keys not offset by the span start": ("layer_prefill_rows", _edited(
+        "layer_prefill_rows", ("k_index=span)", "k_index=span - lo)"))),
     "deepstack after every layer": ("stack_prefill", _edited(
         "stack_prefill", ("i < 3 and i < len(ds)", "i < len(ds)"))),
 }
@@ -239,6 +243,9 @@ PINS = [
     P.test_deepstack_adds_at_rows_only,
     P.test_stack_deepstack_first_three_layers_only,
     P.test_prefill_decode_consistency,
+    lambda: P.test_layer_prefill_rows_equals_whole_prefill("sliding", 3, 1, 0, [0, 1, 5, 9, 16]),
+    lambda: P.test_layer_prefill_rows_equals_whole_prefill("sliding", 3, 2, 1, [16, 2, 9, 6]),
+    lambda: P.test_layer_prefill_rows_equals_whole_prefill("sliding", 3, 1, 0, [3, 4, 11, 12]),
 ]
 
 

@@ -327,6 +327,28 @@ def test_parallel_block_identity_no_post_norm():
     np.testing.assert_allclose(O.layer_prefill(sh, w3, x, pos)[0], x[0] + mlp, atol=1e-12)
 
 
+@pytest.mark.parametrize("kind,window,B,b,rows", [
+    ("sliding", 3, 1, 0, [0, 1, 5, 9, 16]),          # rows spread far wider than the window
+    ("sliding", 3, 1, 0, [0, 1, 2]),                  # rows below the window (no key before 0)
+    ("sliding", 3, 1, 0, [3, 4, 11, 12]),             # first rows whose window edge leaves key 0
+    ("sliding", 3, 2, 1, [16, 2, 9, 6]),              # batch row 1 of 2, rows in no order
+    ("sliding", 1, 2, 1, [0, 7, 16]),                 # window 1: each row sees only itself
+    ("sliding", 40, 1, 0, [4, 16, 0]),                # window beyond L: plain causal
+    ("full", 0, 2, 1, [16, 0, 8, 3]),                 # full layer, batch row 1
+])
+def test_layer_prefill_rows_equals_whole_prefill(kind, window, B, b, rows):
+    """The row sampler returns, in the caller's order, exactly the rows a whole-sequence
+    prefill gives (without deepstack), for every key span the selection implies."""
+    sh = tiny_shape(kind, window)
+    w = rand_weights(sh, seed=70 + window)
+    L = 17
+    x = np.random.default_rng(71).standard_normal((B, L, sh.hidden))
+    pos = mixed_pos(B, L, seed=72)
+    whole = O.layer_prefill(sh, w, x, pos)
+    got = O.layer_prefill_rows(sh, w, x, pos if kind == "sliding" else None, b, rows)
+    np.testing.assert_allclose(got, whole[b, rows], atol=1e-11)
+
+
 def test_window_at_least_L_equals_causal():
     sh = tiny_shape("sliding", 9)
     w = rand_weights(sh, seed=13)
