@@ -151,7 +151,8 @@ def run_full_prefill(args, b, H, W, torch):
 
 
 def run_decode_stack(args, b, H, W, torch):
-    from synth.workloads import WORKLOADS, layer_kind
+    from synth.workloads import WORKLOADS
+    from cohere2_block_mrope_amd.stack import layer_kind
     import dataclasses
     import synth.rng_torch as RT
     cfg = WORKLOADS["decode_stack"]
@@ -245,7 +246,8 @@ def run_decode_stack(args, b, H, W, torch):
 
 
 def run_stack_logits(args, b, H, W, torch):
-    from synth.workloads import WORKLOADS, layer_kind
+    from synth.workloads import WORKLOADS
+    from cohere2_block_mrope_amd.stack import layer_kind
     import dataclasses
     import synth.rng_torch as RT
     cfg = WORKLOADS["stack_logits"]

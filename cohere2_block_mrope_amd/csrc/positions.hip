@@ -106,8 +106,13 @@ __global__ __launch_bounds__(kThreads) void positions_kernel(
       break;
     }
     const int gh = h / merge, gw = w / merge;
-    const long long nll = (long long)t * gh * gw;
-    if (nll > (long long)(L - sidx)) {
+    // The span t * gh * gw must fit in the rest of the row. Each factor is at least one, so
+    // a factor beyond the rest already fails; otherwise the product is below 2^57 (the row
+    // holds at most 2^19 tokens) and cannot wrap.
+    const long long rest = (long long)(L - sidx);
+    const bool too_big = t > rest || gh > rest || gw > rest || (long long)t * gh * gw > rest;
+    const long long nll = too_big ? rest + 1 : (long long)t * gh * gw;
+    if (too_big) {
       if (tid == 0) s_err = COMPASS_POS_SPAN_MISMATCH;
       break;
     }

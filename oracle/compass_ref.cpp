@@ -140,8 +140,9 @@ int cref_mrope_positions(const int32_t* tok, int B, int L, int image_id, const i
       const int t = grid[3 * k], h = grid[3 * k + 1], w = grid[3 * k + 2];
       if (t < 1 || h < 1 || w < 1 || h % merge || w % merge) return 4;
       const int gh = h / merge, gw = w / merge;
-      const long long n = (long long)t * gh * gw;
-      if (l + n > L) return 1;
+      const __int128 n_exact = (__int128)t * gh * gw;  // exact: no int64 wrap for any int32 grid
+      if (l + n_exact > L) return 1;
+      const long long n = (long long)n_exact;
       for (long long r = 0; r < n; ++r)
         if (tok[(size_t)b * L + l + r] != image_id) return 1;
       for (long long r = 0; r < n; ++r) {

@@ -92,11 +92,6 @@ WORKLOADS: Dict[str, dict] = {
 }
 
 
-def layer_kind(i: int) -> str:
-    """Layer-type pattern of the stack: full attention exactly when i % 4 == 3."""
-    return "full" if i % 4 == 3 else "sliding"
-
-
 def _uniform_ints(seed: int, n: int, lo: int, hi: int) -> np.ndarray:
     with np.errstate(over="ignore"):
         idx = np.arange(n, dtype=np.uint64)

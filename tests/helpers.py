@@ -141,3 +141,33 @@ def rand_np(seed: int, shape_tuple, std=1.0, mean=0.0, bf16=True) -> np.ndarray:
     from synth import normal
     v = normal(seed, int(np.prod(shape_tuple)), std=std, mean=mean).reshape(shape_tuple)
     return bf16_round(v) if bf16 else v
+
+
+# Attention probe: a layer with Wo = 64 I and w_down = 0 (needs Hq * hd == D) returns
+# out = x + 64 o, which exposes the attention output o alone through the layer call.
+PROBE_SCALE = 64.0
+
+
+def probe_weights(shape: LayerShape, w: dict) -> dict:
+    """The attention-probe layer's weights: w with Wo = 64 I and w_down = 0."""
+    D = shape.hidden
+    assert shape.n_q_heads * shape.head_dim == D, "the probe needs Hq * hd == hidden"
+    p = dict(w)
+    p["wo"] = (PROBE_SCALE * np.eye(D)).astype(np.float32)
+    p["w_down"] = np.zeros_like(w["w_down"])
+    return p
+
+
+def check_attn_rows(shape: LayerShape, out_probe, x, o_ref, what: str = "") -> float:
+    """Row-wise gate on the attention output: (out - x) of the probe layer against 64 o of
+    the oracle, each row on its own scale, allowing the storage rounding of out."""
+    g = np64(out_probe).reshape(-1, shape.hidden) if isinstance(out_probe, torch.Tensor) \
+        else np.asarray(out_probe, np.float64).reshape(-1, shape.hidden)
+    xr = np.asarray(x, np.float64).reshape(-1, shape.hidden)
+    d_ref = PROBE_SCALE * np.asarray(o_ref, np.float64).reshape(-1, shape.hidden)
+    ulp = 2.0 ** -8 if shape.dtype == "bf16" else 2.0 ** -23
+    excess = np.abs((g - xr) - d_ref) - ulp * np.abs(xr + d_ref)
+    per_row = np.max(excess, axis=1) / np.max(np.abs(d_ref), axis=1)
+    worst = int(np.argmax(per_row))
+    assert per_row[worst] <= tol(shape), f"{what}: attention row {worst} rel err {per_row[worst]:.3e}"
+    return float(per_row[worst])

@@ -137,10 +137,11 @@ def test_prefill_large_logits():
 
     At this spread the storage roundings decide the result by percents: the layer feeds the
     bf16-rounded LayerNorm output to the projection and stores q / k / v in bf16, and that
-    alone moves the fp64 oracle's output by 2.2e-2 here. So the reference follows the same
-    storage steps: a = bf16(LN(x)), q = bf16(a Wq^T), the kernel's own K / V (read back from
-    the cache), act = bf16(silu(a Wg^T) * (a Wu^T)), then the oracle's attention in fp64 and
-    the bf16-rounded attention output through Wo. What remains is the softmax arithmetic
+    alone moves the fp64 oracle's output by 2.2e-2 here. So the reference, built from the
+    oracle's functions alone, follows the same storage steps: a = bf16(LN(x)), q = bf16(a Wq^T),
+    k = bf16(a Wk^T), v = bf16(a Wv^T), act = bf16(silu(a Wg^T) * (a Wu^T)), then the oracle's
+    attention in fp64 and the bf16-rounded attention output through Wo; the kernel's cache is
+    checked against that k and v. What remains is the softmax arithmetic
     (bf16 P) plus rare one-ulp differences: 3.2e-3 measured. A softmax that loses precision fails
     the 8e-3 gate (re-rounding q * log2(e) / sqrt(hd) to bf16, for one, gives 2.5e-2 here in a
     CPU emulation). A full-attention (NoPE) layer, so no rotation angle enters q."""
@@ -158,7 +159,9 @@ def test_prefill_large_logits():
     f64 = lambda n: w[n].astype(np.float64)
     a = H.bf16_round(O.layer_norm(x[0], w["ln_w"], sh.ln_eps))
     q = H.bf16_round(a @ f64("wq").T).reshape(L, Hq, hd).transpose(1, 0, 2)
-    k, v = H.np64(kc)[0], H.np64(vc)[0]
+    k = H.bf16_round(a @ f64("wk").T).reshape(L, sh.n_kv_heads, hd).transpose(1, 0, 2)
+    v = H.bf16_round(a @ f64("wv").T).reshape(L, sh.n_kv_heads, hd).transpose(1, 0, 2)
+    assert H.rel_err(H.np64(kc)[0], k) <= 2e-2 and H.rel_err(H.np64(vc)[0], v) <= 2e-2
     s = np.einsum("hqd,hkd->hqk", q, np.repeat(k, Hq // sh.n_kv_heads, axis=0)) / np.sqrt(hd)
     spread = np.log2(np.e) * float(np.std(s[:, np.tril(np.ones((L, L), bool))]))
     assert spread > 25.0, f"score spread {spread:.1f} log2 units: the case is not large-logit"

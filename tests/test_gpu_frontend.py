@@ -20,6 +20,7 @@ from synth import stream_seed
 from synth import workloads as W
 import synth.rng_torch as RT
 from tests import helpers as H
+import cohere2_block_mrope_amd.stack as S
 
 pytestmark = pytest.mark.gpu
 
@@ -210,7 +211,7 @@ def gpu_greedy_generate(sh, layer_w, E, nw, scale, tokens, grid, off, feats, ds,
     cap = L + n_new
     caches = []
     for i, w in enumerate(layer_w):
-        shi = sh.with_kind(W.layer_kind(i))
+        shi = sh.with_kind(S.layer_kind(i))
         kc = torch.zeros((Bn, sh.n_kv_heads, cap, sh.head_dim), dtype=tdt, device="cuda")
         vc = torch.zeros_like(kc)
         dsd = H.to_dev(ds[i], tdt) if i < 3 else None
@@ -229,7 +230,7 @@ def gpu_greedy_generate(sh, layer_w, E, nw, scale, tokens, grid, off, feats, ds,
         x, _ = embed_dev(tok, Ed, None, None, cd)
         b.compass_decode_positions(lens, delta, 0 if step == 0 else 1, p3)
         for i, w in enumerate(layer_w):
-            shi = sh.with_kind(W.layer_kind(i))
+            shi = sh.with_kind(S.layer_kind(i))
             H.run_decode(shi, w, x, p3, caches[i][0], caches[i][1], lens, out=x)
         hid[:, step + 1] = x
         tok, _ = argmax_dev(x, nd, sh.ln_eps, Ed, scale, cd)

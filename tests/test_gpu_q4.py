@@ -18,6 +18,7 @@ from synth import workloads as W
 from synth.workloads import WORKLOADS
 import synth.rng_torch as RT
 from tests import helpers as H
+import cohere2_block_mrope_amd.stack as S
 from tests.test_gpu_small import check_layer_out
 
 pytestmark = pytest.mark.gpu
@@ -88,7 +89,7 @@ def test_q4_decode_full_size(layer):
     """The batched-decode workload's widths (hidden 2048, 16/4 heads, hd 128, I 8192), B = 64 over
     a cache of 8192 tokens (window 4096 on the sliding layer), sampled rows against the oracle."""
     cfg = WORKLOADS["decode_stack"]
-    sh = dataclasses.replace(cfg["shape"], kind=W.layer_kind(layer))
+    sh = dataclasses.replace(cfg["shape"], kind=S.layer_kind(layer))
     Bn, n = cfg["B"], cfg["cache_len"]
     cap = n + 8
     Hkv, hd = sh.n_kv_heads, sh.head_dim

@@ -68,7 +68,8 @@ def test_positions_c1_layout_bit_exact():
     assert delta[0] == -992
 
 
-@pytest.mark.parametrize("case", ["short_span", "extra_pads", "unused_image", "bad_grid", "span_past_end"])
+@pytest.mark.parametrize("case", ["short_span", "extra_pads", "unused_image", "bad_grid", "span_past_end",
+                                  "grid_product_past_int64"])
 def test_positions_error_codes(case):
     n = 4
     I = W.IMAGE_TOKEN_ID
@@ -78,6 +79,8 @@ def test_positions_error_codes(case):
         "unused_image": ([[1] + [I] * n + [2]], [[1, 4, 4], [1, 2, 2]]),
         "bad_grid": ([[1] + [I] * n + [2]], [[1, 3, 4]]),
         "span_past_end": ([[1, 2] + [I] * (n - 1)], [[1, 4, 4]]),
+        # merged grid 2^21 x 2^21 x 2^22: the pad count 2^64 wraps a 64-bit product to 0
+        "grid_product_past_int64": ([[1] + [I] * n + [2]], [[1 << 21, 1 << 22, 1 << 23]]),
     }
     tok, grid = rows[case]
     tok = np.array(tok, np.int32)
@@ -275,6 +278,62 @@ def test_prefill_then_decode_matches_longer_prefill():
         dec = H.run_decode(sh, wd, xd[:, L - 1].contiguous(), H.ints_to_dev(pos[:, :, L - 1]), kc, vc, lens)
         torch.cuda.synchronize()
         assert H.rel_err(H.np64(dec), H.np64(full[:, L - 1])) <= 2e-2
+
+
+@pytest.mark.parametrize("kind,win", [("full", 0), ("sliding", 4096), ("sliding", 1000)])
+def test_decode_long_cache_attention_probe(kind, win):
+    """Caches past 4096 keys: the full layer merges up to 20 chunks of 256 keys (more than one
+    group of 16 in the chunk merge) and the window-4096 layer up to 17. Each row's attention
+    output is gated on its own scale through the probe layer (Wo = 64 I, w_down = 0), which a
+    window or merge error cannot hide behind the MLP branch; the plain layer output too."""
+    sh = H.small_shape("bf16", kind, 128, 4, 1, 512, 512, win)
+    lens = np.array([0, 17, 255, 1000, 4095, 4096, 4097, 4500, 4999], np.int32)
+    Bn, cap = len(lens), 5000
+    w, _, _ = layer_case(sh, 1, 8, seed=91)
+    x = H.rand_np(92, (Bn, sh.hidden))
+    kc = H.rand_np(93, (Bn, 1, cap, 128))
+    vc = H.rand_np(94, (Bn, 1, cap, 128))
+    pos = O.decode_positions(lens, np.array([0, 3, -5, 0, 7, 0, -992, 0, 1], np.int64))
+    wp = H.probe_weights(sh, w)
+    kd, vd = H.to_dev(kc, torch.bfloat16), H.to_dev(vc, torch.bfloat16)
+    args = (H.to_dev(x, torch.bfloat16), H.ints_to_dev(pos), kd, vd, H.ints_to_dev(lens))
+    out = H.run_decode(sh, H.weights_to_dev(sh, w), *args)
+    probe = H.run_decode(sh, H.weights_to_dev(sh, wp), *args)
+    torch.cuda.synchronize()
+    ref, _, _ = O.layer_decode(sh, w, x, pos, kc, vc, lens)
+    ref_p, _, _ = O.layer_decode(sh, wp, x, pos, kc, vc, lens)
+    check_layer_out(sh, out, x, ref, f"decode {kind} W={win}")
+    H.check_attn_rows(sh, probe, x, (ref_p - x) / H.PROBE_SCALE, f"decode {kind} W={win}")
+
+
+@pytest.mark.parametrize("offset", [8100, 32700])
+def test_prefill_then_decode_at_large_positions(offset):
+    """Row L-1 of prefill(L) against decode of token L-1 over prefill(L-1)'s cache with the
+    positions moved up by `offset`, where the rotation angles are largest. The prefill
+    epilogue evaluates each angle in turns with the hardware sine and cosine, the decode
+    epilogue in radians with the accurate sincosf; both stay within the gate of each other and
+    of the oracle, and so do the rotated keys of the last token."""
+    sh = H.small_shape("bf16", "sliding", 128, 4, 1, 512, 512, 50)
+    Bn, L = 2, 130
+    w, x, pos = layer_case(sh, Bn, L, seed=23)
+    pos = pos + offset
+    wd = H.weights_to_dev(sh, w)
+    cap = L + 5
+    kc = torch.zeros((Bn, 1, cap, 128), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    kf = torch.zeros_like(kc)
+    xd = H.to_dev(x, torch.bfloat16)
+    full = H.run_prefill(sh, wd, xd, H.ints_to_dev(pos), kv=(kf, torch.zeros_like(kc)))
+    H.run_prefill(sh, wd, xd[:, :L - 1].contiguous(), H.ints_to_dev(pos[:, :, :L - 1]), kv=(kc, vc))
+    lens = torch.full((Bn,), L - 1, dtype=torch.int32, device="cuda")
+    dec = H.run_decode(sh, wd, xd[:, L - 1].contiguous(), H.ints_to_dev(pos[:, :, L - 1]), kc, vc, lens)
+    torch.cuda.synchronize()
+    ref, st = O.layer_prefill(sh, w, x, pos, return_stages=True)
+    assert H.rel_err(H.np64(dec), H.np64(full[:, L - 1])) <= 2e-2
+    check_layer_out(sh, dec, x[:, L - 1], ref[:, L - 1], f"decode at offset {offset}")
+    check_layer_out(sh, full, x, ref, f"prefill at offset {offset}")
+    assert H.rel_err(H.np64(kc[:, :, L - 1]), st["k"][:, :, L - 1]) <= 2e-2  # decode's rotation
+    assert H.rel_err(H.np64(kf[:, :, L - 1]), st["k"][:, :, L - 1]) <= 2e-2  # prefill's rotation
 
 
 # ------------------------------------------------------------------------------ logits

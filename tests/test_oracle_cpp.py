@@ -60,7 +60,8 @@ def test_positions_bit_exact():
 
 
 @pytest.mark.parametrize("case,code", [("extra pads", O.POS_EXTRA_PADS), ("bad grid", O.POS_BAD_GRID),
-                                       ("span", O.POS_SPAN_MISMATCH), ("unused", O.POS_UNUSED_IMAGES)])
+                                       ("span", O.POS_SPAN_MISMATCH), ("unused", O.POS_UNUSED_IMAGES),
+                                       ("grid past int64", O.POS_SPAN_MISMATCH)])
 def test_position_errors_match(case, code):
     img = W.IMAGE_TOKEN_ID
     tok = np.array([[5, img, img, img, img, 6]], np.int32)
@@ -69,6 +70,8 @@ def test_position_errors_match(case, code):
         off = np.array([0, 0], np.int32)
     elif case == "bad grid":
         grid = np.array([[1, 3, 4]], np.int32)
+    elif case == "grid past int64":  # merged grid 2^21 x 2^21 x 2^22: 2^64 pads
+        grid = np.array([[1 << 21, 1 << 22, 1 << 23]], np.int32)
     elif case == "span":
         tok = np.array([[5, img, img, 7, img, 6]], np.int32)
     else:
