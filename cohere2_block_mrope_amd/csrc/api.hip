@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -41,7 +42,7 @@ struct ProfRec {
   hipEvent_t e0, e1;
 };
 std::mutex g_prof_mu;
-bool g_prof_on = false;
+std::atomic<bool> g_prof_on{false};  // read without the lock on every launch
 std::vector<ProfRec> g_prof;
 std::vector<std::pair<hipEvent_t, hipEvent_t>> g_prof_pool;
 std::vector<std::string> g_prof_names;
@@ -51,8 +52,9 @@ struct KScope {
   hipEvent_t stop = nullptr;
   hipStream_t s;
   KScope(const char* name, hipStream_t st) : s(st) {
+    if (!g_prof_on.load(std::memory_order_relaxed)) return;  // profiling off: no lock, no events
     std::lock_guard<std::mutex> lk(g_prof_mu);
-    if (!g_prof_on || g_prof.size() >= COMPASS_PROFILE_MAX) return;
+    if (!g_prof_on.load(std::memory_order_relaxed) || g_prof.size() >= COMPASS_PROFILE_MAX) return;
     const size_t i = g_prof.size();
     if (i >= g_prof_pool.size()) {
       hipEvent_t a, b;
@@ -712,7 +714,7 @@ int compass_logits_argmax(int32_t R, int32_t D, int32_t V, int32_t dtype, const 
 
 int compass_profile_enable(int on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  g_prof_on = on != 0;
+  g_prof_on.store(on != 0, std::memory_order_relaxed);
   return COMPASS_OK;
 }
 

@@ -180,7 +180,12 @@ int compass_layer_prefill_chunk(const compass_layer_desc *d, const compass_layer
                                 int32_t n_ds, void *out, void *workspace, size_t ws_bytes,
                                 void *stream);
 
-/* One decode step of one layer: one new token per row.
+/* One decode step of one layer: one new token per row. The mlxcel Compass issue defines
+ * it: "Text decoder forward" gives the layer (one shared LayerNorm, the attention and
+ * SwiGLU branches summed into the residual, MRoPE on sliding layers only); the correction
+ * under "Acceptance criteria" keeps a dense cache with the window applied as a mask; and
+ * "Position ids (get_rope_index)" places a generated token at its cache offset plus the
+ * row's rope_delta on all three axes.
  *   x [B, D]; pos [3, B] int32 (lens[b] + rope_delta[b] on every axis; unread for FULL)
  *   kv (required): the new token's K/V are written at index lens[b]; keys
  *   max(0, lens[b] - window + 1) .. lens[b] (sliding) or 0 .. lens[b] (full) are
@@ -254,9 +259,11 @@ int compass_embed(int32_t R, int32_t D, int32_t V, int32_t dtype, const int32_t 
 int compass_decode_positions(int32_t B, int32_t *lens, const int32_t *rope_delta,
                              int32_t advance, int32_t *pos, void *stream);
 
-/* Greedy head: token[r] = the vocabulary id of the largest logit of compass_logits for
- * row r (the same LayerNorm and logits GEMM, so the same fp32 values; the smallest id
- * on ties), max_logit[r] (may be NULL) = that logit.
+/* Greedy head, the step that turns the tied-embedding logits of "Text decoder forward"
+ * (mlxcel Compass issue) into the next token of greedy generation, as in that issue's
+ * "Validation" text-generation check: token[r] = the vocabulary id of the largest logit
+ * of compass_logits for row r (the same LayerNorm and logits GEMM, so the same fp32
+ * values; the smallest id on ties), max_logit[r] (may be NULL) = that logit.
  *   h: R rows of D elements, row r at h + r * ldh (ldh = 0 means D; e.g. ldh = L * D
  *   with h pointing at row L - 1 picks the last token of every [L, D] batch row);
  *   ldh * element size must be a multiple of 16.   token out [R] int32 (device).
