@@ -80,6 +80,9 @@ _sig = {
                                                    ctypes.c_size_t, _P]),
     "compass_layer_decode": (ctypes.c_int, [ctypes.POINTER(compass_layer_desc), ctypes.POINTER(compass_layer_weights),
                                             _I, _P, _P, ctypes.POINTER(compass_kv), _P, _P, ctypes.c_size_t, _P]),
+    "compass_layer_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(compass_layer_desc),
+                                                    ctypes.POINTER(compass_layer_weights), _I, _P, _P,
+                                                    ctypes.POINTER(compass_kv), _P, _P]),
     "compass_layer_decode_q4": (ctypes.c_int, [ctypes.POINTER(compass_layer_desc),
                                                ctypes.POINTER(compass_layer_weights_q4), _I, _P, _P,
                                                ctypes.POINTER(compass_kv), _P, _P, ctypes.c_size_t, _P]),
@@ -205,6 +208,16 @@ def compass_layer_decode(desc, weights: compass_layer_weights, x, pos, kv: compa
     _check(_lib.compass_layer_decode(ctypes.byref(desc), ctypes.byref(weights), B, _ptr(x), _ptr(pos),
                                      ctypes.byref(kv), _ptr(out), _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+COMPASS_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def compass_layer_decode_noalloc(desc, weights: compass_layer_weights, x, pos, kv: compass_kv, out,
+                                 stream=None) -> None:
+    B = x.shape[0]
+    _check(_lib.compass_layer_decode_noalloc(ctypes.byref(desc), ctypes.byref(weights), B, _ptr(x), _ptr(pos),
+                                             ctypes.byref(kv), _ptr(out), _stream(stream)))
 
 
 def compass_layer_decode_q4(desc, weights: compass_layer_weights_q4, x, pos, kv: compass_kv, out, workspace,

@@ -313,6 +313,39 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// ----------------------------------------------------------------- no-allocation scratch
+// Device memory of compass_layer_decode_noalloc: a file-scope device array that each GPU
+// the library runs on holds from the loading of this code object until the process ends.
+// In host code `scratch` names a host-side stand-in, not a device address: it is never
+// passed to a kernel, a copy or a memset. Its device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and kept in g_scratch.
+static __device__ __align__(256) unsigned char scratch[COMPASS_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::vector<std::pair<int, void*>> g_scratch;  // (device, device address of scratch)
+
+int scratch_address(void** p) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(COMPASS_E_DEVICE, "hipGetDevice failed: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  for (const auto& sc : g_scratch)
+    if (sc.first == dev) {
+      *p = sc.second;
+      return COMPASS_OK;
+    }
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || ptr == nullptr)
+    return fail(COMPASS_E_DEVICE, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev,
+                hipGetErrorString(e));
+  if (((uintptr_t)ptr & (kAlign - 1)) != 0)
+    return fail(COMPASS_E_DEVICE, "scratch on device %d is not 256-byte aligned", dev);
+  g_scratch.emplace_back(dev, ptr);
+  *p = ptr;
+  return COMPASS_OK;
+}
+
 }  // namespace
 
 hipError_t compass::ensure_dynamic_lds(const void* kernel, int bytes) {
@@ -476,10 +509,13 @@ int compass_layer_prefill_chunk(const compass_layer_desc* d, const compass_layer
   return prefill_impl(d, w, B, L, x, pos, kv, kv->lens, ds_rows, ds, n_ds, out, workspace, ws_bytes, stream);
 }
 
-// One decode step; the GEMM weights are either bf16/fp32 (w) or 4-bit affine (wq).
+// One decode step; the GEMM weights are either bf16/fp32 (w) or 4-bit affine (wq). With
+// need != NULL the call only validates its arguments (host code, no HIP call) and returns
+// the workspace bytes it would use in *need.
 static int decode_impl(const compass_layer_desc* d, const compass_layer_weights* w,
                        const compass_layer_weights_q4* wq, int32_t B, const void* x, const int32_t* pos,
-                       const compass_kv* kv, void* out, void* workspace, size_t ws_bytes, void* stream) {
+                       const compass_kv* kv, void* out, void* workspace, size_t ws_bytes, void* stream,
+                       size_t* need = nullptr) {
   int rc = check_desc(d);
   if (rc) return rc;
   if (wq) {
@@ -504,6 +540,10 @@ static int decode_impl(const compass_layer_desc* d, const compass_layer_weights*
   if ((long long)B * m.Hkv * kv->capacity * m.hd > (1LL << 40))
     return fail(COMPASS_E_UNSUPPORTED, "kv cache too large");
   const DecodeWs ws = decode_ws(d, B, kv->capacity);
+  if (need) {
+    *need = ws.total;
+    return ok();
+  }
   if (!workspace || ws_bytes < ws.total)
     return fail(COMPASS_E_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, ws.total);
   if (((uintptr_t)workspace & (kAlign - 1)) != 0)
@@ -571,6 +611,23 @@ int compass_layer_decode(const compass_layer_desc* d, const compass_layer_weight
                          void* workspace, size_t ws_bytes, void* stream) {
   if (!w) return fail(COMPASS_E_INVALID, "weights struct is NULL");
   return decode_impl(d, w, nullptr, B, x, pos, kv, out, workspace, ws_bytes, stream);
+}
+
+int compass_layer_decode_noalloc(const compass_layer_desc* d, const compass_layer_weights* w, int32_t B,
+                                 const void* x, const int32_t* pos, const compass_kv* kv, void* out,
+                                 void* stream) {
+  if (!w) return fail(COMPASS_E_INVALID, "weights struct is NULL");
+  size_t need = 0;
+  int rc = decode_impl(d, w, nullptr, B, x, pos, kv, out, nullptr, 0, stream, &need);
+  if (rc) return rc;
+  if (need > (size_t)COMPASS_NOALLOC_SCRATCH_BYTES)
+    return fail(COMPASS_E_WORKSPACE,
+                "decode of B=%d over capacity %d needs %zu bytes of scratch, above the no-allocation "
+                "maximum of %zu bytes (use compass_layer_decode with a caller workspace)",
+                B, kv->capacity, need, (size_t)COMPASS_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws))) return rc;
+  return decode_impl(d, w, nullptr, B, x, pos, kv, out, ws, (size_t)COMPASS_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int compass_layer_decode_q4(const compass_layer_desc* d, const compass_layer_weights_q4* w, int32_t B,

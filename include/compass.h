@@ -197,6 +197,24 @@ int compass_layer_decode(const compass_layer_desc *d, const compass_layer_weight
                          int32_t B, const void *x, const int32_t *pos, const compass_kv *kv,
                          void *out, void *workspace, size_t ws_bytes, void *stream);
 
+/* Decode without allocation, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. It is
+ * compass_layer_decode (same arguments, kernels, outputs and errors) with the workspace
+ * taken from a device array of COMPASS_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on until the process ends; the call allocates and frees nothing.
+ * The first call on a device looks up that device's array (make that first call outside
+ * any graph capture). The decode step needs no workspace byte to start at zero.
+ * A step whose workspace (compass_workspace_size(d, B, 1, kv->capacity, 1)) exceeds
+ * COMPASS_NOALLOC_SCRATCH_BYTES returns COMPASS_E_WORKSPACE before any launch; at the
+ * Compass widths (hidden 2048, 16/4 heads, head_dim 128, I 8192) and B = 64 that allows
+ * a full-attention layer a capacity of about 22,000 keys. Every call on one GPU shares
+ * that GPU's array and it keeps the last call's contents: calls that overlap on one GPU
+ * (on different streams or threads) race and must be serialized by the caller. */
+#define COMPASS_NOALLOC_SCRATCH_BYTES (64u << 20)
+int compass_layer_decode_noalloc(const compass_layer_desc *d, const compass_layer_weights *w,
+                                 int32_t B, const void *x, const int32_t *pos,
+                                 const compass_kv *kv, void *out, void *stream);
+
 /* 4-bit affine weights: the quantization block of the 4-bit checkpoint in the mlxcel
  * Compass issue's config section (group size 64, 4 bits, affine mode). For a matrix of
  * [rows, cols] (cols a multiple of 64):

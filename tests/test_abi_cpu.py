@@ -253,3 +253,22 @@ def test_q4_decode_argument_errors(b):
     with pytest.raises(b.CompassError) as e:  # workspace too small
         b.compass_layer_decode_q4(compass_shape(b), wq4(), x, pos, kv, out, FakePtr(0x400000, n=64), stream=0)
     assert e.value.code == b.COMPASS_E_WORKSPACE
+
+
+def test_noalloc_decode_checks_before_any_launch(b):
+    """The no-allocation decode validates like compass_layer_decode and rejects a step whose
+    workspace exceeds the scratch, all before any HIP call."""
+    d = compass_shape(b, kind=b.COMPASS_FULL, window=0)
+    x = FakePtr(0x100000, shape=(64, 2048))
+    kv = b.compass_kv()
+    kv.k, kv.v, kv.lens, kv.capacity = 0x500000, 0x600000, 0x700000, 1 << 16
+    assert b.compass_workspace_size(d, 64, 1, 1 << 16, 1) > b.COMPASS_NOALLOC_SCRATCH_BYTES
+    with pytest.raises(b.CompassError) as e:
+        b.compass_layer_decode_noalloc(d, weights(b), x, None, kv, FakePtr(0x300000), stream=0)
+    assert e.value.code == b.COMPASS_E_WORKSPACE and "no-allocation maximum" in b.compass_last_error()
+    with pytest.raises(b.CompassError) as e:
+        b.compass_layer_decode_noalloc(d, weights(b, 0x10004), x, None, kv, FakePtr(0x300000), stream=0)
+    assert e.value.code == b.COMPASS_E_ALIGN
+    with pytest.raises(b.CompassError) as e:
+        b.compass_layer_decode_noalloc(d, weights(b), x, None, b.compass_kv(), FakePtr(0x300000), stream=0)
+    assert e.value.code == b.COMPASS_E_INVALID
