@@ -445,6 +445,52 @@ def layer_prefill_chunk(shape, w: Dict[str, np.ndarray], x: np.ndarray, pos: Opt
 
 
 # ----------------------------------------------------------------------------------------
+# Varlen prefill. Page 5 ("How it fits together") plans prefill per request, each with its own
+# MRoPE positions and its own prefix cache; page 1 ("Validation") requires prefill to stay
+# causal within a sequence. Packed rows [cu[s], cu[s+1]) are sequence s, a chunk continuing
+# that sequence's dense cache at start[s] (0 when no cache is kept); sequences never see one
+# another's keys. A sequence whose chunk does not fit its cache produces nothing.
+# ----------------------------------------------------------------------------------------
+def layer_prefill_varlen(shape, w: Dict[str, np.ndarray], x: np.ndarray, pos: Optional[np.ndarray],
+                         cu_seqlens: Sequence[int], k_cache: Optional[np.ndarray] = None,
+                         v_cache: Optional[np.ndarray] = None, start: Optional[Sequence[int]] = None):
+    """x [T, D] packed rows; pos [3, T] (sliding layers); cu_seqlens [n_seq + 1] with
+    cu[0] = 0 <= cu[1] <= ... <= cu[n_seq] = T; caches [n_seq, Hkv, cap, hd] holding at least
+    start[s] tokens of sequence s (read only here), or None with start None.
+
+    Returns (out [T, D], k_new, v_new): k_new / v_new are lists with [Hkv, len_s, hd] per
+    sequence. Rows of a sequence whose chunk does not fit its cache come back as NaN."""
+    x = np.asarray(x, dtype=F64)
+    T, D = x.shape
+    cu = [int(c) for c in cu_seqlens]
+    if cu[0] != 0 or cu[-1] != T or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError(f"cu_seqlens {cu} do not partition {T} rows")
+    Hkv, hd = shape.n_kv_heads, shape.head_dim
+    out = np.full((T, D), np.nan)
+    k_new, v_new = [], []
+    for sq in range(len(cu) - 1):
+        lo, hi = cu[sq], cu[sq + 1]
+        n = hi - lo
+        s0 = 0 if start is None else int(start[sq])
+        if k_cache is None:
+            kc = np.zeros((1, Hkv, 0, hd))
+            vc = np.zeros((1, Hkv, 0, hd))
+        else:
+            if s0 < 0 or s0 + n > k_cache.shape[2]:
+                k_new.append(None); v_new.append(None)
+                continue
+            kc, vc = k_cache[sq:sq + 1], v_cache[sq:sq + 1]
+        if n == 0:
+            k_new.append(np.zeros((Hkv, 0, hd))); v_new.append(np.zeros((Hkv, 0, hd)))
+            continue
+        p = None if pos is None else np.asarray(pos)[:, None, lo:hi]
+        o, kn, vn = layer_prefill_chunk(shape, w, x[None, lo:hi], p, kc, vc, np.array([s0]))
+        out[lo:hi] = o[0]
+        k_new.append(kn[0]); v_new.append(vn[0])
+    return out, k_new, v_new
+
+
+# ----------------------------------------------------------------------------------------
 # Logits. Page 1, "Text decoder forward": h = LayerNorm(h); logits = embed.as_linear(h) *
 # logit_scale. Page 2 ("Cohere2 Command R"): the scale is an in-place fp32 multiply.
 # ----------------------------------------------------------------------------------------

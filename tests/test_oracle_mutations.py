@@ -121,6 +121,22 @@ def _chunk_start_off_by_one(shape, w, x, pos, k_cache, v_cache, start):
     return _orig_chunk(shape, w, x, pos, k_cache, v_cache, np.maximum(np.asarray(start) - 1, 0))
 
 
+_orig_varlen = O.layer_prefill_varlen
+
+
+def _varlen_sequences_see_each_other(shape, w, x, pos, cu_seqlens, k_cache=None, v_cache=None, start=None):
+    """The packed batch treated as one long row."""
+    if k_cache is not None:
+        return _orig_varlen(shape, w, x, pos, cu_seqlens, k_cache, v_cache, start)
+    T = np.asarray(x).shape[0]
+    return _orig_varlen(shape, w, x, pos, [0, T], None, None, None)[0], None, None
+
+
+def _varlen_start_ignored(shape, w, x, pos, cu_seqlens, k_cache=None, v_cache=None, start=None):
+    return _orig_varlen(shape, w, x, pos, cu_seqlens, k_cache, v_cache,
+                        None if start is None else np.zeros(len(start), dtype=np.int64))
+
+
 _orig_embed = O.embed
 _orig_greedy = O.greedy_token
 
@@ -208,6 +224,8 @@ MUTANTS = {
         "layer_prefill_rows", ("int(rows.min()) - shape.window + 1", "int(rows.min()) - shape.window + 2"))),
     "row sampler keys not offset by the span start": ("layer_prefill_rows", _edited(
         "layer_prefill_rows", ("k_index=span)", "k_index=span - lo)"))),
+    "varlen sequences see each other": ("layer_prefill_varlen", _varlen_sequences_see_each_other),
+    "varlen cache start ignored": ("layer_prefill_varlen", _varlen_start_ignored),
     "deepstack after every layer": ("stack_prefill", _edited(
         "stack_prefill", ("i < 3 and i < len(ds)", "i < len(ds)"))),
 }
@@ -246,6 +264,9 @@ PINS = [
     lambda: P.test_layer_prefill_rows_equals_whole_prefill("sliding", 3, 1, 0, [0, 1, 5, 9, 16]),
     lambda: P.test_layer_prefill_rows_equals_whole_prefill("sliding", 3, 2, 1, [16, 2, 9, 6]),
     lambda: P.test_layer_prefill_rows_equals_whole_prefill("sliding", 3, 1, 0, [3, 4, 11, 12]),
+    P.test_varlen_equal_lengths_equals_batched_prefill,
+    lambda: P.test_varlen_each_sequence_is_its_own_prefill("sliding", 3),
+    P.test_varlen_continues_each_sequence_cache,
 ]
 
 

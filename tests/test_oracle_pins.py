@@ -474,6 +474,80 @@ def test_chunked_prefill_equals_one_prefill(kind, W):
     np.testing.assert_allclose(vnew, np.stack(ref_v), atol=1e-12)
 
 
+def test_varlen_equal_lengths_equals_batched_prefill():
+    """Packed sequences of equal length L are the rows of one [B, L] prefill."""
+    for kind, W in (("sliding", 3), ("full", 0)):
+        sh = tiny_shape(kind, W)
+        w = rand_weights(sh, seed=80)
+        B, L = 3, 6
+        x = np.random.default_rng(81).standard_normal((B, L, sh.hidden))
+        pos = mixed_pos(B, L, seed=82)
+        ref, st = O.layer_prefill(sh, w, x, pos, return_stages=True)
+        out, kn, vn = O.layer_prefill_varlen(sh, w, x.reshape(B * L, -1), pos.reshape(3, B * L),
+                                             [0, L, 2 * L, 3 * L])
+        np.testing.assert_allclose(out, ref.reshape(B * L, -1), atol=1e-12)
+        for b in range(B):
+            np.testing.assert_allclose(kn[b], st["k"][b], atol=1e-12)
+            np.testing.assert_allclose(vn[b], st["v"][b], atol=1e-12)
+
+
+@pytest.mark.parametrize("kind,W", [("sliding", 3), ("sliding", 1), ("full", 0)])
+def test_varlen_each_sequence_is_its_own_prefill(kind, W):
+    """Ragged packed sequences (one empty, one of a single token) each equal the prefill of
+    that sequence alone: no key crosses a sequence boundary."""
+    sh = tiny_shape(kind, W)
+    w = rand_weights(sh, seed=83)
+    lens = [5, 1, 0, 9, 3]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1])
+    x = np.random.default_rng(84).standard_normal((T, sh.hidden))
+    pos = np.random.default_rng(85).integers(0, 50, size=(3, T))
+    out, kn, _ = O.layer_prefill_varlen(sh, w, x, pos, cu)
+    for s_, n in enumerate(lens):
+        lo = int(cu[s_])
+        if n == 0:
+            assert kn[s_].shape[1] == 0
+            continue
+        ref, st = O.layer_prefill(sh, w, x[None, lo:lo + n], pos[:, None, lo:lo + n], return_stages=True)
+        np.testing.assert_allclose(out[lo:lo + n], ref[0], atol=1e-12)
+        np.testing.assert_allclose(kn[s_], st["k"][0], atol=1e-12)
+
+
+def test_varlen_continues_each_sequence_cache():
+    """With caches, sequence s continues its own cache at start[s]: its rows and new K/V are
+    the tail of one prefill of that sequence's prefix + chunk; a sequence whose chunk does not
+    fit its cache yields NaN rows and no K/V."""
+    sh = tiny_shape("sliding", 4)
+    w = rand_weights(sh, seed=86)
+    lens, starts, cap = [4, 2, 6, 3], [0, 5, 3, 9], 11
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1])
+    full_len = max(a + b for a, b in zip(lens, starts))
+    xr = np.random.default_rng(87).standard_normal((len(lens), full_len, sh.hidden))
+    posr = mixed_pos(len(lens), full_len, seed=88)
+    kc = np.full((len(lens), sh.n_kv_heads, cap, sh.head_dim), np.nan)
+    vc = np.full_like(kc, np.nan)
+    x = np.empty((T, sh.hidden))
+    pos = np.empty((3, T), np.int64)
+    refs = []
+    for s_, (n, s0) in enumerate(zip(lens, starts)):
+        full, st = O.layer_prefill(sh, w, xr[s_:s_ + 1, :s0 + n], posr[:, s_:s_ + 1, :s0 + n], return_stages=True)
+        kc[s_, :, :s0], vc[s_, :, :s0] = st["k"][0][:, :s0], st["v"][0][:, :s0]
+        x[cu[s_]:cu[s_ + 1]] = xr[s_, s0:s0 + n]
+        pos[:, cu[s_]:cu[s_ + 1]] = posr[:, s_, s0:s0 + n]
+        refs.append((full[0, s0:], st["k"][0][:, s0:]))
+    out, kn, _ = O.layer_prefill_varlen(sh, w, x, pos, cu, kc, vc, starts)
+    for s_, (n, s0) in enumerate(zip(lens, starts)):
+        rows = out[cu[s_]:cu[s_ + 1]]
+        if s0 + n > cap:
+            assert np.all(np.isnan(rows)) and kn[s_] is None
+            continue
+        np.testing.assert_allclose(rows, refs[s_][0], atol=1e-11)
+        np.testing.assert_allclose(kn[s_], refs[s_][1], atol=1e-12)
+    with pytest.raises(ValueError):
+        O.layer_prefill_varlen(sh, w, x, pos, [0, 3, 2, T])
+
+
 def test_one_token_chunk_equals_decode():
     for kind, W in (("sliding", 4), ("full", 0)):
         sh = tiny_shape(kind, W)
