@@ -16,8 +16,10 @@ GEMM): algorithmic flops per launch / its mean launch time from HIP events recor
 around every launch while the timed steps are repeated (the throughput itself is timed
 without the events). "traffic" is its HBM bytes per launch from committed rocprofv3
 counter passes (profiles/gemm_proj_sliding_prefill_traffic.json) while they match the current kernel
-sources. "cpu_baseline" is the fp64 oracle timed on this host on one full layer of the
-same workload.
+sources. "cpu_baseline" is the plain fp32 C++ oracle (OpenMP) timed on this host on one
+whole layer of the same workload, with the host's CPU model, nproc and the threads used,
+and the fp64 numpy oracle on that layer as a second figure. "extra" also holds the tiny
+fp32 layer (hidden 256, L = 128) on the GPU and on the C++ oracle.
 """
 from __future__ import annotations
 
@@ -43,7 +45,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-extra", action="store_true", help="headline workload only")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--only", default=None, help="run one workload: sliding_prefill|full_prefill|decode_stack|stack_logits|chunked_prefill (for profiling)")
+    p.add_argument("--only", default=None, help="run one workload: sliding_prefill|tiny_f32|full_prefill|decode_stack|stack_logits|chunked_prefill|varlen_prefill (for profiling)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run plain 512 MiB copies (reference launches for the HBM byte counters)")
     return p.parse_args()
@@ -336,24 +338,119 @@ def run_chunked_prefill(args, b, H, W, torch):
             "kernels_us": {k: round(v["mean_us"], 1) for k, v in stats.items()}}
 
 
+def run_varlen_prefill(args, b, H, W, torch):
+    """Varlen prefill of the sliding layer (headline widths, window 1024): 8 sequences of
+    1536, 1024, 512, 384, 256, 200, 128 and 56 tokens (4096 in all, text positions per
+    sequence) packed into one launch, each written to its own cache."""
+    sh, w, _, _, _, _ = setup_sliding_prefill(H, W, torch)
+    lens = [1536, 1024, 512, 384, 256, 200, 128, 56]
+    T = sum(lens)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda")
+    pos = torch.from_numpy(np.concatenate([np.broadcast_to(np.arange(n), (3, n)) for n in lens], axis=1)
+                           .astype(np.int32)).cuda()
+    import synth.rng_torch as RT
+    x = RT.normal(W.stream_seed(W.Stream.SLIDING_PREFILL, 1, W.TensorId.X), T * sh.hidden).to(torch.bfloat16).view(T, sh.hidden)
+    wd = H.weights_to_dev(sh, w)
+    d = H.desc(sh)
+    kc = torch.empty((len(lens), sh.n_kv_heads, max(lens), sh.head_dim), dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty_like(kc)
+    kv = b.make_kv(kc, vc)
+    ws = H.workspace(b.compass_varlen_workspace_size(d, len(lens), T))
+    out = torch.empty_like(x)
+    status = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    wts = b.make_weights(wd)
+    step = lambda: b.compass_layer_prefill_varlen(d, wts, cu, x, pos, kv, None, None, out, status, ws)
+    sec, stats = timed(step, args.steps, args.warmup, b, torch)
+    assert int(status.item()) == 0
+    return {"workload": f"varlen prefill, sliding layer (headline widths, window 1024): {len(lens)} sequences "
+                        f"of {lens} tokens packed into {T} rows, one launch per kernel, caches written",
+            "ms_per_step": 1e3 * sec, "tokens_per_s_per_layer": T / sec,
+            "kernels_us": {k: round(v["mean_us"], 1) for k, v in stats.items()}}
+
+
+def cpu_info():
+    """The host CPU's model string and the core count nproc reports."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count(), len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(sh, w, x, tok, grid, off):
-    """The fp64 oracle (test infrastructure) timed on this host: the only use of oracle/ here."""
+    """The oracles (test infrastructure) timed on this host: the only use of oracle/ here.
+
+    The figure is the plain fp32 C++ oracle (OpenMP over rows, queries and heads, as
+    many threads as OMP_NUM_THREADS allows) on one whole layer of the headline workload,
+    positions included. The fp64 numpy oracle on the same layer is a second figure."""
     import threadpoolctl
     from oracle import compass_oracle as O
-    info = threadpoolctl.threadpool_info()
-    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    from oracle import ref as R
     from synth.workloads import IMAGE_TOKEN_ID
-    # Whole passes (positions + layer) until at least 10 s have run, at most 8.
-    runs, t0 = 0, time.perf_counter()
-    while runs < 8 and (runs == 0 or time.perf_counter() - t0 < 10.0):
-        pos, _ = O.mrope_positions(tok, IMAGE_TOKEN_ID, grid, off, 2)
-        O.layer_prefill(sh, w, x, pos)
-        runs += 1
-    sec = time.perf_counter() - t0
+    model, ncpu, naff = cpu_info()
     L = x.shape[1]
-    return {"value": runs * L / sec, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{runs} full sliding-layer prefills of the headline workload ({L} tokens each, positions + "
-                      f"layer) in fp64 numpy on {threads} BLAS threads, {sec:.1f} s"}
+    threads = R.num_threads()
+    t0 = time.perf_counter()
+    code, pos, _ = R.mrope_positions(tok, IMAGE_TOKEN_ID, grid, off, 2)
+    R.layer_forward(sh, w, x, pos)
+    sec = time.perf_counter() - t0
+    assert code == 0
+    info = threadpoolctl.threadpool_info()
+    blas = max([i.get("num_threads", 1) for i in info] or [1])
+    t1 = time.perf_counter()
+    pos64, _ = O.mrope_positions(tok, IMAGE_TOKEN_ID, grid, off, 2)
+    O.layer_prefill(sh, w, x, pos64)
+    sec64 = time.perf_counter() - t1
+    return {"value": L / sec, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"one whole sliding-layer prefill of the headline workload ({L} tokens, positions + layer) "
+                      f"by the plain fp32 C++ oracle (double accumulation) on {threads} OpenMP threads: {sec:.1f} s",
+            "cpu_model": model, "nproc": ncpu, "affinity_cpus": naff,
+            "numpy_fp64": {"value": L / sec64, "unit": "tokens/s", "blas_threads": blas,
+                           "sample": f"the same layer by the fp64 numpy oracle: {sec64:.1f} s"}}
+
+
+def run_tiny_f32(args, b, H, W, torch):
+    """The fp32 parity workload (hidden 256, 4/1 heads, hd 64, I 1024, window 32, MRoPE [12, 10, 10],
+    128 text tokens): positions + one fp32 layer on the GPU, and the C++ oracle on the same layer."""
+    from synth.workloads import WORKLOADS
+    cfg = WORKLOADS["tiny_sliding_f32"]
+    sh, L = cfg["shape"], cfg["L"]
+    w = W.make_layer_weights(sh, W.Stream.TINY_SLIDING_F32, 0)
+    x = W.make_layer_input(sh, W.Stream.TINY_SLIDING_F32, L).reshape(1, L, sh.hidden)
+    tok = W.text_tokens(W.stream_seed(W.Stream.TINY_SLIDING_F32, 0, W.TensorId.TOKENS), L).reshape(1, L)
+    grid, off = np.zeros((1, 3), np.int32), np.zeros(2, np.int32)
+    wd, xd = H.weights_to_dev(sh, w), H.to_dev(x, torch.float32)
+    tokd, gridd, offd = H.ints_to_dev(tok), H.ints_to_dev(grid), H.ints_to_dev(off)
+    pos = torch.empty((3, 1, L), dtype=torch.int32, device="cuda")
+    delta = torch.empty((1,), dtype=torch.int32, device="cuda")
+    status = torch.empty((1,), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(xd)
+    d = H.desc(sh)
+    ws = H.workspace(b.compass_workspace_size(d, 1, L, 0, 0))
+    wts = b.make_weights(wd)
+
+    def step():
+        b.compass_mrope_positions(tokd, W.IMAGE_TOKEN_ID, gridd, offd, 2, pos, delta, status)
+        b.compass_layer_prefill(d, wts, xd, pos, None, None, None, out, ws)
+
+    sec, stats = timed(step, max(20, args.steps), 5, b, torch)
+    assert int(status.item()) == 0
+    res = {"workload": cfg["name"], "us_per_step": 1e6 * sec, "tokens_per_s_per_layer": L / sec,
+           "kernels_us": {k: round(v["mean_us"], 1) for k, v in stats.items()}}
+    if not args.no_cpu:
+        from oracle import ref as R
+        p = np.arange(L)
+        t0 = time.perf_counter()
+        for _ in range(3):
+            R.layer_forward(sh, w, x, np.stack([p, p, p])[:, None, :])
+        res["cpu_oracle_us_per_layer"] = 1e6 * (time.perf_counter() - t0) / 3
+        res["cpu_oracle_threads"] = R.num_threads()
+    return res
 
 
 GEMM_SOURCES = ["gemm_bf16.hip", "gemm_common.h", "common.h", "launch.h"]
@@ -441,7 +538,9 @@ def main():
     else:
         line = None
     if not args.no_extra:
-        for key, fn in (("full_prefill", run_full_prefill), ("decode_stack", run_decode_stack), ("stack_logits", run_stack_logits), ("chunked_prefill", run_chunked_prefill)):
+        for key, fn in (("tiny_f32", run_tiny_f32), ("full_prefill", run_full_prefill),
+                        ("decode_stack", run_decode_stack), ("stack_logits", run_stack_logits),
+                        ("chunked_prefill", run_chunked_prefill), ("varlen_prefill", run_varlen_prefill)):
             if args.only in (None, key):
                 log(f"{key}: running")
                 res_extra[key] = fn(args, b, H, W, torch)

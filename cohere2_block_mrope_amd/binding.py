@@ -78,6 +78,11 @@ _sig = {
                                                    ctypes.POINTER(compass_layer_weights), _I, _I, _P, _P,
                                                    ctypes.POINTER(compass_kv), _P, _P, _I, _P, _P,
                                                    ctypes.c_size_t, _P]),
+    "compass_varlen_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(compass_layer_desc), _I, _I]),
+    "compass_layer_prefill_varlen": (ctypes.c_int, [ctypes.POINTER(compass_layer_desc),
+                                                    ctypes.POINTER(compass_layer_weights), _I, _I, _P, _P, _P,
+                                                    ctypes.POINTER(compass_kv), _P, _P, _I, _P, _P, _P,
+                                                    ctypes.c_size_t, _P]),
     "compass_layer_decode": (ctypes.c_int, [ctypes.POINTER(compass_layer_desc), ctypes.POINTER(compass_layer_weights),
                                             _I, _P, _P, ctypes.POINTER(compass_kv), _P, _P, ctypes.c_size_t, _P]),
     "compass_layer_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(compass_layer_desc),
@@ -200,6 +205,22 @@ def compass_layer_prefill_chunk(desc, weights: compass_layer_weights, x, pos, kv
                                             ctypes.byref(kv), _ptr(ds_rows), _ptr(ds), n_ds, _ptr(out),
                                             _ptr(workspace), workspace.numel() * workspace.element_size(),
                                             _stream(stream)))
+
+
+def compass_varlen_workspace_size(desc, n_seq: int, T: int) -> int:
+    return int(_lib.compass_varlen_workspace_size(ctypes.byref(desc), n_seq, T))
+
+
+def compass_layer_prefill_varlen(desc, weights: compass_layer_weights, cu_seqlens, x, pos, kv: Optional[compass_kv],
+                                 ds_rows, ds, out, status, workspace, stream=None) -> None:
+    """x [T, D] packed rows; cu_seqlens int32 [n_seq + 1] on the device."""
+    T = x.shape[0]
+    n_seq = cu_seqlens.shape[0] - 1
+    n_ds = 0 if ds_rows is None else int(ds_rows.numel())
+    _check(_lib.compass_layer_prefill_varlen(ctypes.byref(desc), ctypes.byref(weights), n_seq, T, _ptr(cu_seqlens),
+                                             _ptr(x), _ptr(pos), None if kv is None else ctypes.byref(kv),
+                                             _ptr(ds_rows), _ptr(ds), n_ds, _ptr(out), _ptr(status), _ptr(workspace),
+                                             workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def compass_layer_decode(desc, weights: compass_layer_weights, x, pos, kv: compass_kv, out, workspace,

@@ -179,9 +179,11 @@ Dims dims(const compass_layer_desc* d) {
 }
 
 struct PrefillWs {
-  size_t a, q, kc, vc, a2, raw, total;
+  size_t a, q, kc, vc, a2, raw, row_seq, tiles, n_tiles, total;
+  int max_tiles;
 };
-PrefillWs prefill_ws(const compass_layer_desc* d, long long B, long long L) {
+// Varlen prefill (n_seq > 0): B = 1, L = T packed rows, plus the plan's buffers.
+PrefillWs prefill_ws(const compass_layer_desc* d, long long B, long long L, long long n_seq = 0) {
   const Dims m = dims(d);
   const long long T = B * L;
   PrefillWs w;
@@ -196,6 +198,15 @@ PrefillWs prefill_ws(const compass_layer_desc* d, long long B, long long L) {
   else {
     const int so = gemm_bf16_resid_splits((int)T, (int)m.D, (int)m.K2);  // split-K output partials
     if (so > 1) off += up((long long)so * T * m.D * 4);
+  }
+  w.max_tiles = 0;
+  w.row_seq = w.tiles = w.n_tiles = off;
+  if (n_seq > 0) {
+    const int tr = varlen_tile_rows(d->dtype);
+    w.max_tiles = tr > 0 ? (int)((T + tr - 1) / tr + n_seq) : 0;
+    w.row_seq = off; off += up(T * 4);
+    w.tiles = off; off += up((long long)2 * w.max_tiles * 4 + 4);
+    w.n_tiles = off; off += up(4);
   }
   w.total = off;
   return w;
@@ -395,16 +406,34 @@ size_t compass_workspace_size(const compass_layer_desc* d, int32_t B, int32_t L,
   return prefill_ws(d, B, L).total;
 }
 
+// Varlen prefill: n_seq packed sequences with device offsets cu; status (device, may be
+// NULL) receives the plan's status bits.
+struct VarlenArgs {
+  int n_seq;
+  const int32_t* cu;
+  int32_t* status;
+};
+
 // Prefill of a [B, L] chunk. start == NULL: plain prefill (K/V at cache rows [0, L) when a
-// cache is given); start = kv->lens: the chunk continues the cache of each row.
+// cache is given); start = kv->lens: the chunk continues the cache of each row. With va,
+// B = 1 and L = T packed rows of va->n_seq sequences; start (may be NULL) then holds the
+// tokens already cached per sequence.
 static int prefill_impl(const compass_layer_desc* d, const compass_layer_weights* w, int32_t B,
                         int32_t L, const void* x, const int32_t* pos, const compass_kv* kv,
                         const int32_t* start, const int32_t* ds_rows, const void* ds, int32_t n_ds,
-                        void* out, void* workspace, size_t ws_bytes, void* stream) {
+                        void* out, void* workspace, size_t ws_bytes, void* stream,
+                        const VarlenArgs* va = nullptr) {
   int rc = check_desc(d);
   if (rc) return rc;
   if ((rc = check_weights(w))) return rc;
   if (B < 1 || L < 1) return fail(COMPASS_E_INVALID, "B=%d, L=%d must be >= 1", B, L);
+  if (va) {
+    if (va->n_seq < 1 || va->n_seq > kVarlenMaxSeqs)
+      return fail(COMPASS_E_UNSUPPORTED, "n_seq=%d must be in [1, %d]", va->n_seq, kVarlenMaxSeqs);
+    if (L > kVarlenMaxTokens)
+      return fail(COMPASS_E_UNSUPPORTED, "T=%d packed rows exceed %d", L, kVarlenMaxTokens);
+    if (!va->cu) return fail(COMPASS_E_INVALID, "cu_seqlens is NULL");
+  }
   const Dims m = dims(d);
   const long long T = (long long)B * L;
   if (T * (m.K2 > m.Nv ? m.K2 : m.Nv) > (1LL << 31) - 1 || T > (1LL << 31) - 1)
@@ -419,7 +448,8 @@ static int prefill_impl(const compass_layer_desc* d, const compass_layer_weights
   if (kv) {
     if (!kv->k || !kv->v) return fail(COMPASS_E_INVALID, "kv->k or kv->v is NULL");
     if (!aligned16(kv->k) || !aligned16(kv->v)) return fail(COMPASS_E_ALIGN, "kv not 16-byte aligned");
-    if (kv->capacity < L) return fail(COMPASS_E_INVALID, "kv capacity %d < L=%d", kv->capacity, L);
+    if (va ? kv->capacity < 1 : kv->capacity < L)
+      return fail(COMPASS_E_INVALID, "kv capacity %d < %d", kv->capacity, va ? 1 : L);
     // The attention kernels address one (row, kv head) slice of the cache with 32-bit byte
     // offsets.
     if ((long long)kv->capacity * m.hd * m.esz > (1LL << 31) - 1)
@@ -431,13 +461,22 @@ static int prefill_impl(const compass_layer_desc* d, const compass_layer_weights
     if (!ds_rows || !ds) return fail(COMPASS_E_INVALID, "deepstack pointers NULL with n_ds > 0");
     if (!aligned16(ds)) return fail(COMPASS_E_ALIGN, "ds not 16-byte aligned");
   }
-  const PrefillWs ws = prefill_ws(d, B, L);
+  const PrefillWs ws = prefill_ws(d, B, L, va ? va->n_seq : 0);
   if (!workspace || ws_bytes < ws.total)
     return fail(COMPASS_E_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, ws.total);
   if (((uintptr_t)workspace & (kAlign - 1)) != 0)
     return fail(COMPASS_E_ALIGN, "workspace not 256-byte aligned");
 
   char* wsb = (char*)workspace;
+  VarlenPlan plan{};
+  if (va) {
+    plan.cu = va->cu;
+    plan.n_seq = va->n_seq;
+    plan.row_seq = (int32_t*)(wsb + ws.row_seq);
+    plan.tiles = (int32_t*)(wsb + ws.tiles);
+    plan.n_tiles = (int32_t*)(wsb + ws.n_tiles);
+    plan.max_tiles = ws.max_tiles;
+  }
   void* a = wsb + ws.a;
   void* q = wsb + ws.q;
   void* kc = kv ? kv->k : (void*)(wsb + ws.kc);
@@ -459,14 +498,20 @@ static int prefill_impl(const compass_layer_desc* d, const compass_layer_weights
   ep.kc = kc; ep.vc = vc; ep.cap = cap;
   ep.lens = nullptr;
   ep.kv_start = start;
+  ep.row_seq = va ? plan.row_seq : nullptr;
+  ep.cu = va ? va->cu : nullptr;
+  ep.kv_by_seq = (va && kv) ? 1 : 0;
   ep.act = a2; ep.ldact = (int)m.K2; ep.act_col0 = (int)m.qd;
   ep.nq64 = (int)(m.qd / 64); ep.nk64 = (int)(m.Hkv * m.hd / 64);
   ep.I = (int)m.I;
   const RopeTable rt = rope_table(d);
   const BMap pb = proj_bmap(d, w), ob = out_bmap(d, w);
-  const RowStart rs{start, L, cap};
+  const RowStart rs{va ? nullptr : start, L, cap, va ? plan.row_seq : nullptr};
 
   (void)hipGetLastError();
+  if (va)
+    LAUNCH("varlen_plan", s, launch_varlen_plan(plan, L, start, kv ? kv->capacity : 0,
+                                                varlen_tile_rows(dt), va->status, s));
   LAUNCH("layernorm", s, launch_layernorm(dt, x, w->ln_w, d->ln_eps, a, (int)T, (int)m.D, s));
   if (dt == COMPASS_BF16) {
     LAUNCH("gemm_proj", s, launch_gemm_bf16_proj(a, (int)m.D, (int)T, (int)m.D, pb, (int)m.Nv, ep, rt, s));
@@ -474,8 +519,13 @@ static int prefill_impl(const compass_layer_desc* d, const compass_layer_weights
     LAUNCH("gemm_proj_f32", s, launch_gemm_f32_raw(a, (int)m.D, (int)T, (int)m.D, pb, (int)m.Nv, 1, raw, 1.f, s));
     LAUNCH("proj_epilogue", s, launch_proj_epilogue(dt, raw, 1, (int)T, (int)m.Nv, ep, rt, s));
   }
-  LAUNCH("attn_prefill", s, launch_attention_prefill(dt, q, kc, vc, B, (int)m.Hq, (int)m.Hkv, L, cap,
-                                                     (int)m.hd, sliding, d->window, start, a2, (int)m.K2, s));
+  if (va)
+    LAUNCH("attn_prefill", s, launch_attention_prefill_varlen(dt, q, kc, vc, L, (int)m.Hq, (int)m.Hkv, cap,
+                                                              (int)m.hd, sliding, d->window, start, kv ? 1 : 0,
+                                                              plan, a2, (int)m.K2, s));
+  else
+    LAUNCH("attn_prefill", s, launch_attention_prefill(dt, q, kc, vc, B, (int)m.Hq, (int)m.Hkv, L, cap,
+                                                       (int)m.hd, sliding, d->window, start, a2, (int)m.K2, s));
   if (dt == COMPASS_BF16) {
     const int so = gemm_bf16_resid_splits((int)T, (int)m.D, (int)m.K2);
     if (so > 1) {  // too few output tiles to fill the CUs: split K, then reduce with the residual
@@ -507,6 +557,21 @@ int compass_layer_prefill_chunk(const compass_layer_desc* d, const compass_layer
                                 void* workspace, size_t ws_bytes, void* stream) {
   if (!kv || !kv->lens) return fail(COMPASS_E_INVALID, "chunked prefill needs kv with lens (tokens already cached)");
   return prefill_impl(d, w, B, L, x, pos, kv, kv->lens, ds_rows, ds, n_ds, out, workspace, ws_bytes, stream);
+}
+
+size_t compass_varlen_workspace_size(const compass_layer_desc* d, int32_t n_seq, int32_t T) {
+  const std::string saved = g_err;
+  if (check_desc(d) != COMPASS_OK || n_seq < 1 || T < 1) { g_err = saved; return 0; }
+  return prefill_ws(d, 1, T, n_seq).total;
+}
+
+int compass_layer_prefill_varlen(const compass_layer_desc* d, const compass_layer_weights* w, int32_t n_seq,
+                                 int32_t T, const int32_t* cu_seqlens, const void* x, const int32_t* pos,
+                                 const compass_kv* kv, const int32_t* ds_rows, const void* ds, int32_t n_ds,
+                                 void* out, int32_t* status, void* workspace, size_t ws_bytes, void* stream) {
+  const VarlenArgs va{n_seq, cu_seqlens, status};
+  return prefill_impl(d, w, 1, T, x, pos, kv, kv ? kv->lens : nullptr, ds_rows, ds, n_ds, out, workspace,
+                      ws_bytes, stream, &va);
 }
 
 // One decode step; the GEMM weights are either bf16/fp32 (w) or 4-bit affine (wq). With

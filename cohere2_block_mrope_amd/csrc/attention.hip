@@ -42,6 +42,14 @@ struct AttnParams {
   int ldo;
   float scale_log2;  // log2(e) / sqrt(hd)
   int nqb;
+  // Varlen prefill (tiles != NULL): workgroup x takes tile x of the plan; q is [Hq, T, hd]
+  // and o row m holds packed row m; keys come from cache row s (kv_by_seq, first query at
+  // start[s]) or from the packed scratch [Hkv, T, hd] (first query at index 0).
+  const int32_t* tiles;
+  const int32_t* n_tiles;
+  const int32_t* cu;
+  int T;
+  int kv_by_seq;
 };
 
 constexpr int QB = 128, KB = 64;
@@ -64,16 +72,44 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
-  const int qb = P.nqb - 1 - blockIdx.x;  // heaviest (latest) query blocks first
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int h = blockIdx.y;
   const int g = P.Hq / P.Hkv, kvh = h / g;
+  // The workgroup's sequence b, query block qb, its L queries, the rows of its first query in
+  // q (rows of HD) and in o, the start of its (row, kv head) K/V slice and the slice's rows.
+  int b, qb, L, s0, slice_rows;
+  size_t qrow0, orow0, kvrow0;
+  if (P.tiles) {
+    if ((int)blockIdx.x >= P.n_tiles[0]) return;  // past the plan's tiles (uniform)
+    b = P.tiles[2 * blockIdx.x];
+    qb = P.tiles[2 * blockIdx.x + 1];
+    const int m0 = P.cu[b];
+    L = P.cu[b + 1] - m0;
+    qrow0 = (size_t)h * P.T + m0;
+    orow0 = m0;
+    if (P.kv_by_seq) {  // the plan lists live sequences only: 0 <= start[b] <= cap - L
+      s0 = P.start ? P.start[b] : 0;
+      kvrow0 = ((size_t)b * P.Hkv + kvh) * P.cap;
+      slice_rows = P.cap;
+    } else {
+      s0 = 0;
+      kvrow0 = (size_t)kvh * P.T + m0;
+      slice_rows = L;
+    }
+  } else {
+    qb = P.nqb - 1 - blockIdx.x;  // heaviest (latest) query blocks first
+    b = blockIdx.z;
+    L = P.L;
+    qrow0 = ((size_t)b * P.Hq + h) * L;
+    orow0 = (size_t)b * L;
+    // Cache index of the chunk's first query (rows whose chunk does not fit are computed
+    // as if it started at 0: in bounds, and their outputs are never stored by the layer).
+    s0 = P.start ? P.start[b] : 0;
+    if (s0 < 0 || s0 > P.cap - L) s0 = 0;
+    kvrow0 = ((size_t)b * P.Hkv + kvh) * P.cap;
+    slice_rows = P.cap;
+  }
   const int q0 = qb * QB;
-  const int L = P.L;
   const int qw = q0 + 32 * wave + (lane & 31);  // this lane's query (row of the chunk)
-  // Cache index of the chunk's first query (rows whose chunk does not fit are computed
-  // as if it started at 0: in bounds, and their outputs are never stored by the layer).
-  int s0 = P.start ? P.start[b] : 0;
-  if (s0 < 0 || s0 > P.cap - L) s0 = 0;
   const int a0 = s0 + q0;   // cache index of the workgroup's first query
   const int aw = s0 + qw;   // cache index of this lane's query
   const int half = lane >> 5;
@@ -81,7 +117,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
   // Q fragments (B operand of S^T): lane holds query qw, d = 16 ks + 8 half .. + 8.
   bf16x8_t qf[QK];
   {
-    const bf16_t* qp = P.q + (((size_t)b * P.Hq + h) * L + min(qw, L - 1)) * HD + 8 * half;
+    const bf16_t* qp = P.q + (qrow0 + min(qw, L - 1)) * HD + 8 * half;
 #pragma unroll
     for (int ks = 0; ks < QK; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * ks);
   }
@@ -90,8 +126,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
   const int k_lo = P.sliding ? max(0, a0 - P.window + 1) : 0;
   const int kt0 = k_lo / KB, kt1 = q_hi / KB;
 
-  const bf16_t* kbase = P.k + ((size_t)b * P.Hkv + kvh) * P.cap * HD;
-  const bf16_t* vbase = P.v + ((size_t)b * P.Hkv + kvh) * P.cap * HD;
+  const bf16_t* kbase = P.k + kvrow0 * HD;
+  const bf16_t* vbase = P.v + kvrow0 * HD;
   // Software pipeline over key tiles: S^T of tile t + 1 is computed while the softmax of
   // tile t runs (independent MFMA and VALU work in one instruction stream). Tile t sits in
   // K buffer (t - kt0) & 1 and V buffer (t - kt0) & 1; K runs one tile ahead of V, so during
@@ -102,7 +138,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
   // SGPR, so tiles that lie wholly before that row (all but the last) need no per-tile
   // address arithmetic, only this thread's fixed offsets.
   const int last_key = s0 + L - 1;
-  const int slice_bytes = P.cap * HD * 2;
+  const int slice_bytes = slice_rows * HD * 2;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, slice_bytes, kBufferDword3);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, slice_bytes, kBufferDword3);
   int toff[LD_PER_T];
@@ -336,7 +372,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
 
   if (qw >= L) return;
   const float inv = 1.0f / l_run;
-  bf16_t* op = P.o + ((size_t)b * L + qw) * P.ldo + (size_t)h * HD;
+  bf16_t* op = P.o + (orow0 + qw) * P.ldo + (size_t)h * HD;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -350,25 +386,60 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
 }
 
 // ---------------------------------------------------------------- fp32
+// Varlen (row_seq != NULL): workgroup x takes packed row x (skipped when not live); q is
+// [Hq, T, hd], keys come from cache row s (kv_by_seq) or the packed scratch [Hkv, T, hd].
+struct AttnVarlenF32 {
+  const int32_t* row_seq;
+  const int32_t* cu;
+  int T;
+  int kv_by_seq;
+};
+
 template <int HD>
 __global__ __launch_bounds__(64) void attn_prefill_f32(const float* __restrict__ q,
                                                        const float* __restrict__ k,
                                                        const float* __restrict__ v, int Hq, int Hkv,
                                                        int L, int cap, int sliding, int window,
                                                        const int32_t* __restrict__ start,
-                                                       float scale, float* __restrict__ o, int ldo) {
+                                                       float scale, float* __restrict__ o, int ldo,
+                                                       AttnVarlenF32 vl) {
   constexpr int DPL = (HD + 63) / 64;  // d values per lane in the PV accumulation
   __shared__ float qs[HD];
-  const int il = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
-  int s0 = start ? start[b] : 0;  // cache index of the chunk's first query
-  if (s0 < 0 || s0 > cap - L) s0 = 0;
-  const int i = s0 + il;          // cache index of this query
+  const int h = blockIdx.y, lane = threadIdx.x;
   const int kvh = h / (Hq / Hkv);
-  const float* qp = q + (((size_t)b * Hq + h) * L + il) * HD;
+  int il, s0;
+  const float *qp, *kb, *vb;
+  float* op;
+  if (vl.row_seq) {
+    const int m = blockIdx.x;
+    const int sq = vl.row_seq[m];
+    if (sq < 0) return;  // row not processed (uniform)
+    const int m0 = vl.cu[sq];
+    il = m - m0;
+    qp = q + ((size_t)h * vl.T + m) * HD;
+    op = o + (size_t)m * ldo + (size_t)h * HD;
+    if (vl.kv_by_seq) {
+      s0 = start ? start[sq] : 0;
+      kb = k + ((size_t)sq * Hkv + kvh) * cap * HD;
+      vb = v + ((size_t)sq * Hkv + kvh) * cap * HD;
+    } else {
+      s0 = 0;
+      kb = k + ((size_t)kvh * vl.T + m0) * HD;
+      vb = v + ((size_t)kvh * vl.T + m0) * HD;
+    }
+  } else {
+    il = blockIdx.x;
+    const int b = blockIdx.z;
+    s0 = start ? start[b] : 0;  // cache index of the chunk's first query
+    if (s0 < 0 || s0 > cap - L) s0 = 0;
+    qp = q + (((size_t)b * Hq + h) * L + il) * HD;
+    op = o + ((size_t)b * L + il) * ldo + (size_t)h * HD;
+    kb = k + ((size_t)b * Hkv + kvh) * cap * HD;
+    vb = v + ((size_t)b * Hkv + kvh) * cap * HD;
+  }
+  const int i = s0 + il;          // cache index of this query
   for (int d = lane; d < HD; d += 64) qs[d] = qp[d];
   __syncthreads();
-  const float* kb = k + ((size_t)b * Hkv + kvh) * cap * HD;
-  const float* vb = v + ((size_t)b * Hkv + kvh) * cap * HD;
   const int lo = sliding ? max(0, i - window + 1) : 0;
   float m = -INFINITY, l = 0.f, acc[DPL];
 #pragma unroll
@@ -400,7 +471,6 @@ __global__ __launch_bounds__(64) void attn_prefill_f32(const float* __restrict__
       }
     }
   }
-  float* op = o + ((size_t)b * L + il) * ldo + (size_t)h * HD;
 #pragma unroll
   for (int t = 0; t < DPL; ++t) {
     const int d = lane + 64 * t;
@@ -422,18 +492,53 @@ hipError_t launch_attention_prefill(int dtype, const void* q, const void* k, con
     P.o = (bf16_t*)o; P.ldo = ldo;
     P.scale_log2 = kLog2e / sqrtf((float)hd);
     P.nqb = (L + QB - 1) / QB;
+    P.tiles = nullptr; P.n_tiles = nullptr; P.cu = nullptr; P.T = 0; P.kv_by_seq = 0;
     const dim3 grid(P.nqb, Hq, B);
     if (hd == 128) attn_prefill_bf16<128><<<grid, 256, 0, s>>>(P);
     else attn_prefill_bf16<64><<<grid, 256, 0, s>>>(P);
   } else {
     const dim3 grid(L, Hq, B);
     const float scale = 1.0f / sqrtf((float)hd);
+    const AttnVarlenF32 vl{nullptr, nullptr, 0, 0};
     if (hd == 128)
       attn_prefill_f32<128><<<grid, 64, 0, s>>>((const float*)q, (const float*)k, (const float*)v, Hq,
-                                                Hkv, L, cap, sliding, window, start, scale, (float*)o, ldo);
+                                                Hkv, L, cap, sliding, window, start, scale, (float*)o, ldo, vl);
     else
       attn_prefill_f32<64><<<grid, 64, 0, s>>>((const float*)q, (const float*)k, (const float*)v, Hq,
-                                               Hkv, L, cap, sliding, window, start, scale, (float*)o, ldo);
+                                               Hkv, L, cap, sliding, window, start, scale, (float*)o, ldo, vl);
+  }
+  return hipGetLastError();
+}
+
+int varlen_tile_rows(int dtype) { return dtype == 1 ? QB : 0; }
+
+hipError_t launch_attention_prefill_varlen(int dtype, const void* q, const void* k, const void* v, int T,
+                                           int Hq, int Hkv, int cap, int hd, int sliding, int window,
+                                           const int32_t* start, int kv_by_seq, const VarlenPlan& vp,
+                                           void* o, int ldo, hipStream_t s) {
+  if (dtype == 1) {
+    AttnParams P;
+    P.q = (const bf16_t*)q; P.k = (const bf16_t*)k; P.v = (const bf16_t*)v;
+    P.B = 1; P.Hq = Hq; P.Hkv = Hkv; P.L = T; P.cap = cap;
+    P.sliding = sliding; P.window = window;
+    P.start = start;
+    P.o = (bf16_t*)o; P.ldo = ldo;
+    P.scale_log2 = kLog2e / sqrtf((float)hd);
+    P.nqb = 0;
+    P.tiles = vp.tiles; P.n_tiles = vp.n_tiles; P.cu = vp.cu; P.T = T; P.kv_by_seq = kv_by_seq;
+    const dim3 grid(vp.max_tiles, Hq, 1);
+    if (hd == 128) attn_prefill_bf16<128><<<grid, 256, 0, s>>>(P);
+    else attn_prefill_bf16<64><<<grid, 256, 0, s>>>(P);
+  } else {
+    const dim3 grid(T, Hq, 1);
+    const float scale = 1.0f / sqrtf((float)hd);
+    const AttnVarlenF32 vl{vp.row_seq, vp.cu, T, kv_by_seq};
+    if (hd == 128)
+      attn_prefill_f32<128><<<grid, 64, 0, s>>>((const float*)q, (const float*)k, (const float*)v, Hq,
+                                                Hkv, T, cap, sliding, window, start, scale, (float*)o, ldo, vl);
+    else
+      attn_prefill_f32<64><<<grid, 64, 0, s>>>((const float*)q, (const float*)k, (const float*)v, Hq,
+                                               Hkv, T, cap, sliding, window, start, scale, (float*)o, ldo, vl);
   }
   return hipGetLastError();
 }

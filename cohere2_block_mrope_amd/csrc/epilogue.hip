@@ -50,7 +50,14 @@ __global__ __launch_bounds__(256) void proj_epilogue_kernel(const float* __restr
   } else {
     b = m / E.L; l = m - b * E.L;
     lc = l;
-    if (E.kv_start) {  // chunked prefill: rows whose chunk does not fit the cache are skipped
+    if (E.row_seq) {  // varlen: rows of sequences that are not processed are skipped
+      const int sq = E.row_seq[m];
+      if (sq < 0) return;
+      if (E.kv_by_seq && !gu && u / half >= E.Hq) {  // K/V to the sequence's cache row
+        b = sq;
+        lc = (E.kv_start ? E.kv_start[sq] : 0) + (m - E.cu[sq]);
+      }
+    } else if (E.kv_start) {  // chunked prefill: rows whose chunk does not fit the cache are skipped
       const int s0 = E.kv_start[b];
       if (s0 < 0 || s0 > E.cap - E.L) return;
       lc = l + s0;
@@ -97,7 +104,7 @@ __global__ __launch_bounds__(256) void splitk_resid_kernel(const float* __restri
   for (; z + 4 <= splits; z += 4)
     acc += (r[z * sq] + r[(z + 1) * sq]) + (r[(z + 2) * sq] + r[(z + 3) * sq]);
   for (; z < splits; ++z) acc += r[z * sq];
-  if (!row_live(rs, (int)(idx / N) / rs.L)) return;  // rows left untouched
+  if (!row_live_m(rs, (int)(idx / N))) return;  // rows left untouched
 #pragma unroll
   for (int e = 0; e < 4; ++e) out[idx + e] = Elt<T>::from_f(Elt<T>::to_f(x[idx + e]) + acc[e]);
 }
@@ -108,7 +115,7 @@ __global__ __launch_bounds__(256) void deepstack_kernel(const int32_t* __restric
                                                         RowStart rs, T* out) {
   const int r = blockIdx.x;
   const int row = rows[r];
-  if (row < 0 || row >= n_rows || !row_live(rs, row / rs.L)) return;
+  if (row < 0 || row >= n_rows || !row_live_m(rs, row)) return;
   for (int c = blockIdx.y * 256 + threadIdx.x; c < D; c += gridDim.y * 256) {
     T* o = out + (size_t)row * D + c;
     *o = Elt<T>::from_f(Elt<T>::to_f(*o) + Elt<T>::to_f(ds[(size_t)r * D + c]));

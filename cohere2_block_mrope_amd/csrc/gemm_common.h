@@ -161,18 +161,28 @@ __device__ __forceinline__ void proj_qkv_epilogue(const GemmParams& P, const f32
         const int mm = min(m, P.M - 1);
         int b, l;
         if (E.decode) { b = mm; l = E.lens[b]; } else { b = mm / E.L; l = mm - b * E.L; }
-        // Cache index of this row's K/V: chunked prefill continues after kv_start[b]
-        // tokens (rows whose chunk does not fit are not written).
-        int lc = l;
+        // Cache row and index of this row's K/V: chunked prefill continues after
+        // kv_start[b] tokens (rows whose chunk does not fit are not written); a packed
+        // varlen row goes to its sequence's cache row (or stays in the packed scratch).
+        int lc = l, bkv = b;
         bool store = m < P.M;
-        if (kind != 0 && !E.decode && E.kv_start) {
-          const int s0 = E.kv_start[b];
-          store = store && s0 >= 0 && s0 <= E.cap - E.L;
-          lc = l + (store ? s0 : 0);
+        if (kind != 0 && !E.decode) {
+          if (E.row_seq) {
+            const int sq = E.row_seq[mm];
+            store = store && sq >= 0;
+            if (E.kv_by_seq && sq >= 0) {
+              bkv = sq;
+              lc = (E.kv_start ? E.kv_start[sq] : 0) + (mm - E.cu[sq]);
+            }
+          } else if (E.kv_start) {
+            const int s0 = E.kv_start[b];
+            store = store && s0 >= 0 && s0 <= E.cap - E.L;
+            lc = l + (store ? s0 : 0);
+          }
         }
         bf16_t* dst;
         if (kind == 0) dst = base + (((size_t)b * E.Hq + head) * E.Lq + (E.decode ? 0 : l)) * HD;
-        else dst = base + (((size_t)b * E.Hkv + head) * E.cap + lc) * HD;
+        else dst = base + (((size_t)bkv * E.Hkv + head) * E.cap + lc) * HD;
         float pt = 0.f, ph = 0.f, pw = 0.f;
         if (rot) {
           pt = (float)E.pos[mm];
@@ -266,7 +276,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& P, f32x16_t (&ac
           const int n = nw0 + 32 * j + col4;
           if (m >= P.M || n >= P.N) continue;
           if constexpr (MODE == MODE_RESID) {
-            if (!row_live(P.rs, m / P.rs.L)) continue;
+            if (!row_live_m(P.rs, m)) continue;
           }
           if constexpr (MODE == MODE_RAW) {
             *reinterpret_cast<f32x4_t*>(P.raw + ((size_t)z * P.M + m) * P.N + n) = f32x4_t{v[0], v[1], v[2], v[3]};

@@ -93,7 +93,15 @@ struct ProjEpi {
   int cap;
   const int32_t* lens;  // decode: cache index of the new token, per row
   const int32_t* kv_start;  // chunked prefill: row b's K/V go to cache index kv_start[b] + l
-                            // (rows with kv_start[b] outside [0, cap - L] write none); else NULL
+                            // (rows with kv_start[b] outside [0, cap - L] write none); else NULL.
+                            // Varlen: the cached tokens of each sequence (NULL: none).
+  // Varlen prefill (packed sequences, B = 1 and L = T): row_seq[m] is the sequence of packed
+  // row m, or -1 when the row is not processed (its K/V are not written); cu[s] is the first
+  // packed row of sequence s. kv_by_seq: K/V of row m go to cache row s at kv_start[s] +
+  // m - cu[s]; otherwise to the packed scratch [1, Hkv, T, hd] at row m. NULL when not varlen.
+  const int32_t* row_seq;
+  const int32_t* cu;
+  int kv_by_seq;
   void* act;            // act[m * ldact + act_col0 + c] = silu(gate) * up
   int ldact;
   int act_col0;
@@ -104,10 +112,13 @@ struct ProjEpi {
 // Chunked prefill rows: row b of a [B, L] chunk continues a cache holding start[b] tokens
 // and is processed only when 0 <= start[b] <= cap - L; otherwise it is skipped (no K/V
 // written, its output rows left as they were). start == NULL: every row is live.
+// Varlen prefill: row_seq (when not NULL) decides instead, row m being live iff
+// row_seq[m] >= 0.
 struct RowStart {
   const int32_t* start;
   int L;
   int cap;
+  const int32_t* row_seq;
 };
 #ifdef __HIPCC__
 __device__ __forceinline__ bool row_live(const RowStart& r, int b) {
@@ -115,7 +126,26 @@ __device__ __forceinline__ bool row_live(const RowStart& r, int b) {
   const int s0 = r.start[b];
   return s0 >= 0 && s0 <= r.cap - r.L;
 }
+// Liveness of flattened row m (= b * L + l, or a packed varlen row).
+__device__ __forceinline__ bool row_live_m(const RowStart& r, int m) {
+  if (r.row_seq) return r.row_seq[m] >= 0;
+  return row_live(r, m / r.L);
+}
 #endif
+
+// Varlen prefill plan (device buffers carved from the workspace): the packed rows' sequences
+// and the attention's query tiles. tiles[2 t], tiles[2 t + 1] = (sequence, query block) of
+// tile t < *n_tiles, ordered by query block, latest first.
+struct VarlenPlan {
+  const int32_t* cu;  // [n_seq + 1], caller's offsets (validated on the device)
+  int n_seq;
+  int32_t* row_seq;   // [T]
+  int32_t* tiles;     // [2 * max_tiles]
+  int32_t* n_tiles;   // [1]
+  int max_tiles;
+};
+constexpr int kVarlenMaxSeqs = 4096;
+constexpr int kVarlenMaxTokens = 1 << 19;
 
 // Raise `kernel`'s dynamic LDS limit to `bytes` on the current device, once per (device,
 // kernel); thread-safe (defined in api.hip).
@@ -182,6 +212,22 @@ hipError_t launch_splitk_resid(int dtype, const float* raw, int splits, int M, i
 hipError_t launch_attention_prefill(int dtype, const void* q, const void* k, const void* v, int B,
                                     int Hq, int Hkv, int L, int cap, int hd, int sliding, int window,
                                     const int32_t* start, void* o, int ldo, hipStream_t s);
+// Varlen prefill attention over T packed rows (q [Hq, T, hd]; o row m at o[m * ldo + h * hd]).
+// kv_by_seq: keys of sequence s in cache row s of k, v [n_seq, Hkv, cap, hd], its first query
+// at cache index start[s] (start NULL: 0); else keys in the packed scratch [Hkv, T, hd].
+// Only the plan's tiles (bf16) or live rows (fp32) are computed.
+hipError_t launch_attention_prefill_varlen(int dtype, const void* q, const void* k, const void* v, int T,
+                                           int Hq, int Hkv, int cap, int hd, int sliding, int window,
+                                           const int32_t* start, int kv_by_seq, const VarlenPlan& vp,
+                                           void* o, int ldo, hipStream_t s);
+// Builds the plan: validates cu (cu[0] = 0, non-decreasing, cu[n_seq] = T), marks each
+// sequence live iff start == NULL or 0 <= start[s] <= cap - len_s, fills row_seq (-1 for
+// rows not processed) and, when tile_rows > 0, the query tiles of tile_rows queries.
+// status (may be NULL) gets bit 0 for invalid offsets (then nothing is live) and bit 1
+// when a sequence was skipped.
+hipError_t launch_varlen_plan(const VarlenPlan& vp, int T, const int32_t* start, int cap, int tile_rows,
+                              int32_t* status, hipStream_t s);
+int varlen_tile_rows(int dtype);
 
 // Decode attention, split over key chunks, then combine.
 int decode_chunk_keys(int dtype, int hd);

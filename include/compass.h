@@ -180,6 +180,36 @@ int compass_layer_prefill_chunk(const compass_layer_desc *d, const compass_layer
                                 int32_t n_ds, void *out, void *workspace, size_t ws_bytes,
                                 void *stream);
 
+/* Varlen prefill: n_seq sequences of different lengths packed into T rows, one launch,
+ * no padding (FreeToken PR "feat(mm): serve image input on the Qwen families", "How it
+ * fits together": prefill planned per request, each with its own MRoPE positions and its
+ * own prefix cache; mlxcel Compass issue, "Validation": prefill causal within a sequence,
+ * and the "Acceptance criteria" correction: dense cache, window as a mask). Sequence s is
+ * packed rows [cu_seqlens[s], cu_seqlens[s + 1]); its token i attends to the keys of that
+ * sequence only.
+ *   cu_seqlens: device int32 [n_seq + 1], cu[0] = 0, non-decreasing, cu[n_seq] = T
+ *     (empty sequences allowed). 1 <= n_seq <= 4096, 1 <= T <= 524288.
+ *   x [T, D]; pos [3, T] int32 (each sequence's own positions; sliding only); out [T, D]
+ *     (may alias x); ds_rows index packed rows.
+ *   kv (optional): caches [n_seq, Hkv, capacity, hd]; kv->lens (optional, device [n_seq]):
+ *     tokens sequence s already holds (NULL: none). Token i of sequence s then sits at cache
+ *     index lens[s] + i, its K/V (after MRoPE on sliding layers) are written there, and it
+ *     sees cache keys j <= lens[s] + i (and > lens[s] + i - window on sliding layers). A
+ *     sequence with lens[s] < 0 or lens[s] + len_s > capacity is skipped: no K/V written,
+ *     its out rows left as they were. kv NULL: K/V stay in the workspace.
+ *   status (optional, device int32 [1], read after the stream synchronizes): bit 0 = the
+ *     offsets are invalid (then nothing is computed or written), bit 1 = a sequence was
+ *     skipped.
+ *   workspace: compass_varlen_workspace_size(d, n_seq, T) bytes, 256-byte aligned. Other
+ *   errors as compass_layer_prefill (all checked on the host before any launch). */
+size_t compass_varlen_workspace_size(const compass_layer_desc *d, int32_t n_seq, int32_t T);
+int compass_layer_prefill_varlen(const compass_layer_desc *d, const compass_layer_weights *w,
+                                 int32_t n_seq, int32_t T, const int32_t *cu_seqlens,
+                                 const void *x, const int32_t *pos, const compass_kv *kv,
+                                 const int32_t *ds_rows, const void *ds, int32_t n_ds,
+                                 void *out, int32_t *status, void *workspace, size_t ws_bytes,
+                                 void *stream);
+
 /* One decode step of one layer: one new token per row. The mlxcel Compass issue defines
  * it: "Text decoder forward" gives the layer (one shared LayerNorm, the attention and
  * SwiGLU branches summed into the residual, MRoPE on sliding layers only); the correction

@@ -4,7 +4,9 @@
 // file; the HIP library shares no code with it. It is a second, independent oracle next
 // to the fp64 numpy one: data are fp32 (float storage for every tensor and every
 // intermediate), each dot product, mean or softmax sum is accumulated in double and
-// rounded once. Straight loops in the order of the definitions, no blocking.
+// rounded once. Straight loops in the order of the definitions, no blocking. Independent
+// rows, queries and heads run in parallel (OpenMP); each result is computed by one thread
+// in the same order as a serial run, so the output does not depend on the thread count.
 //
 // Definitions followed (mlxcel issue "feat(vlm): add Cohere Compass / North-Micro-Vision
 // (cohere_compass) VLM"):
@@ -21,6 +23,8 @@
 //    grid (t, h / m, w / m) covers t * (h / m) * (w / m) pad tokens at start + (i, j, k);
 //    the next text position is start + max(t, h / m, w / m).
 //  * Tied logits: LayerNorm then the embedding as a linear map, times logit_scale.
+#include <omp.h>
+
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -44,6 +48,7 @@ double dot(const float* a, const float* b, int n) {
 
 // y[r] = LayerNorm(x[r]) * w over rows of n (biased variance).
 void layer_norm(const float* x, const float* w, float eps, int rows, int n, float* y) {
+#pragma omp parallel for schedule(static)
   for (int r = 0; r < rows; ++r) {
     const float* xr = x + (size_t)r * n;
     double mu = 0.0;
@@ -59,6 +64,7 @@ void layer_norm(const float* x, const float* w, float eps, int rows, int n, floa
 
 // y[r][o] = sum_i x[r][i] * W[o][i]  (W in nn.Linear [out, in] layout)
 void linear(const float* x, const float* W, int rows, int in, int out, float* y) {
+#pragma omp parallel for collapse(2) schedule(static)
   for (int r = 0; r < rows; ++r)
     for (int o = 0; o < out; ++o) y[(size_t)r * out + o] = (float)dot(x + (size_t)r * in, W + (size_t)o * in, in);
 }
@@ -108,6 +114,9 @@ float silu(float g) { return (float)((double)g / (1.0 + std::exp(-(double)g))); 
 }  // namespace
 
 extern "C" {
+
+// Threads the parallel loops use (OMP_NUM_THREADS, else the cores the runtime sees).
+int cref_num_threads(void) { return omp_get_max_threads(); }
 
 typedef struct {
   int32_t D, Hq, Hkv, hd, I;
@@ -187,8 +196,10 @@ void cref_layer_forward(const cref_shape* cs, const float* const* w, int B, int 
   linear(a.data(), w[3], (int)T, D, Hkv * hd, v.data());
   linear(a.data(), w[5], (int)T, D, I, gt.data());
   linear(a.data(), w[6], (int)T, D, I, up.data());
+#pragma omp parallel for schedule(static)
   for (size_t i = 0; i < T * I; ++i) act[i] = (float)((double)silu(gt[i]) * (double)up[i]);
   if (s.sliding) {
+#pragma omp parallel for collapse(2) schedule(static)
     for (int b = 0; b < B; ++b)
       for (int l = 0; l < L; ++l) {
         const int64_t p[3] = {pos[((size_t)0 * B + b) * L + l], pos[((size_t)1 * B + b) * L + l],
@@ -209,11 +220,12 @@ void cref_layer_forward(const cref_shape* cs, const float* const* w, int B, int 
   // Attention: query l of row b at cache index n = s0 + l sees keys j <= n (and j > n - W
   // on sliding layers); key j < s0 comes from the cache, j >= s0 from this block.
   const double scale = 1.0 / std::sqrt((double)hd);
+#pragma omp parallel for collapse(3) schedule(dynamic, 16)
   for (int b = 0; b < B; ++b) {
-    const int s0 = start ? start[b] : 0;
     for (int h = 0; h < Hq; ++h) {
-      const int kvh = h / g;
       for (int l = 0; l < L; ++l) {
+        const int s0 = start ? start[b] : 0;
+        const int kvh = h / g;
         const int n = s0 + l;
         const int lo = s.sliding ? (n - s.window + 1 > 0 ? n - s.window + 1 : 0) : 0;
         const float* qv = &q[(((size_t)b * L + l) * Hq + h) * hd];
@@ -227,12 +239,14 @@ void cref_layer_forward(const cref_shape* cs, const float* const* w, int B, int 
         }
         double z = 0.0;
         for (int j = lo; j <= n; ++j) z += std::exp(sc[j - lo] - mx);
+        // p_j = exp(s_j - max) / z, each evaluated once.
+        for (int j = lo; j <= n; ++j) sc[j - lo] = std::exp(sc[j - lo] - mx) / z;
         for (int d = 0; d < hd; ++d) {
           double acc = 0.0;
           for (int j = lo; j <= n; ++j) {
             const float* vv = j < s0 ? &vc[(((size_t)b * Hkv + kvh) * cap + j) * hd]
                                      : &v[(((size_t)b * L + (j - s0)) * Hkv + kvh) * hd];
-            acc += std::exp(sc[j - lo] - mx) / z * (double)vv[d];
+            acc += sc[j - lo] * (double)vv[d];
           }
           o[(((size_t)b * L + l) * Hq + h) * hd + d] = (float)acc;
         }
@@ -240,6 +254,7 @@ void cref_layer_forward(const cref_shape* cs, const float* const* w, int B, int 
     }
   }
   // out = x + o Wo^T + act Wd^T (the two branches added to the residual).
+#pragma omp parallel for collapse(2) schedule(static)
   for (size_t r = 0; r < T; ++r)
     for (int c = 0; c < D; ++c) {
       const double attn = dot(&o[r * Hq * hd], w[4] + (size_t)c * Hq * hd, Hq * hd);
@@ -258,6 +273,7 @@ void cref_logits(int R, int D, int V, const float* h, const float* nw, float eps
                  float* logits) {
   std::vector<float> a((size_t)R * D);
   layer_norm(h, nw, eps, R, D, a.data());
+#pragma omp parallel for collapse(2) schedule(static)
   for (int r = 0; r < R; ++r)
     for (int v = 0; v < V; ++v) {
       const float l = (float)dot(&a[(size_t)r * D], E + (size_t)v * D, D);

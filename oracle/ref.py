@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libcompass_ref.so")
 
 def build() -> str:
     tmp = LIB + ".tmp"
-    subprocess.run(["g++", "-O2", "-std=c++17", "-shared", "-fPIC", "-o", tmp, SRC], check=True)
+    subprocess.run(["g++", "-O2", "-std=c++17", "-fopenmp", "-shared", "-fPIC", "-o", tmp, SRC], check=True)
     os.replace(tmp, LIB)
     return LIB
 
@@ -40,6 +40,11 @@ def lib():
             build()
         _lib = ctypes.CDLL(LIB)
     return _lib
+
+
+def num_threads() -> int:
+    """Threads the reference's parallel loops use."""
+    return int(lib().cref_num_threads())
 
 
 def _f32(a):

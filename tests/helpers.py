@@ -115,7 +115,9 @@ def run_logits(h: torch.Tensor, norm_w, eps: float, embed, scale: float, dtype: 
     return logits
 
 
-def np64(t: torch.Tensor) -> np.ndarray:
+def np64(t) -> np.ndarray:
+    if isinstance(t, np.ndarray):
+        return t.astype(np.float64)
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
