@@ -226,6 +226,13 @@ def run_decode_stack(args, b, H, W, torch):
            "kernels_us": {k: round(v["mean_us"], 1) for k, v in stats.items()}}
     if att:
         res["decode_attn_hbm_frac"] = att_bytes_mean / (att["mean_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS
+    # HBM bytes per decode-attention launch from the committed counter passes (null once the
+    # kernel's sources have changed since), next to the algorithmic bytes.
+    res["decode_attn_traffic"] = {
+        "sliding": {"hbm_bytes": traffic_for("decode_attn_sliding_decode_stack", DECODE_SOURCES),
+                    "algorithmic_bytes": kv_bytes_slide},
+        "full": {"hbm_bytes": traffic_for("decode_attn_full_decode_stack", DECODE_SOURCES),
+                 "algorithmic_bytes": kv_bytes_full}}
     q4_bytes_proj = (sh.hidden // 2 + 4 * (sh.hidden // 64)) * ((sh.n_q_heads + 2 * Hkv) * hd + 2 * sh.intermediate)
     K2 = sh.n_q_heads * hd + sh.intermediate
     q4_bytes_out = (K2 // 2 + 4 * (K2 // 64)) * sh.hidden
@@ -454,6 +461,7 @@ def run_tiny_f32(args, b, H, W, torch):
 
 
 GEMM_SOURCES = ["gemm_bf16.hip", "gemm_common.h", "common.h", "launch.h"]
+DECODE_SOURCES = ["decode.hip", "common.h", "launch.h"]
 
 
 def traffic_for(name: str, sources):

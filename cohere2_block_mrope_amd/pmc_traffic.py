@@ -44,10 +44,12 @@ def _rows(d: str):
             yield from csv.DictReader(fh)
 
 
-def mean_kib(d: str, counter: str, kernel: str, min_kib: float = 0.0):
-    """(mean value, dispatch count) of `counter` over dispatches whose name contains `kernel`."""
+def mean_kib(d: str, counter: str, kernel: str, min_kib: float = 0.0, grid: int = 0):
+    """(mean value, dispatch count) of `counter` over dispatches whose name contains `kernel`
+    (and, when grid > 0, whose grid holds exactly `grid` work-items)."""
     vals = [float(r["Counter_Value"]) for r in _rows(d)
-            if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]]
+            if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]
+            and (grid <= 0 or int(r.get("Grid_Size", -1)) == grid)]
     vals = [v for v in vals if v >= min_kib]
     if not vals:
         raise SystemExit(f"no {counter} dispatches of '{kernel}' under {d}")
@@ -63,6 +65,7 @@ def main(argv=None):
     p.add_argument("--name", required=True, help="record name: profiles/<name>_traffic.{json,md}")
     p.add_argument("--sources", nargs="+", required=True, help="csrc files the kernel is built from")
     p.add_argument("--algorithmic-bytes", type=float, default=None)
+    p.add_argument("--grid", type=int, default=0, help="only dispatches of this many work-items")
     p.add_argument("--command", default="", help="the command line of the counter passes, for the summary")
     a = p.parse_args(argv)
 
@@ -71,12 +74,13 @@ def main(argv=None):
     big = 0.25 * known_kib
     cf, ncf = mean_kib(a.fetch, "FETCH_SIZE", COPY_KERNEL, big)
     cw, ncw = mean_kib(a.write, "WRITE_SIZE", COPY_KERNEL, big)
-    kf, nkf = mean_kib(a.fetch, "FETCH_SIZE", a.kernel)
-    kw, nkw = mean_kib(a.write, "WRITE_SIZE", a.kernel)
+    kf, nkf = mean_kib(a.fetch, "FETCH_SIZE", a.kernel, grid=a.grid)
+    kw, nkw = mean_kib(a.write, "WRITE_SIZE", a.kernel, grid=a.grid)
     f_fetch, f_write = known_kib / cf, known_kib / cw
     read_b, write_b = kf * 1024 * f_fetch, kw * 1024 * f_write
     rec = {
         "kernel": a.kernel,
+        "grid_work_items": a.grid or None,
         "source_files": a.sources,
         "source_sha256": source_digest(a.sources),
         "hbm_bytes_per_launch": read_b + write_b,
@@ -95,7 +99,7 @@ def main(argv=None):
         fh.write("\n")
     alg = f"{a.algorithmic_bytes / 1e6:.1f} MB" if a.algorithmic_bytes else "n/a"
     lines = [
-        f"# HBM traffic of `{a.kernel}` ({a.name})",
+        f"# HBM traffic of `{a.kernel}` ({a.name})" + (f", dispatches of {a.grid:,} work-items" if a.grid else ""),
         "",
         f"Counter passes (each its own run): `{a.command}`",
         "",
