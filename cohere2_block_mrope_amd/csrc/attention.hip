@@ -50,6 +50,13 @@ struct AttnParams {
   const int32_t* cu;
   int T;
   int kv_by_seq;
+  // XCD-aware order of the dense grid (1-D grid; xmode 0: grid (nqb, Hq, B) as is). The
+  // workgroups that share one (row, kv head) K/V slice run on one XCD so that its L2 serves
+  // their key tiles: workgroup id i runs on XCD i % 8. xmode 1 (B * Hkv a multiple of 8):
+  // XCD x takes groups x, x + 8, ... one after the other; xmode 2 (B * Hkv divides 8):
+  // 8 / (B * Hkv) XCDs share a group, dealing its work units round-robin. Inside a group the
+  // units run latest query block first, the group's query heads next to each other.
+  int xmode;
 };
 
 constexpr int QB = 128, KB = 64;
@@ -72,8 +79,27 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
-  const int h = blockIdx.y;
-  const int g = P.Hq / P.Hkv, kvh = h / g;
+  const int g = P.Hq / P.Hkv;
+  int h = blockIdx.y;
+  int bx = blockIdx.x, bz = blockIdx.z;  // dense grid coordinates (x: heaviest first)
+  if (P.xmode) {
+    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+    const int groups = P.B * P.Hkv, per_group = P.nqb * g;
+    int grp, j;
+    if (P.xmode == 1) {
+      grp = xcd + 8 * (local / per_group);
+      j = local - (local / per_group) * per_group;
+    } else {
+      const int r = 8 / groups;
+      grp = xcd % groups;
+      j = local * r + xcd / groups;
+      if (j >= per_group) return;  // uniform: past the group's units
+    }
+    bz = grp / P.Hkv;
+    h = (grp - bz * P.Hkv) * g + j % g;
+    bx = j / g;
+  }
+  const int kvh = h / g;
   // The workgroup's sequence b, query block qb, its L queries, the rows of its first query in
   // q (rows of HD) and in o, the start of its (row, kv head) K/V slice and the slice's rows.
   int b, qb, L, s0, slice_rows;
@@ -96,8 +122,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
       slice_rows = L;
     }
   } else {
-    qb = P.nqb - 1 - blockIdx.x;  // heaviest (latest) query blocks first
-    b = blockIdx.z;
+    qb = P.nqb - 1 - bx;  // heaviest (latest) query blocks first
+    b = bz;
     L = P.L;
     qrow0 = ((size_t)b * P.Hq + h) * L;
     orow0 = (size_t)b * L;
@@ -493,7 +519,18 @@ hipError_t launch_attention_prefill(int dtype, const void* q, const void* k, con
     P.scale_log2 = kLog2e / sqrtf((float)hd);
     P.nqb = (L + QB - 1) / QB;
     P.tiles = nullptr; P.n_tiles = nullptr; P.cu = nullptr; P.T = 0; P.kv_by_seq = 0;
-    const dim3 grid(P.nqb, Hq, B);
+    const int groups = B * Hkv, per_group = P.nqb * (Hq / Hkv);
+    dim3 grid(P.nqb, Hq, B);
+    if (groups % 8 == 0) {
+      P.xmode = 1;
+      grid = dim3((unsigned)(groups * per_group), 1, 1);
+    } else if (8 % groups == 0) {
+      P.xmode = 2;
+      const int r = 8 / groups;
+      grid = dim3((unsigned)(8 * ((per_group + r - 1) / r)), 1, 1);
+    } else {
+      P.xmode = 0;
+    }
     if (hd == 128) attn_prefill_bf16<128><<<grid, 256, 0, s>>>(P);
     else attn_prefill_bf16<64><<<grid, 256, 0, s>>>(P);
   } else {
@@ -526,6 +563,7 @@ hipError_t launch_attention_prefill_varlen(int dtype, const void* q, const void*
     P.scale_log2 = kLog2e / sqrtf((float)hd);
     P.nqb = 0;
     P.tiles = vp.tiles; P.n_tiles = vp.n_tiles; P.cu = vp.cu; P.T = T; P.kv_by_seq = kv_by_seq;
+    P.xmode = 0;
     const dim3 grid(vp.max_tiles, Hq, 1);
     if (hd == 128) attn_prefill_bf16<128><<<grid, 256, 0, s>>>(P);
     else attn_prefill_bf16<64><<<grid, 256, 0, s>>>(P);
