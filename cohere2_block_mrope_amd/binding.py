@@ -45,7 +45,8 @@ class compass_layer_desc(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("intermediate", ctypes.c_int32), ("kind", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("mrope_section", ctypes.c_int32 * 3), ("rope_theta", ctypes.c_float),
-                ("ln_eps", ctypes.c_float), ("dtype", ctypes.c_int32), ("rope_layout", ctypes.c_int32)]
+                ("ln_eps", ctypes.c_float), ("dtype", ctypes.c_int32), ("rope_layout", ctypes.c_int32),
+                ("ln_fuse", ctypes.c_int32)]
 
 
 class compass_layer_weights(ctypes.Structure):
@@ -133,9 +134,10 @@ def _stream(stream) -> Optional[int]:
 
 def make_desc(hidden: int, n_q_heads: int, n_kv_heads: int, head_dim: int, intermediate: int, kind: int,
               window: int, mrope_section, rope_theta: float, ln_eps: float, dtype: int,
-              rope_layout: int = COMPASS_ROPE_INTERLEAVED) -> compass_layer_desc:
+              rope_layout: int = COMPASS_ROPE_INTERLEAVED, ln_fuse: int = 0) -> compass_layer_desc:
     d = compass_layer_desc()
     d.rope_layout = rope_layout
+    d.ln_fuse = ln_fuse
     d.hidden, d.n_q_heads, d.n_kv_heads, d.head_dim, d.intermediate = hidden, n_q_heads, n_kv_heads, head_dim, intermediate
     d.kind, d.window = kind, window
     d.mrope_section[:] = list(mrope_section)

@@ -113,6 +113,7 @@ int check_desc(const compass_layer_desc* d) {
     return fail(COMPASS_E_UNSUPPORTED, "(Hq + 2 Hkv) * head_dim must be a multiple of 128");
   if ((long long)(d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim + 2LL * d->intermediate > (1LL << 30))
     return fail(COMPASS_E_UNSUPPORTED, "projection width too large");
+  if (d->ln_fuse != 0 && d->ln_fuse != 1) return fail(COMPASS_E_INVALID, "ln_fuse %d is neither 0 nor 1", d->ln_fuse);
   if (d->rope_layout != COMPASS_ROPE_INTERLEAVED && d->rope_layout != COMPASS_ROPE_SECTIONS)
     return fail(COMPASS_E_INVALID, "rope_layout %d is neither INTERLEAVED nor SECTIONS", d->rope_layout);
   if (!(d->ln_eps >= 0.f) || !isfinite(d->ln_eps))
@@ -512,10 +513,16 @@ static int prefill_impl(const compass_layer_desc* d, const compass_layer_weights
   if (va)
     LAUNCH("varlen_plan", s, launch_varlen_plan(plan, L, start, kv ? kv->capacity : 0,
                                                 varlen_tile_rows(dt), va->status, s));
-  LAUNCH("layernorm", s, launch_layernorm(dt, x, w->ln_w, d->ln_eps, a, (int)T, (int)m.D, s));
-  if (dt == COMPASS_BF16) {
+  if (dt == COMPASS_BF16 && d->ln_fuse) {
+    float2* stats = (float2*)a;  // the LayerNorm output buffer holds the row statistics instead
+    LAUNCH("ln_stats", s, launch_ln_stats(x, d->ln_eps, stats, (int)T, (int)m.D, s));
+    LAUNCH("gemm_proj", s, launch_gemm_bf16_proj(x, (int)m.D, (int)T, (int)m.D, pb, (int)m.Nv, ep, rt, s, stats,
+                                                 w->ln_w));
+  } else if (dt == COMPASS_BF16) {
+    LAUNCH("layernorm", s, launch_layernorm(dt, x, w->ln_w, d->ln_eps, a, (int)T, (int)m.D, s));
     LAUNCH("gemm_proj", s, launch_gemm_bf16_proj(a, (int)m.D, (int)T, (int)m.D, pb, (int)m.Nv, ep, rt, s));
   } else {
+    LAUNCH("layernorm", s, launch_layernorm(dt, x, w->ln_w, d->ln_eps, a, (int)T, (int)m.D, s));
     LAUNCH("gemm_proj_f32", s, launch_gemm_f32_raw(a, (int)m.D, (int)T, (int)m.D, pb, (int)m.Nv, 1, raw, 1.f, s));
     LAUNCH("proj_epilogue", s, launch_proj_epilogue(dt, raw, 1, (int)T, (int)m.Nv, ep, rt, s));
   }

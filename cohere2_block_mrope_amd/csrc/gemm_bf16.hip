@@ -36,7 +36,7 @@ namespace {
 
 using namespace gemm;
 
-template <int BM, int BN, int MODE, int BKIND>
+template <int BM, int BN, int MODE, int BKIND, bool LNA = false>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams P) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int MB = WM / 32, NB = WN / 32;
@@ -112,9 +112,17 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams P) {
   constexpr int PIECES = A_PER_T + B_PER_T;
   constexpr int MFMAS = (BK / 16) * MB * NB;
   u32x4_t ra[A_PER_T], rb[B_PER_T];
+  // LNA: the LayerNorm weight of the stage's 8 columns of this thread (loaded with the last
+  // A piece, after the stage before has stored all its A pieces), and the tile rows'
+  // (mean, rstd) in LDS.
+  u32x4_t wv = {0u, 0u, 0u, 0u};
+  float2* s_st = reinterpret_cast<float2*>(smem + 2 * (BM + BN) * BK);
   auto load_piece = [&](int k0, int p) __attribute__((always_inline)) {
     if (p < A_PER_T) {
       ra[p] = *reinterpret_cast<const u32x4_t*>(P.A + aoff[p] + k0);
+      if constexpr (LNA) {
+        if (p == A_PER_T - 1) wv = *reinterpret_cast<const u32x4_t*>(P.ln_w + k0 + lchunk * 8);
+      }
     } else {
       const int i = p - A_PER_T;
       const u32x4_t* src = reinterpret_cast<const u32x4_t*>(
@@ -127,9 +135,22 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams P) {
     }
   };
   auto store_piece = [&](int buf, int p) __attribute__((always_inline)) {
-    if (p < A_PER_T)
-      *reinterpret_cast<u32x4_t*>(As + buf * BM * BK + swz(arow0 + 8 * p, lchunk)) = ra[p];
-    else
+    if (p < A_PER_T) {
+      u32x4_t v = ra[p];
+      if constexpr (LNA) {  // the same fp32 expression as the LayerNorm kernel, one bf16 rounding
+        const float2 st = s_st[arow0 + 8 * p];
+        const uint32_t xs[4] = {v.x, v.y, v.z, v.w}, ws[4] = {wv.x, wv.y, wv.z, wv.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float x0 = __uint_as_float(xs[j] << 16), x1 = __uint_as_float(xs[j] & 0xffff0000u);
+          const float w0 = __uint_as_float(ws[j] << 16), w1 = __uint_as_float(ws[j] & 0xffff0000u);
+          o[j] = pack_bf2((x0 - st.x) * st.y * w0, (x1 - st.x) * st.y * w1);
+        }
+        v = u32x4_t{o[0], o[1], o[2], o[3]};
+      }
+      *reinterpret_cast<u32x4_t*>(As + buf * BM * BK + swz(arow0 + 8 * p, lchunk)) = v;
+    } else
       *reinterpret_cast<u32x4_t*>(Bs + buf * BN * BK + swz(brow0 + 8 * (p - A_PER_T), lchunk)) =
           rb[p - A_PER_T];
   };
@@ -192,6 +213,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams P) {
     __syncthreads();
   };
 
+  if constexpr (LNA) {
+    for (int i = tid; i < BM; i += 256) s_st[i] = P.ln_stats[min(m0 + i, P.M - 1)];
+    __syncthreads();
+  }
   const int nk = (kend - kbeg) / BK;
   if (nk > 0) {
 #pragma unroll
@@ -216,12 +241,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams P) {
   else gemm_epilogue<MODE, MB, NB>(P, acc, m0 + wm * WM, n0 + wn * WN, lane, blockIdx.z);
 }
 
-template <int BM, int BN, int MODE, int BKIND>
+template <int BM, int BN, int MODE, int BKIND, bool LNA = false>
 hipError_t launch(const GemmParams& P, dim3 grid, hipStream_t s) {
-  constexpr size_t lds = (size_t)2 * (BM + BN) * BK * sizeof(bf16_t);
-  const hipError_t e = ensure_dynamic_lds((const void*)gemm_bf16_kernel<BM, BN, MODE, BKIND>, (int)lds);
+  constexpr size_t lds = (size_t)2 * (BM + BN) * BK * sizeof(bf16_t) + (LNA ? BM * sizeof(float2) : 0);
+  const hipError_t e = ensure_dynamic_lds((const void*)gemm_bf16_kernel<BM, BN, MODE, BKIND, LNA>, (int)lds);
   if (e != hipSuccess) return e;
-  gemm_bf16_kernel<BM, BN, MODE, BKIND><<<grid, 256, lds, s>>>(P);
+  gemm_bf16_kernel<BM, BN, MODE, BKIND, LNA><<<grid, 256, lds, s>>>(P);
   return hipGetLastError();
 }
 
@@ -251,10 +276,14 @@ int device_cus() {
 }
 
 hipError_t launch_gemm_bf16_proj(const void* A, int lda, int M, int K, const BMap& bm, int N,
-                                 const ProjEpi& ep, const RopeTable& rt, hipStream_t s) {
+                                 const ProjEpi& ep, const RopeTable& rt, hipStream_t s,
+                                 const float2* ln_stats, const void* ln_w) {
   GemmParams P = base_params(A, lda, M, K, bm, N);
   P.ep = ep;
   P.rt = rt;
+  P.ln_stats = ln_stats;
+  P.ln_w = (const bf16_t*)ln_w;
+  const bool lna = ln_stats != nullptr;
   P.tiles_n = (N + 255) / 256;
   // 128-row tiles when they need fewer rounds over the CUs, counting a 128 x 256 tile at
   // 0.6 of a 256 x 256 one (measured per-flop efficiency of the smaller tile).
@@ -263,10 +292,12 @@ hipError_t launch_gemm_bf16_proj(const void* A, int lda, int M, int K, const BMa
   const long long r128 = ((long long)((M + 127) / 128) * P.tiles_n + cus - 1) / cus;
   if (3 * r128 < 5 * r256) {
     P.tiles_m = (M + 127) / 128;
-    return launch<128, 256, MODE_PROJ, 1>(P, dim3(P.tiles_m * P.tiles_n), s);
+    return lna ? launch<128, 256, MODE_PROJ, 1, true>(P, dim3(P.tiles_m * P.tiles_n), s)
+               : launch<128, 256, MODE_PROJ, 1>(P, dim3(P.tiles_m * P.tiles_n), s);
   }
   P.tiles_m = (M + 255) / 256;
-  return launch<256, 256, MODE_PROJ, 1>(P, dim3(P.tiles_m * P.tiles_n), s);
+  return lna ? launch<256, 256, MODE_PROJ, 1, true>(P, dim3(P.tiles_m * P.tiles_n), s)
+             : launch<256, 256, MODE_PROJ, 1>(P, dim3(P.tiles_m * P.tiles_n), s);
 }
 
 int gemm_bf16_resid_splits(int M, int N, int K) {

@@ -27,6 +27,10 @@ struct GemmParams {
   RowStart rs;       // RESID: rows of batch rows that are not live are not stored
   ProjEpi ep;        // PROJ
   RopeTable rt;
+  // PROJ with the LayerNorm fused: A is the layer input x, each A piece is normalized in
+  // registers as (x - mean) * rstd * ln_w before it is staged in LDS.
+  const float2* ln_stats;  // [M] (mean, rstd)
+  const bf16_t* ln_w;      // [K]
 };
 
 constexpr int BK = 64;

@@ -163,8 +163,14 @@ hipError_t launch_layernorm(int dtype, const void* x, const void* w, float eps, 
 
 // bf16 MFMA GEMMs, C[m, n] = sum_k A[m, k] * B[n, k], A [M, lda] bf16.
 // Fused projection epilogue (MRoPE, q/k/v scatter, SwiGLU); N = virtual projection width.
+// ln_stats != NULL: A is the layer input x and the LayerNorm is fused: each A piece is
+// normalized in registers, (x - mean) * rstd * ln_w with the rows' (mean, rstd) from
+// launch_ln_stats, before it is staged in LDS.
 hipError_t launch_gemm_bf16_proj(const void* A, int lda, int M, int K, const BMap& bm, int N,
-                                 const ProjEpi& ep, const RopeTable& rt, hipStream_t s);
+                                 const ProjEpi& ep, const RopeTable& rt, hipStream_t s,
+                                 const float2* ln_stats = nullptr, const void* ln_w = nullptr);
+// Per-row (mean, rstd) of bf16 rows [rows, D], the LayerNorm kernel's own values.
+hipError_t launch_ln_stats(const void* x, float eps, float2* stats, int rows, int D, hipStream_t s);
 // out[m, n] = x[m, n] + C (bf16; out may alias x); rows m of batch rows b = m / rs.L that
 // are not live (RowStart) are not stored.
 hipError_t launch_gemm_bf16_resid(const void* A, int lda, int M, int K, const BMap& bm, int N,

@@ -17,10 +17,13 @@ namespace {
 constexpr int kRowsPerBlock = 4;
 
 // VPL: values per lane held in registers (D <= 64 * VPL); bf16 loads are 8 wide.
-template <typename T, int VPL>
+// STATS: write only the row's (mean, rstd) to stats[row] (the fused projection GEMM then
+// normalizes its A tiles itself, with the same values).
+template <typename T, int VPL, bool STATS = false>
 __global__ __launch_bounds__(256) void layernorm_kernel(const T* __restrict__ x,
                                                         const T* __restrict__ w, float eps,
-                                                        T* __restrict__ a, int rows, int D, long long ldx) {
+                                                        T* __restrict__ a, int rows, int D, long long ldx,
+                                                        float2* __restrict__ stats = nullptr) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -32,7 +35,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const T* __restrict__ x,
   // Small rows also fetch the weight up front, so its loads overlap the row's instead of
   // following the two reductions.
   using W16 = typename std::conditional<sizeof(T) == 2, u32x4_t, float4>::type;
-  constexpr bool kEarlyW = NV <= 8;
+  constexpr bool kEarlyW = NV <= 8 && !STATS;
   W16 wpre[kEarlyW ? NV : 1];
   if constexpr (kEarlyW) {
 #pragma unroll
@@ -79,6 +82,10 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const T* __restrict__ x,
   }
   const float var = wave_sum(q) / (float)D;
   const float rstd = 1.0f / sqrtf(var + eps);
+  if constexpr (STATS) {
+    if (lane == 0) stats[row] = make_float2(mean, rstd);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int e = (i * 64 + lane) * V;
@@ -123,6 +130,16 @@ hipError_t launch_t(const void* x, long long ldx, const void* w, float eps, void
 }
 
 }  // namespace
+
+hipError_t launch_ln_stats(const void* x, float eps, float2* stats, int rows, int D, hipStream_t s) {
+  const dim3 grid((rows + kRowsPerBlock - 1) / kRowsPerBlock);
+  const bf16_t* xp = (const bf16_t*)x;
+  if (D <= 64 * 8) layernorm_kernel<bf16_t, 8, true><<<grid, 256, 0, s>>>(xp, nullptr, eps, nullptr, rows, D, D, stats);
+  else if (D <= 64 * 32) layernorm_kernel<bf16_t, 32, true><<<grid, 256, 0, s>>>(xp, nullptr, eps, nullptr, rows, D, D, stats);
+  else if (D <= 64 * 64) layernorm_kernel<bf16_t, 64, true><<<grid, 256, 0, s>>>(xp, nullptr, eps, nullptr, rows, D, D, stats);
+  else layernorm_kernel<bf16_t, 256, true><<<grid, 256, 0, s>>>(xp, nullptr, eps, nullptr, rows, D, D, stats);
+  return hipGetLastError();
+}
 
 hipError_t launch_layernorm(int dtype, const void* x, const void* w, float eps, void* a, int rows,
                             int D, hipStream_t s, long long ldx) {

@@ -92,6 +92,16 @@ typedef struct {
   float ln_eps;
   int32_t dtype;         /* compass_dtype */
   int32_t rope_layout;   /* compass_rope_layout; 0 = interleaved */
+  int32_t ln_fuse;       /* bf16 prefill only: 0 (default) = LayerNorm kernel writing the
+                            normalized bf16 rows, then the projection GEMM; 1 = the LayerNorm
+                            fused into the projection GEMM ("Text decoder forward": one shared
+                            LayerNorm feeding both branches): a statistics pass writes each
+                            row's (mean, rstd), and the GEMM normalizes every A tile in
+                            registers, (x - mean) * rstd * ln_w, as it stages it into LDS.
+                            The two give bitwise identical results. 0 is faster on MI355X:
+                            each A row block is staged by every column tile (76 of them at
+                            the Compass widths), so normalizing there costs more than the
+                            LayerNorm kernel it saves. Decode and fp32 ignore the field. */
 } compass_layer_desc;
 
 /* Weights of one layer, nn.Linear layout [out, in], no biases (section "Weight keys":

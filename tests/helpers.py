@@ -24,13 +24,14 @@ def cdtype(shape: LayerShape) -> int:
     return 1 if shape.dtype == "bf16" else 0
 
 
-def desc(shape: LayerShape):
+def desc(shape: LayerShape, ln_fuse: int = 0):
     b = B()
     return b.make_desc(shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.intermediate,
                        b.COMPASS_SLIDING if shape.kind == "sliding" else b.COMPASS_FULL,
                        shape.window if shape.kind == "sliding" else 0, shape.mrope_section, shape.rope_theta,
                        shape.ln_eps, cdtype(shape),
-                       b.COMPASS_ROPE_SECTIONS if shape.rope_layout == "sections" else b.COMPASS_ROPE_INTERLEAVED)
+                       b.COMPASS_ROPE_SECTIONS if shape.rope_layout == "sections" else b.COMPASS_ROPE_INTERLEAVED,
+                       ln_fuse)
 
 
 def to_dev(a: np.ndarray, dtype) -> torch.Tensor:

@@ -86,6 +86,7 @@ CASES = [
     ("eps nan", dict(ln_eps=float("nan")), "INVALID"),
     ("odd head mix", dict(n_q_heads=3, n_kv_heads=1, head_dim=64), "UNSUPPORTED"),
     ("rope layout 2", dict(rope_layout=2), "INVALID"),
+    ("ln_fuse 2", dict(ln_fuse=2), "INVALID"),
 ]
 
 

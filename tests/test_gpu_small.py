@@ -203,6 +203,8 @@ def test_window_at_least_L_equals_full_causal_without_rope_difference():
 # ------------------------------------------------------------------------------ decode
 DECODE_CASES = [
     ("bf16", "sliding", 128, 4, 1, 256, 512, 40),
+    ("bf16", "sliding", 128, 8, 1, 512, 512, 300),   # 8 query heads per kv head
+    ("bf16", "full", 64, 8, 1, 256, 512, 0),
     ("bf16", "full", 128, 4, 1, 256, 512, 0),
     ("bf16", "sliding", 64, 8, 2, 256, 512, 300),
     ("f32", "sliding", 64, 4, 1, 256, 1024, 32),
