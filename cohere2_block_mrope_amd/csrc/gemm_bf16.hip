@@ -237,8 +237,20 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams P) {
     step(kt, false, false);
   }
 
-  if constexpr (MODE == MODE_ARGMAX) argmax_epilogue<MB, NB>(P, acc, m0 + wm * WM, n0 + wn * WN, 2 * tn + wn, lane);
-  else gemm_epilogue<MODE, MB, NB>(P, acc, m0 + wm * WM, n0 + wn * WN, lane, blockIdx.z);
+  if constexpr (MODE == MODE_ARGMAX) {
+    argmax_epilogue<MB, NB>(P, acc, m0 + wm * WM, n0 + wn * WN, 2 * tn + wn, lane);
+  } else if constexpr (MODE == MODE_PROJ) {
+    // Tiles with q / k / v columns stage their rows' data in LDS (free after the main loop's
+    // last barrier) for the q / k / v epilogue.
+    ProjRow* s_row = reinterpret_cast<ProjRow*>(smem);
+    if (n0 < (P.ep.nq64 + 2 * P.ep.nk64) * 64) {  // uniform over the workgroup
+      stage_proj_rows<BM>(P, m0, s_row, tid);
+      __syncthreads();
+    }
+    gemm_epilogue<MODE, MB, NB>(P, acc, m0 + wm * WM, n0 + wn * WN, lane, blockIdx.z, s_row + wm * WM);
+  } else {
+    gemm_epilogue<MODE, MB, NB>(P, acc, m0 + wm * WM, n0 + wn * WN, lane, blockIdx.z);
+  }
 }
 
 template <int BM, int BN, int MODE, int BKIND, bool LNA = false>

@@ -79,11 +79,14 @@ __device__ __forceinline__ void load_group(const f32x16_t (&acc)[MB][NB], int i,
   for (int t = 0; t < 4; ++t) v[t] = acc[i][j][4 * g + t];
 }
 
+// dst is device (global) memory: the store is issued as a global store even where the
+// compiler cannot trace dst back to a kernel argument (a flat store would also count as an
+// LDS / scalar-memory operation in the waits that follow it).
 __device__ __forceinline__ void store_bf16x4(bf16_t* dst, const float (&v)[4]) {
   u32x2_t o;
   o.x = pack_bf2(v[0], v[1]);
   o.y = pack_bf2(v[2], v[3]);
-  *reinterpret_cast<u32x2_t*>(dst) = o;
+  *(__attribute__((address_space(1))) u32x2_t*)dst = o;
 }
 // The same with a streaming hint: for outputs no later kernel reads while they could still
 // be in this XCD's L2, so they leave no dirty lines for the write-back at the kernel's end.
@@ -92,6 +95,63 @@ __device__ __forceinline__ void store_bf16x4_nt(bf16_t* dst, const float (&v)[4]
   o.x = pack_bf2(v[0], v[1]);
   o.y = pack_bf2(v[2], v[3]);
   __builtin_nontemporal_store(o, reinterpret_cast<u32x2_t*>(dst));
+}
+
+// Per-row data of the fused projection epilogue, staged in LDS by the workgroup (one row
+// per thread) after the main loop, so that the loads it takes (positions, decode cache
+// indices, chunk starts, varlen sequences) are issued once per row and together, and the
+// waves' epilogues read them from LDS: an LDS read does not wait for earlier global stores,
+// while a global load does (global loads and stores retire through one in-order counter).
+struct ProjRow {
+  int b, lq;    // q: batch row and query index
+  int bkv, lc;  // k / v: cache row and cache index
+  float pt, ph, pw;
+  int kv;       // 1: the row's K / V are written
+};
+
+template <int BM>
+__device__ __forceinline__ void stage_proj_rows(const GemmParams& P, int m0, ProjRow* s_row, int tid) {
+  const ProjEpi& E = P.ep;
+  for (int r = tid; r < BM; r += 256) {
+    const int m = m0 + r;
+    const int mm = min(m, P.M - 1);
+    int pi[3] = {0, 0, 0};
+    if (E.rope) {
+#pragma unroll
+      for (int a = 0; a < 3; ++a) pi[a] = E.pos[(size_t)a * E.pos_stride + mm];
+    }
+    int b, l;
+    if (E.decode) { b = mm; l = E.lens[mm]; } else { b = mm / E.L; l = mm - b * E.L; }
+    // Cache row and index of this row's K/V: chunked prefill continues after kv_start[b]
+    // tokens (rows whose chunk does not fit are not written); a packed varlen row goes to
+    // its sequence's cache row (or stays in the packed scratch).
+    int bkv = b, lc = l;
+    bool kv = m < P.M;
+    if (!E.decode) {
+      if (E.row_seq) {
+        const int sq = E.row_seq[mm];
+        kv = kv && sq >= 0;
+        if (E.kv_by_seq && sq >= 0) {
+          bkv = sq;
+          lc = (E.kv_start ? E.kv_start[sq] : 0) + (mm - E.cu[sq]);
+        }
+      } else if (E.kv_start) {
+        const int s0 = E.kv_start[b];
+        kv = kv && s0 >= 0 && s0 <= E.cap - E.L;
+        lc = l + (kv ? s0 : 0);
+      }
+    }
+    ProjRow R;
+    R.b = b;
+    R.lq = E.decode ? 0 : l;
+    R.bkv = bkv;
+    R.lc = lc;
+    R.pt = (float)pi[0];
+    R.ph = (float)pi[1];
+    R.pw = (float)pi[2];
+    R.kv = kv ? 1 : 0;
+    s_row[r] = R;
+  }
 }
 
 // q / k / v part of the fused projection epilogue for head_dim HD. For HD = 128 the
@@ -103,7 +163,7 @@ __device__ __forceinline__ void store_bf16x4_nt(bf16_t* dst, const float (&v)[4]
 // hardware sin / cos.
 template <int HD, int MB, int NB>
 __device__ __forceinline__ void proj_qkv_epilogue(const GemmParams& P, const f32x16_t (&acc)[MB][NB], int mw0,
-                                                  int ch0, int lane) {
+                                                  int ch0, int lane, const ProjRow* s_row) {
   constexpr int PB = HD / 64;          // 32-column blocks per half head
   constexpr int NHEAD = 128 / HD;      // heads per wave
   constexpr int HALF = HD / 2;
@@ -162,37 +222,16 @@ __device__ __forceinline__ void proj_qkv_epilogue(const GemmParams& P, const f32
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int m = mw0 + 32 * i + 8 * g + rowq;
-        const int mm = min(m, P.M - 1);
-        int b, l;
-        if (E.decode) { b = mm; l = E.lens[b]; } else { b = mm / E.L; l = mm - b * E.L; }
-        // Cache row and index of this row's K/V: chunked prefill continues after
-        // kv_start[b] tokens (rows whose chunk does not fit are not written); a packed
-        // varlen row goes to its sequence's cache row (or stays in the packed scratch).
-        int lc = l, bkv = b;
+        const ProjRow R = s_row[32 * i + 8 * g + rowq];  // s_row starts at the wave's first row
         bool store = m < P.M;
-        if (kind != 0 && !E.decode) {
-          if (E.row_seq) {
-            const int sq = E.row_seq[mm];
-            store = store && sq >= 0;
-            if (E.kv_by_seq && sq >= 0) {
-              bkv = sq;
-              lc = (E.kv_start ? E.kv_start[sq] : 0) + (mm - E.cu[sq]);
-            }
-          } else if (E.kv_start) {
-            const int s0 = E.kv_start[b];
-            store = store && s0 >= 0 && s0 <= E.cap - E.L;
-            lc = l + (store ? s0 : 0);
-          }
-        }
         bf16_t* dst;
-        if (kind == 0) dst = base + (((size_t)b * E.Hq + head) * E.Lq + (E.decode ? 0 : l)) * HD;
-        else dst = base + (((size_t)bkv * E.Hkv + head) * E.cap + lc) * HD;
-        float pt = 0.f, ph = 0.f, pw = 0.f;
-        if (rot) {
-          pt = (float)E.pos[mm];
-          ph = (float)E.pos[(size_t)E.pos_stride + mm];
-          pw = (float)E.pos[2 * (size_t)E.pos_stride + mm];
+        if (kind == 0) {
+          dst = base + (((size_t)R.b * E.Hq + head) * E.Lq + R.lq) * HD;
+        } else {
+          store = store && R.kv;
+          dst = base + (((size_t)R.bkv * E.Hkv + head) * E.cap + R.lc) * HD;
         }
+        const float pt = R.pt, ph = R.ph, pw = R.pw;
 #pragma unroll
         for (int jj = 0; jj < PB; ++jj) {
           float x1[4], x2[4];
@@ -262,11 +301,53 @@ __device__ __forceinline__ void argmax_epilogue(const GemmParams& P, const f32x1
 // launchers); SCALED falls back to element stores otherwise.
 template <int MODE, int MB, int NB>
 __device__ __forceinline__ void gemm_epilogue(const GemmParams& P, f32x16_t (&acc)[MB][NB], int mw0,
-                                              int nw0, int lane, int z) {
+                                              int nw0, int lane, int z, const ProjRow* s_row = nullptr) {
   const int col4 = (lane & 31) & ~3;
   const int rowq = epi_row(lane);
-  if constexpr (MODE == MODE_RAW || MODE == MODE_RESID || MODE == MODE_SCALED) {
-    const bool vec = MODE != MODE_SCALED || ((P.N & 3) == 0 && (P.ldof & 3) == 0);
+  if constexpr (MODE == MODE_RESID) {
+    // The residual values and row flags of two row blocks at a time are loaded before their
+    // first store: global loads and stores retire through one in-order counter, so a load
+    // issued after a store would also wait for that store (one memory round trip per row
+    // group instead of one per two row blocks).
+    constexpr int IC = MB < 2 ? MB : 2;
+#pragma unroll
+    for (int i0 = 0; i0 < MB; i0 += IC) {
+      bool live[IC][4];
+      u32x2_t xv[IC][NB][4];
+#pragma unroll
+      for (int ii = 0; ii < IC; ++ii)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int m = mw0 + 32 * (i0 + ii) + 8 * g + rowq;
+          live[ii][g] = m < P.M && row_live_m(P.rs, m);
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            const int n = nw0 + 32 * j + col4;
+            if (live[ii][g] && n < P.N) xv[ii][j][g] = *reinterpret_cast<const u32x2_t*>(P.x + (size_t)m * P.ldo + n);
+          }
+        }
+#pragma unroll
+      for (int ii = 0; ii < IC; ++ii)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float v[4];
+            load_group(acc, i0 + ii, j, g, v);
+            quad_transpose(v, lane);
+            const int m = mw0 + 32 * (i0 + ii) + 8 * g + rowq;
+            const int n = nw0 + 32 * j + col4;
+            if (!live[ii][g] || n >= P.N) continue;
+            const u32x2_t x2 = xv[ii][j][g];
+            v[0] += __uint_as_float(x2.x << 16);
+            v[1] += __uint_as_float(x2.x & 0xffff0000u);
+            v[2] += __uint_as_float(x2.y << 16);
+            v[3] += __uint_as_float(x2.y & 0xffff0000u);
+            store_bf16x4_nt(P.out + (size_t)m * P.ldo + n, v);
+          }
+    }
+  } else if constexpr (MODE == MODE_RAW || MODE == MODE_SCALED) {
+    const bool vec = MODE == MODE_RAW || ((P.N & 3) == 0 && (P.ldof & 3) == 0);
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -279,19 +360,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& P, f32x16_t (&ac
           const int m = mw0 + 32 * i + 8 * g + rowq;
           const int n = nw0 + 32 * j + col4;
           if (m >= P.M || n >= P.N) continue;
-          if constexpr (MODE == MODE_RESID) {
-            if (!row_live_m(P.rs, m)) continue;
-          }
           if constexpr (MODE == MODE_RAW) {
             *reinterpret_cast<f32x4_t*>(P.raw + ((size_t)z * P.M + m) * P.N + n) = f32x4_t{v[0], v[1], v[2], v[3]};
-          } else if constexpr (MODE == MODE_RESID) {
-            const size_t o = (size_t)m * P.ldo + n;
-            const u32x2_t xv = *reinterpret_cast<const u32x2_t*>(P.x + o);
-            v[0] += __uint_as_float(xv.x << 16);
-            v[1] += __uint_as_float(xv.x & 0xffff0000u);
-            v[2] += __uint_as_float(xv.y << 16);
-            v[3] += __uint_as_float(xv.y & 0xffff0000u);
-            store_bf16x4_nt(P.out + o, v);
           } else {
             float* d = P.outf + (size_t)m * P.ldof + n;
             if (vec) {
@@ -312,25 +382,39 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& P, f32x16_t (&ac
     const int ve = E.nq64 + 2 * E.nk64;
     if (ch0 >= ve) {
       // SwiGLU: chunk ch0 holds gate columns, ch0 + 1 the up columns of the same c.
+      // Every value of the wave is computed (and packed to bf16) before the first store: a
+      // vector-memory operation that followed a store (a spill reload, say) would wait for
+      // it, global loads and stores retiring through one in-order counter.
       bf16_t* act = (bf16_t*)E.act + E.act_col0 + ((ch0 - ve) >> 1) * 64 + col4;
+      u32x2_t o[MB][4][2];
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int m = mw0 + 32 * i + 8 * g + rowq;
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             float v[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) v[t] = silu_f(acc[i][j][4 * g + t]) * acc[i][j + 2][4 * g + t];
             quad_transpose(v, lane);
-            if (m < P.M) store_bf16x4_nt(act + (size_t)m * E.ldact + 32 * j, v);
+            o[i][g][j].x = pack_bf2(v[0], v[1]);
+            o[i][g][j].y = pack_bf2(v[2], v[3]);
+          }
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int m = mw0 + 32 * i + 8 * g + rowq;
+          if (m < P.M) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              __builtin_nontemporal_store(o[i][g][j], reinterpret_cast<u32x2_t*>(act + (size_t)m * E.ldact + 32 * j));
           }
         }
       return;
     }
-    if (E.hd == 128) proj_qkv_epilogue<128>(P, acc, mw0, ch0, lane);
-    else proj_qkv_epilogue<64>(P, acc, mw0, ch0, lane);
+    if (E.hd == 128) proj_qkv_epilogue<128>(P, acc, mw0, ch0, lane, s_row);
+    else proj_qkv_epilogue<64>(P, acc, mw0, ch0, lane, s_row);
   }
 }
 
