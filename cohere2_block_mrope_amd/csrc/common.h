@@ -116,4 +116,29 @@ __device__ __forceinline__ void quad_transpose(float (&v)[4], int lane) {
   v[3] = hi ? a3 : p1;
 }
 
+// The same transpose for values stored as bf16: each lane rounds its rows to bf16 in pairs
+// first, so every exchange moves two values (10 VALU operations per 4 values instead of
+// 18). On entry lane q holds rows 0..3 of column q; on exit the two dwords hold columns
+// 0, 1 and 2, 3 (low half first) of row 2 (q & 1) + (q >> 1). All 64 lanes must be active.
+__device__ __forceinline__ u32x2_t quad_transpose_bf16(const float (&v)[4], int lane) {
+  const bool odd = lane & 1, hi = lane & 2;
+  const uint32_t a = pack_bf2(v[0], v[1]);  // rows 0, 1 of column q
+  const uint32_t b = pack_bf2(v[2], v[3]);  // rows 2, 3 of column q
+  // Exchange with lane q ^ 1: even lanes keep rows 0, 1 and receive them for column q + 1,
+  // odd lanes keep rows 2, 3 and receive them for column q - 1.
+  const uint32_t own = odd ? b : a;
+  const uint32_t rcv = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? a : b), 0xB1, 0xF, 0xF, false);
+  // v_perm byte selects (bytes 0..3: own, 4..7: rcv): x = the lower row of the lane's pair
+  // over the two columns (lower column first), y = the upper row.
+  const uint32_t x = __builtin_amdgcn_perm(rcv, own, odd ? 0x01000504u : 0x05040100u);
+  const uint32_t y = __builtin_amdgcn_perm(rcv, own, odd ? 0x03020706u : 0x07060302u);
+  // Exchange with lane q ^ 2: lanes q < 2 keep the lower row and receive its other two
+  // columns; lanes q >= 2 keep the upper row and receive its first two columns.
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(hi ? x : y), 0x4E, 0xF, 0xF, false);
+  u32x2_t o;
+  o.x = hi ? r2 : x;
+  o.y = hi ? y : r2;
+  return o;
+}
+
 static constexpr float kLog2e = 1.4426950408889634f;

@@ -97,6 +97,19 @@ __device__ __forceinline__ void store_bf16x4_nt(bf16_t* dst, const float (&v)[4]
   __builtin_nontemporal_store(o, reinterpret_cast<u32x2_t*>(dst));
 }
 
+// Regroups two transposed 4-column pieces of each lane's row, p0 at columns col4.. and p1
+// at 32 + col4.. of a 64-column span, across the half-waves (v_permlane32_swap): afterwards
+// p0 belongs to row (rowq & 3) and p1 to row (rowq & 3) + 4 of the 8-row group, both at
+// column (lane >= 32 ? 32 : 0) + col4, so that one store instruction writes 4 rows x 128
+// contiguous bytes (whole cache lines) instead of 8 rows x 64 bytes.
+__device__ __forceinline__ void line_swap(u32x2_t& p0, u32x2_t& p1) {
+  const auto a = __builtin_amdgcn_permlane32_swap(p0.x, p1.x, false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(p0.y, p1.y, false, false);
+  const unsigned a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
+  p0 = u32x2_t{a0, b0};
+  p1 = u32x2_t{a1, b1};
+}
+
 // Per-row data of the fused projection epilogue, staged in LDS by the workgroup (one row
 // per thread) after the main loop, so that the loads it takes (positions, decode cache
 // indices, chunk starts, varlen sequences) are issued once per row and together, and the
@@ -385,7 +398,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& P, f32x16_t (&ac
       // Every value of the wave is computed (and packed to bf16) before the first store: a
       // vector-memory operation that followed a store (a spill reload, say) would wait for
       // it, global loads and stores retiring through one in-order counter.
-      bf16_t* act = (bf16_t*)E.act + E.act_col0 + ((ch0 - ve) >> 1) * 64 + col4;
+      bf16_t* act = (bf16_t*)E.act + E.act_col0 + ((ch0 - ve) >> 1) * 64 + (lane >= 32 ? 32 : 0) + col4;
+      const int rlo = rowq & 3;
       u32x2_t o[MB][4][2];
 #pragma unroll
       for (int i = 0; i < MB; ++i)
@@ -396,19 +410,17 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& P, f32x16_t (&ac
             float v[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) v[t] = silu_f(acc[i][j][4 * g + t]) * acc[i][j + 2][4 * g + t];
-            quad_transpose(v, lane);
-            o[i][g][j].x = pack_bf2(v[0], v[1]);
-            o[i][g][j].y = pack_bf2(v[2], v[3]);
+            o[i][g][j] = quad_transpose_bf16(v, lane);
           }
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int m = mw0 + 32 * i + 8 * g + rowq;
-          if (m < P.M) {
+          line_swap(o[i][g][0], o[i][g][1]);
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-              __builtin_nontemporal_store(o[i][g][j], reinterpret_cast<u32x2_t*>(act + (size_t)m * E.ldact + 32 * j));
+          for (int h = 0; h < 2; ++h) {
+            const int m = mw0 + 32 * i + 8 * g + 4 * h + rlo;
+            if (m < P.M) __builtin_nontemporal_store(o[i][g][h], reinterpret_cast<u32x2_t*>(act + (size_t)m * E.ldact));
           }
         }
       return;
