@@ -280,6 +280,11 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
     // per dot2 against (1, 1).
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    // Wave priority: the exponentials (with the next tile's S^T MFMAs among them) are the
+    // longer dependent chain of an iteration, the PV MFMAs below need no VALU. Raising the
+    // priority for the first part and dropping it for the second lets the other wave of the
+    // SIMD (the other workgroup's) issue its exponentials while this one's PV MFMAs run.
+    __builtin_amdgcn_s_setprio(1);
     float rs = 0.f;
     uint32_t pw[2][2][4];
     bf16x8_t kf[3];
@@ -336,6 +341,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
       const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4_t))(v0 + 8 * VS));
       return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
+    __builtin_amdgcn_s_setprio(0);
     bf16x8_t vf[4];
 #pragma unroll
     for (int c = 0; c < 3; ++c) vf[c] = vfrag(c);
