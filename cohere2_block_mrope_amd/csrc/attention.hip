@@ -370,6 +370,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(AttnParams P) {
   qk(0, Sa);
   if (kt0 + 2 <= kt1) gload(rk, krs, kt0 + 2);
   if (kt0 + 1 <= kt1) gload(rv, vrs, kt0 + 1);
+  // The first iteration stores K(kt0 + 2) into K buffer 0, which every wave has just read.
+  __syncthreads();
   // Iteration t (PAR = (t - kt0) & 1, a constant of the unrolled loop, so every LDS address
   // is a base plus an immediate): S of tile t + 1 from K buffer PAR ^ 1, softmax and PV of
   // tile t from V buffer PAR, then K(t + 2) into K buffer PAR (K(t) was last read in
