@@ -8,13 +8,17 @@
 //   * the deepstack row update h[rows] += ds ("after layers 0, 1, 2").
 // Each thread handles one rotation pair (or one gate/up pair) so that both members
 // of the pair are combined in registers.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
 namespace compass {
 namespace {
 
-template <typename T>
+// MAXS > 0: at most MAXS splits, every partial load issued before the first add (one memory
+// round trip); MAXS = 0: any count, four splits' loads in flight at a time.
+template <typename T, int MAXS>
 __global__ __launch_bounds__(256) void proj_epilogue_kernel(const float* __restrict__ raw, int splits,
                                                             int M, int N, ProjEpi E, RopeTable rt) {
   const int hd = E.hd, half = hd >> 1;
@@ -25,7 +29,7 @@ __global__ __launch_bounds__(256) void proj_epilogue_kernel(const float* __restr
   const int m = (int)(idx / units);
   const int u = (int)(idx - (long long)m * units);
   const size_t slab = (size_t)M * N;
-  // Sum of the split-K partials of column c, four splits' loads in flight at a time.
+  // Sum of the split-K partials of column c: groups of four splits, then the rest, in order.
   auto sum = [&](int c) {
     const float* r = raw + (size_t)m * N + c;
     float s = 0.f;
@@ -35,16 +39,49 @@ __global__ __launch_bounds__(256) void proj_epilogue_kernel(const float* __restr
     for (; z < splits; ++z) s += r[z * slab];
     return s;
   };
-  // The columns' sums are loaded before the row's cache index (independent loads).
+  // The same sum from partials already loaded (the same additions in the same order).
+  auto sum_loaded = [&](const float* v) {
+    float s = 0.f;
+    int z = 0;
+#pragma unroll
+    for (; z + 4 <= MAXS; z += 4)
+      if (z + 4 <= splits) s += (v[z] + v[z + 1]) + (v[z + 2] + v[z + 3]);
+#pragma unroll
+    for (int y = 0; y < MAXS; ++y)
+      if (y >= (splits & ~3) && y < splits) s += v[y];
+    return s;
+  };
   const bool gu = u >= qkv_units;
   const int hh = u / half, f = u - hh * half;
   const int c1 = hh * hd + f;
   const int cg = u - qkv_units;                                             // gate/up column
   const int vg = (E.nq64 + 2 * E.nk64) * 64 + (cg >> 6) * 128 + (cg & 63);  // virtual gate col
-  float x1 = sum(gu ? vg : c1), x2 = sum(gu ? vg + 64 : c1 + half);
+  const int ca = gu ? vg : c1, cb = gu ? vg + 64 : c1 + half;
+  // Every load of the thread (partials, cache index, position) is issued before its first use.
+  float va[MAXS > 0 ? MAXS : 1], vb[MAXS > 0 ? MAXS : 1];
+  if constexpr (MAXS > 0) {
+    const float* ra = raw + (size_t)m * N + ca;
+    const float* rb = raw + (size_t)m * N + cb;
+#pragma unroll
+    for (int z = 0; z < MAXS; ++z) {
+      va[z] = z < splits ? ra[z * slab] : 0.f;
+      vb[z] = z < splits ? rb[z * slab] : 0.f;
+    }
+  }
+  const int lens_b = E.decode ? E.lens[m] : 0;
+  const bool rot = E.rope && !gu && hh < E.Hq + E.Hkv;
+  const float p = rot ? (float)E.pos[(size_t)rope_axis(rt, f) * E.pos_stride + m] : 0.f;
+  float x1, x2;
+  if constexpr (MAXS > 0) {
+    x1 = sum_loaded(va);
+    x2 = sum_loaded(vb);
+  } else {
+    x1 = sum(ca);
+    x2 = sum(cb);
+  }
   int b, l, lc;
   if (E.decode) {
-    b = m; l = E.lens[b];
+    b = m; l = lens_b;
     if (l < 0 || l >= E.cap) return;
     lc = l;
   } else {
@@ -77,8 +114,7 @@ __global__ __launch_bounds__(256) void proj_epilogue_kernel(const float* __restr
     const int head = isk ? kv : kv - E.Hkv;
     dst = (T*)(isk ? E.kc : E.vc) + (((size_t)b * E.Hkv + head) * E.cap + lc) * hd;
   }
-  if (E.rope && hh < E.Hq + E.Hkv) {
-    const float p = (float)E.pos[(size_t)rope_axis(rt, f) * E.pos_stride + m];
+  if (rot) {
     float sn, cs;
     sincosf(p * rope_inv_freq(rt, f, hd), &sn, &cs);
     const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
@@ -89,8 +125,10 @@ __global__ __launch_bounds__(256) void proj_epilogue_kernel(const float* __restr
 }
 
 // out = x + sum of the split-K partials; four consecutive columns per thread (16-byte
-// partial loads), four splits' loads in flight at a time. N % 4 == 0.
-template <typename T>
+// partial loads). N % 4 == 0. SPL > 0: exactly SPL splits, every load issued before the first
+// add (one memory round trip); SPL = 0: any count, four splits' loads in flight at a time. The
+// additions run in the same order either way: groups of four, then the rest.
+template <typename T, int SPL>
 __global__ __launch_bounds__(256) void splitk_resid_kernel(const float* __restrict__ raw, int splits,
                                                            int M, int N, const T* x, T* out, RowStart rs) {
   const long long q = (long long)blockIdx.x * 256 + threadIdx.x;  // quad of columns
@@ -100,10 +138,21 @@ __global__ __launch_bounds__(256) void splitk_resid_kernel(const float* __restri
   const f32x4_t* r = reinterpret_cast<const f32x4_t*>(raw + idx);
   const size_t sq = slab / 4;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  int z = 0;
-  for (; z + 4 <= splits; z += 4)
-    acc += (r[z * sq] + r[(z + 1) * sq]) + (r[(z + 2) * sq] + r[(z + 3) * sq]);
-  for (; z < splits; ++z) acc += r[z * sq];
+  if constexpr (SPL > 0) {
+    f32x4_t v[SPL];
+#pragma unroll
+    for (int z = 0; z < SPL; ++z) v[z] = r[z * sq];
+    int z = 0;
+#pragma unroll
+    for (; z + 4 <= SPL; z += 4) acc += (v[z] + v[z + 1]) + (v[z + 2] + v[z + 3]);
+#pragma unroll
+    for (; z < SPL; ++z) acc += v[z];
+  } else {
+    int z = 0;
+    for (; z + 4 <= splits; z += 4)
+      acc += (r[z * sq] + r[(z + 1) * sq]) + (r[(z + 2) * sq] + r[(z + 3) * sq]);
+    for (; z < splits; ++z) acc += r[z * sq];
+  }
   if (!row_live_m(rs, (int)(idx / N))) return;  // rows left untouched
 #pragma unroll
   for (int e = 0; e < 4; ++e) out[idx + e] = Elt<T>::from_f(Elt<T>::to_f(x[idx + e]) + acc[e]);
@@ -128,8 +177,13 @@ hipError_t launch_proj_epilogue(int dtype, const float* raw, int splits, int M, 
                                 const ProjEpi& ep, const RopeTable& rt, hipStream_t s) {
   const long long units = (long long)M * ((ep.Hq + 2 * ep.Hkv) * (ep.hd / 2) + ep.I);
   const dim3 grid((unsigned)((units + 255) / 256));
-  if (dtype == 1) proj_epilogue_kernel<bf16_t><<<grid, 256, 0, s>>>(raw, splits, M, N, ep, rt);
-  else proj_epilogue_kernel<float><<<grid, 256, 0, s>>>(raw, splits, M, N, ep, rt);
+  if (dtype == 1) {
+    if (splits <= 4) proj_epilogue_kernel<bf16_t, 4><<<grid, 256, 0, s>>>(raw, splits, M, N, ep, rt);
+    else proj_epilogue_kernel<bf16_t, 0><<<grid, 256, 0, s>>>(raw, splits, M, N, ep, rt);
+  } else {
+    if (splits <= 4) proj_epilogue_kernel<float, 4><<<grid, 256, 0, s>>>(raw, splits, M, N, ep, rt);
+    else proj_epilogue_kernel<float, 0><<<grid, 256, 0, s>>>(raw, splits, M, N, ep, rt);
+  }
   return hipGetLastError();
 }
 
@@ -139,10 +193,21 @@ hipError_t launch_splitk_resid(int dtype, const float* raw, int splits, int M, i
   const dim3 grid((unsigned)((n + 255) / 256));
   RowStart rs = rs_in;
   if (rs.L < 1) rs.L = 1;
-  if (dtype == 1)
-    splitk_resid_kernel<bf16_t><<<grid, 256, 0, s>>>(raw, splits, M, N, (const bf16_t*)x, (bf16_t*)out, rs);
-  else
-    splitk_resid_kernel<float><<<grid, 256, 0, s>>>(raw, splits, M, N, (const float*)x, (float*)out, rs);
+  auto go = [&](auto spl) {
+    constexpr int SPL = decltype(spl)::value;
+    if (dtype == 1)
+      splitk_resid_kernel<bf16_t, SPL><<<grid, 256, 0, s>>>(raw, splits, M, N, (const bf16_t*)x, (bf16_t*)out, rs);
+    else
+      splitk_resid_kernel<float, SPL><<<grid, 256, 0, s>>>(raw, splits, M, N, (const float*)x, (float*)out, rs);
+  };
+  switch (splits) {
+    case 1: go(std::integral_constant<int, 1>{}); break;
+    case 2: go(std::integral_constant<int, 2>{}); break;
+    case 4: go(std::integral_constant<int, 4>{}); break;
+    case 8: go(std::integral_constant<int, 8>{}); break;
+    case 16: go(std::integral_constant<int, 16>{}); break;
+    default: go(std::integral_constant<int, 0>{});
+  }
   return hipGetLastError();
 }
 
