@@ -243,6 +243,41 @@ def test_decode_parity(case):
     assert np.array_equal(kg.transpose(0, 2, 1, 3)[mask], kc.transpose(0, 2, 1, 3)[mask])
 
 
+@pytest.mark.parametrize("case", [c for c in DECODE_CASES if c[0] == "bf16"], ids=lambda c: "-".join(map(str, c)))
+def test_decode_reads_only_the_new_row_and_visible_keys(case):
+    """Every cache row from lens[b] on starts as NaN: row lens[b] is the new token's K/V,
+    written in the same step (the bf16 path appends it inside the attention kernel, which
+    then reads the chunk holding it), and rows past it are never visible. A stale read of
+    the new row, or any read past it that is not masked before the PV product, turns the
+    output NaN."""
+    dt, kind, hd, Hq, Hkv, D, I, win = case
+    sh = H.small_shape(dt, kind, hd, Hq, Hkv, D, I, win)
+    lens = np.array([0, 1, 63, 64, 255, 256, 257, 511, 700], np.int32)
+    Bn, cap = len(lens), 770
+    w, _, _ = layer_case(sh, 1, 8, seed=hd + Hq + 1)
+    x = H.rand_np(15, (Bn, D), bf16=True)
+    kc = H.rand_np(16, (Bn, Hkv, cap, hd), bf16=True)
+    vc = H.rand_np(17, (Bn, Hkv, cap, hd), bf16=True)
+    pos = O.decode_positions(lens, np.zeros(Bn, np.int64))
+    ref, knew, vnew = O.layer_decode(sh, w, x, pos, kc, vc, lens)
+    kn, vn = kc.copy(), vc.copy()
+    for i, n in enumerate(lens):
+        kn[i, :, n:] = np.nan
+        vn[i, :, n:] = np.nan
+    kd, vd = H.to_dev(kn, torch.bfloat16), H.to_dev(vn, torch.bfloat16)
+    out = H.run_decode(sh, H.weights_to_dev(sh, w), H.to_dev(x, torch.bfloat16), H.ints_to_dev(pos), kd, vd,
+                       H.ints_to_dev(lens))
+    torch.cuda.synchronize()
+    o = H.np64(out)
+    assert np.isfinite(o).all()
+    assert H.rel_err(o, ref) <= H.tol(sh)
+    kg, vg = H.np64(kd), H.np64(vd)
+    for i, n in enumerate(lens):
+        assert H.rel_err(kg[i, :, n], knew[i]) <= H.tol(sh)
+        assert H.rel_err(vg[i, :, n], vnew[i]) <= H.tol(sh)
+        assert np.isnan(kg[i, :, n + 1:]).all() and np.isnan(vg[i, :, n + 1:]).all()
+
+
 def test_decode_skips_rows_with_lens_out_of_range():
     sh = H.small_shape("bf16", "sliding", 128, 4, 1, 256, 512, 40)
     lens = np.array([5, 64, 63], np.int32)  # capacity 64: row 1 is out of range
