@@ -213,7 +213,7 @@ PrefillWs prefill_ws(const compass_layer_desc* d, long long B, long long L, long
   return w;
 }
 
-// Split-K factor of the skinny decode GEMMs: about 512 workgroups in total (measured on
+// Split-K factor of the 64 x 64 decode GEMM tiles: about 512 workgroups in total (measured on
 // MI355X: more splits cost more in the partial-sum traffic than they gain in
 // parallelism), and at least 256 K elements per split.
 int decode_splits(long long tiles, long long K) {
@@ -224,9 +224,20 @@ int decode_splits(long long tiles, long long K) {
   return (int)s;
 }
 
+// Split-K factor of the bf16 decode output GEMM on the skinny kernel (batches of at most 64
+// rows): about one workgroup per CU.
+int skinny_splits(long long tiles, long long K) {
+  if (tiles < 1) tiles = 1;
+  long long s = (256 + tiles / 2) / tiles;
+  if (s > K / 512) s = K / 512;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
 struct DecodeWs {
   size_t a, raw1, q, a2, part, raw2, total;
   int s1, s2, n_chunks;
+  int k2;  // splits of the output GEMM on the skinny bf16 kernel (0: it does not apply)
 };
 DecodeWs decode_ws(const compass_layer_desc* d, long long B, long long cap) {
   const Dims m = dims(d);
@@ -235,6 +246,9 @@ DecodeWs decode_ws(const compass_layer_desc* d, long long B, long long cap) {
   const long long tiles2 = ((B + 63) / 64) * ((m.D + 63) / 64);
   w.s1 = decode_splits(tiles1, m.D);
   w.s2 = decode_splits(tiles2, m.K2);
+  w.k2 = skinny_splits((m.D + 63) / 64, m.K2);
+  if (d->dtype != COMPASS_BF16 || !gemm_skinny_fits((int)B, (int)m.K2, (int)m.D, w.k2)) w.k2 = 0;
+  const long long r2 = w.s2 > w.k2 ? w.s2 : w.k2;
   const long long keys = d->kind == COMPASS_SLIDING ? (cap < d->window ? cap : d->window) : cap;
   const int ck = decode_chunk_keys(d->dtype, d->head_dim);
   w.n_chunks = (int)((keys + ck - 1) / ck);
@@ -245,7 +259,7 @@ DecodeWs decode_ws(const compass_layer_desc* d, long long B, long long cap) {
   w.q = off; off += up(B * m.qd * m.esz);
   w.a2 = off; off += up(B * m.K2 * m.esz);
   w.part = off; off += up(B * m.Hq * (long long)w.n_chunks * (m.hd + 2) * 4);
-  w.raw2 = off; off += up((long long)w.s2 * B * m.D * 4);
+  w.raw2 = off; off += up(r2 * B * m.D * 4);
   w.total = off;
   return w;
 }
@@ -648,7 +662,10 @@ static int decode_impl(const compass_layer_desc* d, const compass_layer_weights*
 
   (void)hipGetLastError();
   LAUNCH("layernorm", s, launch_layernorm(dt, x, wq ? wq->ln_w : w->ln_w, d->ln_eps, a, B, (int)m.D, s));
-  const int s1 = ws.s1, s2 = ws.s2;
+  // The output GEMM streams its weights through the skinny kernel when it applies (measured
+  // faster there; the projection keeps the 64 x 64 split-K tiles).
+  const bool skinny = !wq && ws.k2 > 0;
+  const int s1 = ws.s1, s2 = skinny ? ws.k2 : ws.s2;
   if (wq)
     LAUNCH("gemm_proj_decode_q4", s, launch_gemm_q4_raw(a, (int)m.D, B, (int)m.D, proj_q4map(d, wq), (int)m.Nv, s1,
                                                         raw1, s));
@@ -667,6 +684,9 @@ static int decode_impl(const compass_layer_desc* d, const compass_layer_weights*
   if (wq)
     LAUNCH("gemm_out_decode_q4", s, launch_gemm_q4_raw(a2, (int)m.K2, B, (int)m.K2, out_q4map(d, wq), (int)m.D, s2,
                                                        raw2, s));
+  else if (skinny)
+    LAUNCH("gemm_out_decode", s, launch_gemm_skinny_raw(a2, (int)m.K2, B, (int)m.K2, out_bmap(d, w), (int)m.D, s2,
+                                                        raw2, s));
   else if (dt == COMPASS_BF16)
     LAUNCH("gemm_out_decode", s, launch_gemm_bf16_raw(a2, (int)m.K2, B, (int)m.K2, out_bmap(d, w), (int)m.D, s2,
                                                       raw2, s));

@@ -187,6 +187,12 @@ int gemm_bf16_argmax(const void* A, int lda, int M, int K, const BMap& bm, int N
 // skinny decode GEMMs; the _wide variant uses 256 x 256 tiles).
 hipError_t launch_gemm_bf16_raw(const void* A, int lda, int M, int K, const BMap& bm, int N,
                                 int splits, float* raw, hipStream_t s);
+// The same raw partial sums for at most 64 rows and a BMap of kind 2 (the decode output
+// projection [Wo | Wd]; N a multiple of 4), with K / splits equal to 512, 640, 1024 or 1280: one 64-column
+// tile per workgroup and K-slice, weights loaded several steps ahead.
+bool gemm_skinny_fits(int M, int K, int N, int splits);
+hipError_t launch_gemm_skinny_raw(const void* A, int lda, int M, int K, const BMap& bm, int N, int splits,
+                                  float* raw, hipStream_t s);
 hipError_t launch_gemm_bf16_raw_wide(const void* A, int lda, int M, int K, const BMap& bm, int N,
                                      int splits, float* raw, hipStream_t s);
 // K splits for the residual output GEMM: 1 when 128 x 256 tiles fill the CUs, else enough

@@ -246,10 +246,9 @@ def test_decode_parity(case):
 @pytest.mark.parametrize("case", [c for c in DECODE_CASES if c[0] == "bf16"], ids=lambda c: "-".join(map(str, c)))
 def test_decode_reads_only_the_new_row_and_visible_keys(case):
     """Every cache row from lens[b] on starts as NaN: row lens[b] is the new token's K/V,
-    written in the same step (the bf16 path appends it inside the attention kernel, which
-    then reads the chunk holding it), and rows past it are never visible. A stale read of
-    the new row, or any read past it that is not masked before the PV product, turns the
-    output NaN."""
+    written in the same step before the attention reads it, and rows past it are never
+    visible. A read of the new row before it is written, or any read past it that is not
+    masked before the PV product, turns the output NaN."""
     dt, kind, hd, Hq, Hkv, D, I, win = case
     sh = H.small_shape(dt, kind, hd, Hq, Hkv, D, I, win)
     lens = np.array([0, 1, 63, 64, 255, 256, 257, 511, 700], np.int32)
