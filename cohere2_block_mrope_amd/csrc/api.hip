@@ -184,6 +184,15 @@ struct PrefillWs {
   int max_tiles;
 };
 // Varlen prefill (n_seq > 0): B = 1, L = T packed rows, plus the plan's buffers.
+// K splits of an fp32 prefill GEMM (64 x 64 tiles on the vector ALUs): enough for about one
+// workgroup per CU when the tiles are few, at least 64 K elements per split.
+int f32_prefill_splits(long long M, long long N, long long K) {
+  const long long tiles = ((M + 63) / 64) * ((N + 63) / 64);
+  long long sp = (256 + tiles - 1) / tiles;
+  if (sp > K / 64) sp = K / 64;
+  return sp < 1 ? 1 : (int)sp;
+}
+
 PrefillWs prefill_ws(const compass_layer_desc* d, long long B, long long L, long long n_seq = 0) {
   const Dims m = dims(d);
   const long long T = B * L;
@@ -195,7 +204,10 @@ PrefillWs prefill_ws(const compass_layer_desc* d, long long B, long long L, long
   w.vc = off; off += up(B * m.Hkv * L * m.hd * m.esz);
   w.a2 = off; off += up(T * m.K2 * m.esz);
   w.raw = off;
-  if (d->dtype == COMPASS_F32) off += up(T * (m.Nv > m.D ? m.Nv : m.D) * 4);
+  if (d->dtype == COMPASS_F32) {
+    const long long p1 = f32_prefill_splits(T, m.Nv, m.D) * m.Nv, p2 = f32_prefill_splits(T, m.D, m.K2) * m.D;
+    off += up(T * (p1 > p2 ? p1 : p2) * 4);
+  }
   else {
     const int so = gemm_bf16_resid_splits((int)T, (int)m.D, (int)m.K2);  // split-K output partials
     if (so > 1) off += up((long long)so * T * m.D * 4);
@@ -537,8 +549,9 @@ static int prefill_impl(const compass_layer_desc* d, const compass_layer_weights
     LAUNCH("gemm_proj", s, launch_gemm_bf16_proj(a, (int)m.D, (int)T, (int)m.D, pb, (int)m.Nv, ep, rt, s));
   } else {
     LAUNCH("layernorm", s, launch_layernorm(dt, x, w->ln_w, d->ln_eps, a, (int)T, (int)m.D, s));
-    LAUNCH("gemm_proj_f32", s, launch_gemm_f32_raw(a, (int)m.D, (int)T, (int)m.D, pb, (int)m.Nv, 1, raw, 1.f, s));
-    LAUNCH("proj_epilogue", s, launch_proj_epilogue(dt, raw, 1, (int)T, (int)m.Nv, ep, rt, s));
+    const int sp = f32_prefill_splits(T, m.Nv, m.D);
+    LAUNCH("gemm_proj_f32", s, launch_gemm_f32_raw(a, (int)m.D, (int)T, (int)m.D, pb, (int)m.Nv, sp, raw, 1.f, s));
+    LAUNCH("proj_epilogue", s, launch_proj_epilogue(dt, raw, sp, (int)T, (int)m.Nv, ep, rt, s));
   }
   if (va)
     LAUNCH("attn_prefill", s, launch_attention_prefill_varlen(dt, q, kc, vc, L, (int)m.Hq, (int)m.Hkv, cap,
@@ -557,8 +570,9 @@ static int prefill_impl(const compass_layer_desc* d, const compass_layer_weights
                                                    (int)m.D, rs, s));
     }
   } else {
-    LAUNCH("gemm_out_f32", s, launch_gemm_f32_raw(a2, (int)m.K2, (int)T, (int)m.K2, ob, (int)m.D, 1, raw, 1.f, s));
-    LAUNCH("splitk_resid", s, launch_splitk_resid(dt, raw, 1, (int)T, (int)m.D, x, out, rs, s));
+    const int so = f32_prefill_splits(T, m.D, m.K2);
+    LAUNCH("gemm_out_f32", s, launch_gemm_f32_raw(a2, (int)m.K2, (int)T, (int)m.K2, ob, (int)m.D, so, raw, 1.f, s));
+    LAUNCH("splitk_resid", s, launch_splitk_resid(dt, raw, so, (int)T, (int)m.D, x, out, rs, s));
   }
   if (n_ds > 0)
     LAUNCH("deepstack", s, launch_deepstack(dt, ds_rows, ds, n_ds, (int)m.D, (int)T, rs, out, s));
