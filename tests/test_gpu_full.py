@@ -196,6 +196,44 @@ def test_batched_decode_stack_full_size():
     print(f"decode stack: out {e:.2e}, attention rows per layer {[f'{v:.2e}' for v in worst]}")
 
 
+@pytest.mark.parametrize("kind", ["sliding", "full"])
+def test_decode_compass_widths_odd_batch(kind):
+    """One decode layer at the Compass widths with B = 37 rows (the decode GEMMs' 64-row tiles
+    hold 27 clamped rows) and ragged cache lengths 0 .. 1500 (window 1024 on the sliding
+    layer): every row against the oracle, the attention through the probe layer on its own
+    scale, and the new K/V rows."""
+    cfg = WORKLOADS["decode_stack"]
+    sh = dataclasses.replace(cfg["shape"], kind=kind, window=1024)
+    Bn, cap = 37, 1504
+    Hkv, hd = sh.n_kv_heads, sh.head_dim
+    rng = np.random.default_rng(37)
+    lens_np = np.sort(rng.integers(0, cap - 3, Bn)).astype(np.int32)
+    lens_np[0], lens_np[-1] = 0, cap - 4
+    delta = rng.integers(-50, 50, Bn).astype(np.int64)
+    pos_np = O.decode_positions(lens_np, delta).astype(np.int32)
+    w = W.make_layer_weights(sh, W.Stream.DECODE_STACK, 5)
+    x = W.make_layer_input(sh, W.Stream.DECODE_STACK, Bn, layer=5)
+    kc = RT.normal(stream_seed(W.Stream.DECODE_STACK, 5, W.TensorId.K_CACHE), Bn * Hkv * cap * hd).to(torch.bfloat16).view(Bn, Hkv, cap, hd)
+    vc = RT.normal(stream_seed(W.Stream.DECODE_STACK, 5, W.TensorId.V_CACHE), Bn * Hkv * cap * hd).to(torch.bfloat16).view(Bn, Hkv, cap, hd)
+    k_in, v_in = kc.float().cpu().numpy(), vc.float().cpu().numpy()
+    lens, pos = H.ints_to_dev(lens_np), H.ints_to_dev(pos_np)
+    xd = H.to_dev(x, torch.bfloat16)
+    probe = H.run_decode(sh, H.weights_to_dev(sh, probe_weights(sh, w)), xd, pos, kc.clone(), vc.clone(), lens)
+    out = H.run_decode(sh, H.weights_to_dev(sh, w), xd, pos, kc, vc, lens)
+    torch.cuda.synchronize()
+    sh_ref = dataclasses.replace(sh, kind=O.layer_kind(0 if kind == "sliding" else 3))
+    xin = H.np64(xd)
+    ref, knew, vnew = O.layer_decode(sh_ref, f64w(w), xin, pos_np, k_in, v_in, lens_np)
+    check_layer_out(sh, out, xin, ref, f"{kind} decode, B = 37")
+    ref_p, _, _ = O.layer_decode(sh_ref, f64w(probe_weights(sh, w)), xin, pos_np, k_in, v_in, lens_np)
+    e_att = check_attn_rows(sh, probe, xin, (ref_p - xin) / PROBE_SCALE, f"{kind} decode, B = 37")
+    kg, vg = H.np64(kc), H.np64(vc)
+    for i, n in enumerate(lens_np):
+        assert H.rel_err(kg[i, :, n], knew[i]) <= 2e-2, f"row {i} new K"
+        assert H.rel_err(vg[i, :, n], vnew[i]) <= 2e-2, f"row {i} new V"
+    print(f"{kind} decode at the Compass widths, B = 37: attention rows {e_att:.2e}")
+
+
 def test_stack_prefill_deepstack_logits_full_size():
     """4-layer [S, S, S, F] prefill, L = 4096, deepstack after layers 0-2, 256000-vocab logits x 0.0625:
     the whole stack output against oracle.stack_prefill; the logits of six rows over 7168 vocabulary
