@@ -277,6 +277,31 @@ def test_decode_reads_only_the_new_row_and_visible_keys(case):
         assert np.isnan(kg[i, :, n + 1:]).all() and np.isnan(vg[i, :, n + 1:]).all()
 
 
+@pytest.mark.parametrize("kind", ["sliding", "full"])
+def test_decode_more_rows_than_one_tile(kind):
+    """B = 70 bf16 rows: two 64-row tiles in the decode GEMMs (the projection's split-K tiles and
+    the output GEMM's general path, which takes over above 64 rows), ragged lens."""
+    sh = H.small_shape("bf16", kind, 128, 4, 1, 256, 512, 40 if kind == "sliding" else 0)
+    Bn, cap = 70, 300
+    rng = np.random.default_rng(70)
+    lens = rng.integers(0, cap - 1, Bn).astype(np.int32)
+    w, _, _ = layer_case(sh, 1, 8, seed=70)
+    x = H.rand_np(71, (Bn, sh.hidden), bf16=True)
+    kc = H.rand_np(72, (Bn, 1, cap, 128), bf16=True)
+    vc = H.rand_np(73, (Bn, 1, cap, 128), bf16=True)
+    pos = O.decode_positions(lens, rng.integers(-20, 20, Bn))
+    ref, knew, vnew = O.layer_decode(sh, w, x, pos, kc, vc, lens)
+    kd, vd = H.to_dev(kc, torch.bfloat16), H.to_dev(vc, torch.bfloat16)
+    out = H.run_decode(sh, H.weights_to_dev(sh, w), H.to_dev(x, torch.bfloat16), H.ints_to_dev(pos), kd, vd,
+                       H.ints_to_dev(lens))
+    torch.cuda.synchronize()
+    check_layer_out(sh, out, x.astype(np.float64), ref, f"{kind} decode, B = 70")
+    kg, vg = H.np64(kd), H.np64(vd)
+    for i, n in enumerate(lens):
+        assert H.rel_err(kg[i, :, n], knew[i]) <= H.tol(sh)
+        assert H.rel_err(vg[i, :, n], vnew[i]) <= H.tol(sh)
+
+
 def test_decode_skips_rows_with_lens_out_of_range():
     sh = H.small_shape("bf16", "sliding", 128, 4, 1, 256, 512, 40)
     lens = np.array([5, 64, 63], np.int32)  # capacity 64: row 1 is out of range
