@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams P) {
 
   int tm, tn;
   if (MODE == MODE_RAW) { tm = blockIdx.x % P.tiles_m; tn = blockIdx.x / P.tiles_m; }
-  else tile_coords<8>(P.tiles_m, P.tiles_n, tm, tn);
+  else tile_coords<MODE == MODE_PROJ ? 4 : 8>(P.tiles_m, P.tiles_n, tm, tn);  // row-tile groups: measured
   const int m0 = tm * BM, n0 = tn * BN;
 
   int kbeg = 0, kend = P.K;
