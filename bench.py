@@ -491,6 +491,49 @@ def copy_calibration(torch, nbytes=512 << 20, copies=3):
     return {"bytes_read": nbytes, "bytes_written": nbytes, "copies": copies}
 
 
+def achievable(torch, proj_shape):
+    """What the box itself delivers, measured in the same run, beside the published peaks: a
+    device-to-device copy of 1 GiB (read + write bytes over time) and the vendor bf16 GEMM
+    (torch.matmul, 2-D and contiguous) on 8192^3 and on the projection's own shape (no epilogue).
+    Each figure is the median of 10 timed calls after 3 warm-up calls."""
+    def med(fn, n=10):
+        for _ in range(3):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for e0, e1 in ev:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        t = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+        return t[n // 2] * 1e-3
+    nb = 1 << 30
+    src = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    copy_s = med(lambda: dst.copy_(src))
+    del src, dst
+    out = {"copy_read_write_TBps": 2 * nb / copy_s / 1e12}
+    # Both operand layouts (B as [K, N], and as [N, K] read through a transposed 2-D view, the
+    # layout of this library's weights); the faster one counts.
+    n = 8192
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    bm = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    t = min(med(lambda: torch.matmul(a, bm)), med(lambda: torch.matmul(a, bm.t())))
+    out["vendor_gemm_bf16_8192cube_TFLOPs"] = 2 * n ** 3 / t / 1e12
+    del a, bm
+    M, K, N = proj_shape
+    a = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+    w_kn = torch.randn(K, N, device="cuda").to(torch.bfloat16)
+    w_nk = w_kn.t().contiguous()
+    t = min(med(lambda: torch.matmul(a, w_kn)), med(lambda: torch.matmul(a, w_nk.t())))
+    out["vendor_gemm_bf16_projection_shape"] = {"M": M, "K": K, "N": N, "us": t * 1e6,
+                                                 "TFLOPs": 2 * M * K * N / t / 1e12}
+    del a, w_kn, w_nk
+    torch.cuda.empty_cache()
+    return out
+
+
 def proj_bytes(sh, L):
     """Algorithmic HBM bytes of one fused-projection launch: the normalized activations and
     the five weight matrices read once, q / k / v / SwiGLU output written once (bf16)."""
@@ -538,6 +581,10 @@ def main():
                          "flops_per_launch": proj, "mean_launch_us": gp["mean_us"],
                          "algorithmic_bytes": proj_bytes(sh, L)},
         }
+        Nv = (sh.n_q_heads + 2 * sh.n_kv_heads) * sh.head_dim + 2 * sh.intermediate
+        ach = achievable(torch, (L, sh.hidden, Nv))
+        line["roofline"]["measured_achievable"] = ach
+        line["roofline"]["frac_of_vendor_gemm_8192cube"] = achieved / ach["vendor_gemm_bf16_8192cube_TFLOPs"]
         if not args.no_cpu:
             log("sliding_prefill: timing the CPU oracle")
             line["cpu_baseline"] = cpu_baseline(sh, w, x, tok, grid, off)
