@@ -86,6 +86,10 @@ _sig = {
                                                     ctypes.c_size_t, _P]),
     "compass_layer_decode": (ctypes.c_int, [ctypes.POINTER(compass_layer_desc), ctypes.POINTER(compass_layer_weights),
                                             _I, _P, _P, ctypes.POINTER(compass_kv), _P, _P, ctypes.c_size_t, _P]),
+    "compass_layer_decode_chained": (ctypes.c_int, [ctypes.POINTER(compass_layer_desc),
+                                                    ctypes.POINTER(compass_layer_weights), _I, _P, _P, _P,
+                                                    ctypes.POINTER(compass_kv), _P, _P, ctypes.c_float, _P, _P,
+                                                    ctypes.c_size_t, _P]),
     "compass_layer_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(compass_layer_desc),
                                                     ctypes.POINTER(compass_layer_weights), _I, _P, _P,
                                                     ctypes.POINTER(compass_kv), _P, _P]),
@@ -231,6 +235,15 @@ def compass_layer_decode(desc, weights: compass_layer_weights, x, pos, kv: compa
     _check(_lib.compass_layer_decode(ctypes.byref(desc), ctypes.byref(weights), B, _ptr(x), _ptr(pos),
                                      ctypes.byref(kv), _ptr(out), _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def compass_layer_decode_chained(desc, weights: compass_layer_weights, x, x_norm, pos, kv: compass_kv, out,
+                                 next_ln_w, next_ln_eps: float, out_norm, workspace, stream=None) -> None:
+    B = x.shape[0]
+    _check(_lib.compass_layer_decode_chained(ctypes.byref(desc), ctypes.byref(weights), B, _ptr(x), _ptr(x_norm),
+                                             _ptr(pos), ctypes.byref(kv), _ptr(out), _ptr(next_ln_w),
+                                             float(next_ln_eps), _ptr(out_norm), _ptr(workspace),
+                                             workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 COMPASS_NOALLOC_SCRATCH_BYTES = 64 << 20

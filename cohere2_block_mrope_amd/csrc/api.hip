@@ -615,7 +615,8 @@ int compass_layer_prefill_varlen(const compass_layer_desc* d, const compass_laye
 static int decode_impl(const compass_layer_desc* d, const compass_layer_weights* w,
                        const compass_layer_weights_q4* wq, int32_t B, const void* x, const int32_t* pos,
                        const compass_kv* kv, void* out, void* workspace, size_t ws_bytes, void* stream,
-                       size_t* need = nullptr) {
+                       size_t* need = nullptr, const void* x_norm = nullptr, const void* next_ln_w = nullptr,
+                       float next_ln_eps = 0.f, void* out_norm = nullptr) {
   int rc = check_desc(d);
   if (rc) return rc;
   if (wq) {
@@ -639,6 +640,15 @@ static int decode_impl(const compass_layer_desc* d, const compass_layer_weights*
   if (kv->capacity < 1) return fail(COMPASS_E_INVALID, "kv capacity %d < 1", kv->capacity);
   if ((long long)B * m.Hkv * kv->capacity * m.hd > (1LL << 40))
     return fail(COMPASS_E_UNSUPPORTED, "kv cache too large");
+  if (x_norm || out_norm) {
+    if (d->dtype != COMPASS_BF16 || wq)
+      return fail(COMPASS_E_UNSUPPORTED, "LayerNorm outputs are handed between bf16 layers only");
+    if (out_norm && !next_ln_w) return fail(COMPASS_E_INVALID, "out_norm needs next_ln_w");
+    if (!aligned16(x_norm) || !aligned16(out_norm) || !aligned16(next_ln_w))
+      return fail(COMPASS_E_ALIGN, "x_norm / out_norm / next_ln_w not 16-byte aligned");
+    if (out_norm && (overlap(out_norm, xbytes, x, xbytes) || overlap(out_norm, xbytes, out, xbytes)))
+      return fail(COMPASS_E_INVALID, "out_norm overlaps x or out");
+  }
   const DecodeWs ws = decode_ws(d, B, kv->capacity);
   if (need) {
     *need = ws.total;
@@ -675,7 +685,10 @@ static int decode_impl(const compass_layer_desc* d, const compass_layer_weights*
   const RopeTable rt = rope_table(d);
 
   (void)hipGetLastError();
-  LAUNCH("layernorm", s, launch_layernorm(dt, x, wq ? wq->ln_w : w->ln_w, d->ln_eps, a, B, (int)m.D, s));
+  if (x_norm)
+    a = const_cast<void*>(x_norm);  // this layer's LayerNorm, written by the call that produced x
+  else
+    LAUNCH("layernorm", s, launch_layernorm(dt, x, wq ? wq->ln_w : w->ln_w, d->ln_eps, a, B, (int)m.D, s));
   // The output GEMM streams its weights through the skinny kernel when it applies (measured
   // faster there; the projection keeps the 64 x 64 split-K tiles).
   const bool skinny = !wq && ws.k2 > 0;
@@ -707,8 +720,12 @@ static int decode_impl(const compass_layer_desc* d, const compass_layer_weights*
   else
     LAUNCH("gemm_out_decode", s, launch_gemm_f32_raw(a2, (int)m.K2, B, (int)m.K2, out_bmap(d, w), (int)m.D, ws.s2,
                                                      raw2, 1.f, s));
-  LAUNCH("splitk_resid", s, launch_splitk_resid(dt, raw2, s2, B, (int)m.D, x, out,
-                                                RowStart{kv->lens, 1, kv->capacity}, s));
+  if (out_norm)
+    LAUNCH("splitk_resid", s, launch_splitk_resid_ln(raw2, s2, B, (int)m.D, x, out, RowStart{kv->lens, 1, kv->capacity},
+                                                     next_ln_w, next_ln_eps, out_norm, s));
+  else
+    LAUNCH("splitk_resid", s, launch_splitk_resid(dt, raw2, s2, B, (int)m.D, x, out,
+                                                  RowStart{kv->lens, 1, kv->capacity}, s));
   return ok();
 }
 
@@ -717,6 +734,15 @@ int compass_layer_decode(const compass_layer_desc* d, const compass_layer_weight
                          void* workspace, size_t ws_bytes, void* stream) {
   if (!w) return fail(COMPASS_E_INVALID, "weights struct is NULL");
   return decode_impl(d, w, nullptr, B, x, pos, kv, out, workspace, ws_bytes, stream);
+}
+
+int compass_layer_decode_chained(const compass_layer_desc* d, const compass_layer_weights* w, int32_t B,
+                                 const void* x, const void* x_norm, const int32_t* pos, const compass_kv* kv,
+                                 void* out, const void* next_ln_w, float next_ln_eps, void* out_norm,
+                                 void* workspace, size_t ws_bytes, void* stream) {
+  if (!w) return fail(COMPASS_E_INVALID, "weights struct is NULL");
+  return decode_impl(d, w, nullptr, B, x, pos, kv, out, workspace, ws_bytes, stream, nullptr, x_norm, next_ln_w,
+                     next_ln_eps, out_norm);
 }
 
 int compass_layer_decode_noalloc(const compass_layer_desc* d, const compass_layer_weights* w, int32_t B,

@@ -158,6 +158,98 @@ __global__ __launch_bounds__(256) void splitk_resid_kernel(const float* __restri
   for (int e = 0; e < 4; ++e) out[idx + e] = Elt<T>::from_f(Elt<T>::to_f(x[idx + e]) + acc[e]);
 }
 
+// The bf16 split-K residual of a decode layer fused with the next layer's LayerNorm. One
+// workgroup per row: each thread forms 8 columns of out = x + sum of the partials with the
+// additions of splitk_resid_kernel and keeps the bf16 results (as floats) in LDS; wave 0
+// takes the row's mean and biased variance in the LayerNorm kernel's own order (lane l sums
+// columns 8 (64 i + l) .. + 8 for i = 0, 1, ..., then the xor-shuffle reduction); every
+// thread then writes its 8 columns of (y - mean) * rstd * ln_w with the LayerNorm kernel's
+// expression and rounding, so norm is what that kernel would write for out. Rows that are
+// not live are left untouched.
+template <int SPL>
+__global__ __launch_bounds__(256) void splitk_resid_ln_kernel(const float* __restrict__ raw, int splits, int M,
+                                                              int N, const bf16_t* x, bf16_t* out, RowStart rs,
+                                                              const bf16_t* __restrict__ ln_w, float eps,
+                                                              bf16_t* __restrict__ norm) {
+  extern __shared__ float s_y[];  // [N], then (mean, rstd)
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  if (!row_live_m(rs, row)) return;
+  // The weight of this thread's first 8 columns is loaded with the partials, not after the
+  // statistics (one memory round trip fewer; N <= 2048 has no other columns).
+  u32x4_t w_first = {0u, 0u, 0u, 0u};
+  if (tid * 8 < N) w_first = *reinterpret_cast<const u32x4_t*>(ln_w + tid * 8);
+  const size_t sq = (size_t)M * N / 4;
+  for (int c = tid * 8; c < N; c += 256 * 8) {
+    const size_t idx = (size_t)row * N + c;
+    const f32x4_t* r = reinterpret_cast<const f32x4_t*>(raw + idx);
+    const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(x + idx);
+    const uint32_t x4[4] = {xv.x, xv.y, xv.z, xv.w};
+    uint32_t o4[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {  // two quads of columns
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (SPL > 0) {
+        f32x4_t v[SPL];
+#pragma unroll
+        for (int z = 0; z < SPL; ++z) v[z] = r[z * sq + h];
+        int z = 0;
+#pragma unroll
+        for (; z + 4 <= SPL; z += 4) acc += (v[z] + v[z + 1]) + (v[z + 2] + v[z + 3]);
+#pragma unroll
+        for (; z < SPL; ++z) acc += v[z];
+      } else {
+        int z = 0;
+        for (; z + 4 <= splits; z += 4)
+          acc += (r[z * sq + h] + r[(z + 1) * sq + h]) + (r[(z + 2) * sq + h] + r[(z + 3) * sq + h]);
+        for (; z < splits; ++z) acc += r[z * sq + h];
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t xw = x4[2 * h + j];
+        const bf16_t y0 = f2bf(__uint_as_float(xw << 16) + acc[2 * j]);
+        const bf16_t y1 = f2bf(__uint_as_float(xw & 0xffff0000u) + acc[2 * j + 1]);
+        o4[2 * h + j] = (uint32_t)y0 | ((uint32_t)y1 << 16);
+        s_y[c + 4 * h + 2 * j] = bf2f(y0);
+        s_y[c + 4 * h + 2 * j + 1] = bf2f(y1);
+      }
+    }
+    *reinterpret_cast<u32x4_t*>(out + idx) = u32x4_t{o4[0], o4[1], o4[2], o4[3]};
+  }
+  __syncthreads();
+  if (tid < 64) {
+    float sum = 0.f;
+    for (int e = lane * 8; e < N; e += 512)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sum += s_y[e + j];
+    const float mean = wave_sum(sum) / (float)N;
+    float q = 0.f;
+    for (int e = lane * 8; e < N; e += 512)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float d = s_y[e + j] - mean;
+        q += d * d;
+      }
+    const float var = wave_sum(q) / (float)N;
+    if (lane == 0) {
+      s_y[N] = mean;
+      s_y[N + 1] = 1.0f / sqrtf(var + eps);
+    }
+  }
+  __syncthreads();
+  const float mean = s_y[N], rstd = s_y[N + 1];
+  for (int c = tid * 8; c < N; c += 256 * 8) {
+    const u32x4_t wr = c == tid * 8 ? w_first : *reinterpret_cast<const u32x4_t*>(ln_w + c);
+    const uint32_t w4[4] = {wr.x, wr.y, wr.z, wr.w};
+    uint32_t o4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float w0 = __uint_as_float(w4[j] << 16), w1 = __uint_as_float(w4[j] & 0xffff0000u);
+      o4[j] = pack_bf2((s_y[c + 2 * j] - mean) * rstd * w0, (s_y[c + 2 * j + 1] - mean) * rstd * w1);
+    }
+    *reinterpret_cast<u32x4_t*>(norm + (size_t)row * N + c) = u32x4_t{o4[0], o4[1], o4[2], o4[3]};
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void deepstack_kernel(const int32_t* __restrict__ rows,
                                                         const T* __restrict__ ds, int D, int n_rows,
@@ -208,6 +300,30 @@ hipError_t launch_proj_epilogue(int dtype, const float* raw, int splits, int M, 
     else proj_epilogue_kernel<float, 0><<<grid, 256, 0, s>>>(raw, splits, M, N, ep, rt);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_splitk_resid_ln(const float* raw, int splits, int M, int N, const void* x, void* out,
+                                  const RowStart& rs_in, const void* ln_w, float eps, void* norm, hipStream_t s) {
+  if (N % 8 != 0) return hipErrorInvalidValue;
+  RowStart rs = rs_in;
+  if (rs.L < 1) rs.L = 1;
+  const size_t lds = (size_t)(N + 2) * sizeof(float);
+  auto go = [&](auto spl) -> hipError_t {
+    constexpr int SPL = decltype(spl)::value;
+    const hipError_t e = ensure_dynamic_lds((const void*)splitk_resid_ln_kernel<SPL>, (int)lds);
+    if (e != hipSuccess) return e;
+    splitk_resid_ln_kernel<SPL><<<M, 256, lds, s>>>(raw, splits, M, N, (const bf16_t*)x, (bf16_t*)out, rs,
+                                                   (const bf16_t*)ln_w, eps, (bf16_t*)norm);
+    return hipGetLastError();
+  };
+  switch (splits) {
+    case 1: return go(std::integral_constant<int, 1>{});
+    case 2: return go(std::integral_constant<int, 2>{});
+    case 4: return go(std::integral_constant<int, 4>{});
+    case 8: return go(std::integral_constant<int, 8>{});
+    case 16: return go(std::integral_constant<int, 16>{});
+    default: return go(std::integral_constant<int, 0>{});
+  }
 }
 
 hipError_t launch_splitk_resid(int dtype, const float* raw, int splits, int M, int N, const void* x,

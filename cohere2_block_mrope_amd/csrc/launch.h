@@ -214,6 +214,11 @@ hipError_t launch_proj_epilogue(int dtype, const float* raw, int splits, int M, 
                                 const ProjEpi& ep, const RopeTable& rt, hipStream_t s);
 // out[m, n] = x[m, n] + sum_z raw[z][m][n]; rows m of batch rows b = m / rs.L that are not
 // live (RowStart; decode passes lens with L = 1) are skipped.
+// bf16 split-K residual (as launch_splitk_resid) that also writes the next layer's LayerNorm
+// of each live output row, norm[m] = LayerNorm(out[m]; ln_w, eps) in bf16, with the values
+// the LayerNorm kernel gives. N % 8 == 0.
+hipError_t launch_splitk_resid_ln(const float* raw, int splits, int M, int N, const void* x, void* out,
+                                  const RowStart& rs, const void* ln_w, float eps, void* norm, hipStream_t s);
 hipError_t launch_splitk_resid(int dtype, const float* raw, int splits, int M, int N, const void* x,
                                void* out, const RowStart& rs, hipStream_t s);
 

@@ -237,6 +237,31 @@ int compass_layer_decode(const compass_layer_desc *d, const compass_layer_weight
                          int32_t B, const void *x, const int32_t *pos, const compass_kv *kv,
                          void *out, void *workspace, size_t ws_bytes, void *stream);
 
+/* compass_layer_decode for a stack of layers called one after another, with each layer's
+ * shared LayerNorm ("Text decoder forward" of the mlxcel Compass issue: LayerNorm of the
+ * layer input, weight only, in fp32) computed by the layer before it: the call that
+ * produces a layer's input also writes that input's LayerNorm, from its residual kernel,
+ * and the next call reads it instead of running its own LayerNorm kernel.
+ *   x_norm: NULL (the layer runs its LayerNorm kernel on x), or bf16 [B, D] holding
+ *     LayerNorm(x) with this layer's ln_w and ln_eps, as written to out_norm by the call
+ *     that produced x (given that call's next_ln_w = this layer's ln_w and next_ln_eps =
+ *     its ln_eps). Any other values give a different layer.
+ *   next_ln_w, next_ln_eps, out_norm: out_norm NULL, or bf16 [B, D] that receives
+ *     LayerNorm(out) with the weight next_ln_w (bf16 [D]) and eps next_ln_eps, equal bit
+ *     for bit to what the LayerNorm kernel computes from out; rows that are skipped (lens
+ *     out of range) are not written. next_ln_w is required with out_norm.
+ *   16-byte aligned device buffers; x_norm and out_norm may be the same buffer (x_norm is
+ *   read before out_norm is written, in stream order). Other arguments, the workspace
+ *   (compass_workspace_size(d, B, 1, kv->capacity, 1)), outputs and errors are those of
+ *   compass_layer_decode; the results equal a chain of compass_layer_decode calls bit for
+ *   bit. Needs d->dtype == COMPASS_BF16 when x_norm or out_norm is given (else
+ *   COMPASS_E_UNSUPPORTED). */
+int compass_layer_decode_chained(const compass_layer_desc *d, const compass_layer_weights *w,
+                                 int32_t B, const void *x, const void *x_norm, const int32_t *pos,
+                                 const compass_kv *kv, void *out, const void *next_ln_w,
+                                 float next_ln_eps, void *out_norm, void *workspace, size_t ws_bytes,
+                                 void *stream);
+
 /* Decode without allocation, for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. It is
  * compass_layer_decode (same arguments, kernels, outputs and errors) with the workspace

@@ -273,3 +273,33 @@ def test_noalloc_decode_checks_before_any_launch(b):
     with pytest.raises(b.CompassError) as e:
         b.compass_layer_decode_noalloc(d, weights(b), x, None, b.compass_kv(), FakePtr(0x300000), stream=0)
     assert e.value.code == b.COMPASS_E_INVALID
+
+
+def test_chained_decode_checks(b):
+    """LayerNorm outputs are handed between bf16 layers only, 16-byte aligned, never over x or
+    out, out_norm needs the next layer's weight, and the chained call validates like
+    compass_layer_decode (all rejected before any HIP call)."""
+    kv = b.compass_kv()
+    kv.k, kv.v, kv.capacity, kv.lens = 0x5000000, 0x6000000, 64, 0x7000000
+    x, pos, out, ws = FakePtr(0x100000, shape=(4, 2048)), FakePtr(0x200000), FakePtr(0x300000), FakePtr(0x400000)
+    nrm, lnw = FakePtr(0x800000), FakePtr(0x900000)
+    f32 = compass_shape(b, dtype=b.COMPASS_F32)
+    for d, xn, nw, on, code in [(f32, nrm, None, None, b.COMPASS_E_UNSUPPORTED),
+                                (f32, None, lnw, nrm, b.COMPASS_E_UNSUPPORTED),
+                                (compass_shape(b), None, None, nrm, b.COMPASS_E_INVALID),
+                                (compass_shape(b), FakePtr(0x800008), None, None, b.COMPASS_E_ALIGN),
+                                (compass_shape(b), None, lnw, FakePtr(0x800008), b.COMPASS_E_ALIGN),
+                                (compass_shape(b), None, FakePtr(0x900008), nrm, b.COMPASS_E_ALIGN),
+                                (compass_shape(b), None, lnw, FakePtr(0x100000 + 4096), b.COMPASS_E_INVALID),
+                                (compass_shape(b), None, lnw, FakePtr(0x300000 - 4096), b.COMPASS_E_INVALID)]:
+        with pytest.raises(b.CompassError) as e:
+            b.compass_layer_decode_chained(d, weights(b), x, xn, pos, kv, out, nw, 1e-5, on, ws, stream=0)
+        assert e.value.code == code, (xn, nw, on)
+    with pytest.raises(b.CompassError) as e:  # workspace too small
+        b.compass_layer_decode_chained(compass_shape(b), weights(b), x, nrm, pos, kv, out, lnw, 1e-5, nrm,
+                                       FakePtr(0x400000, n=64), stream=0)
+    assert e.value.code == b.COMPASS_E_WORKSPACE
+    with pytest.raises(b.CompassError) as e:  # no kv
+        b.compass_layer_decode_chained(compass_shape(b), weights(b), x, nrm, pos, b.compass_kv(), out, lnw, 1e-5,
+                                       nrm, ws, stream=0)
+    assert e.value.code == b.COMPASS_E_INVALID
