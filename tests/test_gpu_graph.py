@@ -120,3 +120,54 @@ def test_decode_step_graph_replays_match_eager(kind):
         torch.cuda.synchronize()
         assert torch.equal(out, ref_out), f"replay {r}: layer output"
         assert torch.equal(kc, ref_k) and torch.equal(vc, ref_v), f"replay {r}: K/V cache"
+
+
+def test_chained_decode_graph_replays_match_eager():
+    """Two chained decode layers (sliding, then full; the first hands the second its
+    LayerNorm) captured as one graph."""
+    shapes = [H.small_shape("bf16", k, 128, 4, 1, 256, 512, 16) for k in ("sliding", "full")]
+    Bn, cap = 3, 40
+    b = H.B()
+    wd = [H.weights_to_dev(sh, layer_case(sh, 1, 8, seed=21 + i)[0]) for i, sh in enumerate(shapes)]
+    wts = [b.make_weights(w) for w in wd]
+    ds = [H.desc(sh) for sh in shapes]
+    x = H.to_dev(H.rand_np(22, (Bn, shapes[0].hidden), bf16=True), torch.bfloat16)
+    lens_np = np.array([0, 17, 39], np.int32)
+    pos = H.ints_to_dev(O.decode_positions(lens_np, np.array([0, -3, 5])))
+    lens = H.ints_to_dev(lens_np)
+    caches = [(H.to_dev(H.rand_np(23 + 2 * i, (Bn, 1, cap, 128), bf16=True), torch.bfloat16),
+               H.to_dev(H.rand_np(24 + 2 * i, (Bn, 1, cap, 128), bf16=True), torch.bfloat16)) for i in range(2)]
+    cache0 = [(k.clone(), v.clone()) for k, v in caches]
+    kvs = [b.make_kv(k, v, lens) for k, v in caches]
+    h1, out, nrm = torch.empty_like(x), torch.empty_like(x), torch.empty_like(x)
+    ws = [H.workspace(b.compass_workspace_size(d, Bn, 1, cap, 1)) for d in ds]
+
+    def step():
+        b.compass_layer_decode_chained(ds[0], wts[0], x, None, pos, kvs[0], h1, wd[1]["ln_w"], shapes[1].ln_eps,
+                                       nrm, ws[0])
+        b.compass_layer_decode_chained(ds[1], wts[1], h1, nrm, pos, kvs[1], out, None, 0.0, None, ws[1])
+
+    step()
+    torch.cuda.synchronize()
+    ref_out = out.clone()
+    ref_caches = [(k.clone(), v.clone()) for k, v in caches]
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for r in range(REPLAYS):
+        out.zero_(); h1.zero_(); nrm.zero_()
+        for (k, v), (k0, v0) in zip(caches, cache0):
+            k.copy_(k0); v.copy_(v0)  # the appended rows are written again by the replay
+        _eager_noise()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out), f"replay {r}: output"
+        for i, ((k, v), (rk, rv)) in enumerate(zip(caches, ref_caches)):
+            assert torch.equal(k, rk) and torch.equal(v, rv), f"replay {r}: layer {i} K/V cache"
