@@ -74,12 +74,15 @@ def small_stack():
     return [base.with_kind(O.layer_kind(i)) for i in range(4)]
 
 
-def test_chained_decode_small_stack():
-    """Four layers [S, S, S, F] at small widths, B = 9 with ragged lengths (one row's length
-    outside the cache)."""
+@pytest.mark.parametrize("Bn", [9, 70])
+def test_chained_decode_small_stack(Bn):
+    """Four layers [S, S, S, F] at small widths with ragged lengths, the last row's length
+    outside the cache; B = 70 puts two 64-row tiles in the decode GEMMs (another split-K
+    count in the residual)."""
     shapes = small_stack()
-    lens_np = np.array([0, 1, 39, 40, 41, 255, 256, 300, 301], np.int32)
-    Bn, cap = len(lens_np), 301  # the last row is skipped
+    cap = 301
+    base = np.array([0, 1, 39, 40, 41, 255, 256, 300], np.int32)
+    lens_np = np.concatenate([np.resize(base, Bn - 1), [cap]]).astype(np.int32)  # the last row is skipped
     live = lens_np < cap
     ws_np = [layer_case(sh, 1, 8, seed=40 + i)[0] for i, sh in enumerate(shapes)]
     x = H.rand_np(50, (Bn, shapes[0].hidden), bf16=True)
