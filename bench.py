@@ -179,12 +179,13 @@ def run_decode_stack(args, b, H, W, torch):
     # kernel. The same step as independent compass_layer_decode calls is timed beside it.
     nrm = torch.empty_like(x)
 
-    def decode_layers():
+    def decode_layers(final_w=None):
+        """The chained layers; with final_w the last layer also hands over the final LayerNorm."""
         last = len(layers) - 1
         for i, (d, wts, _, kc, vc, ws) in enumerate(layers):
-            nxt = None if i == last else layers[i + 1][2]["ln_w"]
+            nxt = final_w if i == last else layers[i + 1][2]["ln_w"]
             b.compass_layer_decode_chained(d, wts, h, None if i == 0 else nrm, pos, b.make_kv(kc, vc, lens), h,
-                                           nxt, sh.ln_eps, None if i == last else nrm, ws)
+                                           nxt, sh.ln_eps, None if nxt is None else nrm, ws)
 
     def step():
         h.copy_(x)
@@ -212,8 +213,8 @@ def run_decode_stack(args, b, H, W, torch):
     def greedy_step():
         b.compass_embed(tok, E, None, None, h, est, 1)
         b.compass_decode_positions(lens, delta, 0, pos)
-        decode_layers()
-        b.compass_logits_argmax(h, nw, sh.ln_eps, E, WORKLOADS["stack_logits"]["logit_scale"], tok, None, gws, 1)
+        decode_layers(final_w=nw)  # the greedy head takes the final LayerNorm from the last layer
+        b.compass_logits_argmax(nrm, None, sh.ln_eps, E, WORKLOADS["stack_logits"]["logit_scale"], tok, None, gws, 1)
 
     sec_g, stats_g = timed(greedy_step, max(5, args.steps), 3, b, torch)
     assert int(est.item()) == 0
@@ -264,7 +265,8 @@ def run_decode_stack(args, b, H, W, torch):
             res["q4_step"][name + "_weight_hbm_frac"] = nbytes / (st["mean_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS
     lg = stats_g.get("gemm_logits_argmax", {})
     res["greedy_step"] = {"us_per_step": 1e6 * sec_g,
-                          "what": "embed + decode positions + the 4 layers + tied 256000-vocab logits argmax",
+                          "what": "embed + decode positions + the 4 chained layers (the last one writing the "
+                                  "final LayerNorm) + tied 256000-vocab logits argmax",
                           "kernels_us": {k: round(v["mean_us"], 1) for k, v in stats_g.items()
                                          if k in ("embed", "decode_positions", "logits_layernorm",
                                                   "gemm_logits_argmax", "argmax")}}

@@ -865,37 +865,47 @@ int compass_logits_argmax(int32_t R, int32_t D, int32_t V, int32_t dtype, const 
     return fail(COMPASS_E_ALIGN, "rows of h not 16-byte aligned (ldh=%lld)", (long long)ldh);
   if (R > 65535 || (long long)R * V > (1LL << 40) || (long long)V * D > (1LL << 31) - 1)
     return fail(COMPASS_E_UNSUPPORTED, "R > 65535, or R*V or V*D too large");
-  if (!h || !norm_w || !embed || !token) return fail(COMPASS_E_INVALID, "NULL pointer argument");
+  if (!h || !embed || !token) return fail(COMPASS_E_INVALID, "NULL pointer argument");
   if (!aligned16(h) || !aligned16(norm_w) || !aligned16(embed))
     return fail(COMPASS_E_ALIGN, "tensor not 16-byte aligned");
-  if (!(ln_eps >= 0.f) || !isfinite(ln_eps)) return fail(COMPASS_E_INVALID, "ln_eps must be finite and >= 0");
+  if (norm_w && (!(ln_eps >= 0.f) || !isfinite(ln_eps)))
+    return fail(COMPASS_E_INVALID, "ln_eps must be finite and >= 0");
+  if (!norm_w && (long long)R * ldh > (1LL << 31) - 1)  // the GEMM then reads h itself (32-bit offsets)
+    return fail(COMPASS_E_UNSUPPORTED, "normalized rows: R * ldh above 2^31 - 1");
   const size_t need = compass_logits_argmax_workspace_size(R, D, V, dtype);
   if (!workspace || ws_bytes < need)
     return fail(COMPASS_E_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
   if (((uintptr_t)workspace & (kAlign - 1)) != 0) return fail(COMPASS_E_ALIGN, "workspace not 256-byte aligned");
   const hipStream_t s = (hipStream_t)stream;
-  void* a = workspace;
+  const void* a = workspace;
+  int lda = D;
   BMap eb{};
   eb.kind = 0;
   eb.p[0] = embed;
   eb.ld0 = D;
   (void)hipGetLastError();
   // Same LayerNorm and logits arithmetic as compass_logits (the maxima are bitwise those
-  // of the logits it returns for the same rows).
-  LAUNCH("logits_layernorm", s, launch_layernorm(dtype, h, norm_w, ln_eps, a, R, D, s, (long long)ldh));
+  // of the logits it returns for the same rows). Without norm_w the rows of h are the
+  // normalized rows already.
+  if (norm_w)
+    LAUNCH("logits_layernorm", s, launch_layernorm(dtype, h, norm_w, ln_eps, workspace, R, D, s, (long long)ldh));
+  else {
+    a = h;
+    lda = (int)ldh;
+  }
   if (dtype == COMPASS_BF16) {
     // The argmax is fused into the logits GEMM: only per-span partials reach memory.
     float* pv = (float*)((char*)workspace + up((size_t)R * D * 2));
     int* pi = (int*)((char*)pv + up((size_t)R * argmax_parts_bf16(V) * 4));
     int parts = 0;
     hipError_t ge = hipSuccess;
-    LAUNCH("gemm_logits_argmax", s, (parts = gemm_bf16_argmax(a, D, R, D, eb, V, logit_scale, pv, pi, s, &ge), ge));
+    LAUNCH("gemm_logits_argmax", s, (parts = gemm_bf16_argmax(a, lda, R, D, eb, V, logit_scale, pv, pi, s, &ge), ge));
     LAUNCH("argmax", s, launch_argmax_partials(pv, pi, R, parts, token, max_logit, s));
   } else {
     float* lg = (float*)((char*)workspace + up((size_t)R * D * 4));
     float* pv = (float*)((char*)lg + up((size_t)R * V * 4));
     int* pi = (int*)((char*)pv + up((size_t)R * argmax_chunks(V) * 4));
-    LAUNCH("gemm_logits", s, launch_gemm_f32_raw(a, D, R, D, eb, V, 1, lg, logit_scale, s));
+    LAUNCH("gemm_logits", s, launch_gemm_f32_raw(a, lda, R, D, eb, V, 1, lg, logit_scale, s));
     LAUNCH("argmax", s, launch_argmax(lg, R, V, (long long)V, 1.f, pv, pi, token, max_logit, s));
   }
   return ok();

@@ -351,6 +351,10 @@ int compass_decode_positions(int32_t B, int32_t *lens, const int32_t *rope_delta
  *   with h pointing at row L - 1 picks the last token of every [L, D] batch row);
  *   ldh * element size must be a multiple of 16.   token out [R] int32 (device).
  *   R <= 65535. A NaN logit is never picked (a row of NaN / -inf logits gives id 0).
+ *   norm_w NULL: the rows of h are already normalized (for instance the out_norm of a
+ *   compass_layer_decode_chained call given the final norm weight as next_ln_w, which
+ *   equals this call's own LayerNorm bit for bit); ln_eps is unused and R * ldh must stay
+ *   below 2^31.
  *   workspace: compass_logits_argmax_workspace_size(R, D, V, dtype) bytes, 256-byte
  *   aligned. Other arguments and errors as compass_logits. */
 size_t compass_logits_argmax_workspace_size(int32_t R, int32_t D, int32_t V, int32_t dtype);

@@ -226,6 +226,9 @@ def test_front_end_argument_errors(b):
     assert am(dt=3) == b.COMPASS_E_UNSUPPORTED
     assert "ldh" in (am(ldh=1000) and b.compass_last_error())
     assert am(R=70000, n=1 << 40) == b.COMPASS_E_UNSUPPORTED  # R above the grid limit
+    # pre-normalized rows (norm_w NULL): the GEMM reads h with 32-bit offsets
+    assert am(nw=None, ldh=1 << 29) == b.COMPASS_E_UNSUPPORTED
+    assert am(nw=None, h=None) == b.COMPASS_E_INVALID
 
 
 def test_q4_decode_argument_errors(b):

@@ -155,3 +155,33 @@ def test_chained_decode_compass_widths():
         w64 = {k: np.asarray(v, np.float64) for k, v in ws_np[i].items()}
         ref, _, _ = O.layer_decode(shapes[i], w64, x64, pos_np, cache_in[i][0], cache_in[i][1], lens_np, rows=rows)
         check_layer_out(shapes[i], ob[rows], x64[rows], ref, f"chained Compass layer {i}")
+
+
+def test_chained_decode_into_the_greedy_head():
+    """The last layer hands over the final LayerNorm (next_ln_w = the final norm weight) and
+    the greedy head takes those rows with norm_w NULL: the same tokens and maxima, bit for
+    bit, as the head normalizing the layer output itself."""
+    sh = small_stack()[3]
+    Bn, cap, V = 9, 301, 777
+    lens_np = np.array([0, 1, 39, 40, 41, 255, 256, 299, 300], np.int32)
+    w = layer_case(sh, 1, 8, seed=90)[0]
+    wdev = H.weights_to_dev(sh, w)
+    x = H.to_dev(H.rand_np(91, (Bn, sh.hidden), bf16=True), torch.bfloat16)
+    pos = H.ints_to_dev(O.decode_positions(lens_np, np.zeros(Bn, np.int64)))
+    kc = H.to_dev(H.rand_np(92, (Bn, 1, cap, 128), bf16=True), torch.bfloat16)
+    vc = H.to_dev(H.rand_np(93, (Bn, 1, cap, 128), bf16=True), torch.bfloat16)
+    fnw = H.to_dev(H.rand_np(94, (sh.hidden,), std=0.1, mean=1.0), torch.bfloat16)
+    E = H.to_dev(H.rand_np(95, (V, sh.hidden), std=0.5), torch.bfloat16)
+    norm = torch.empty_like(x)
+    out = run_chained(sh, wdev, x, None, pos, kc, vc, H.ints_to_dev(lens_np), fnw, sh.ln_eps, norm)
+    b = H.B()
+    ws = H.workspace(b.compass_logits_argmax_workspace_size(Bn, sh.hidden, V, 1))
+    res = []
+    for h, nw in ((out, fnw), (norm, None)):
+        tok = torch.full((Bn,), -1, dtype=torch.int32, device="cuda")
+        mx = torch.empty((Bn,), dtype=torch.float32, device="cuda")
+        b.compass_logits_argmax(h, nw, sh.ln_eps, E, 0.25, tok, mx, ws, 1)
+        torch.cuda.synchronize()
+        res.append((tok.clone(), mx.clone()))
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+    assert int(res[1][0].min()) >= 0
