@@ -2,6 +2,7 @@
 
 * one-token prefill (B = 1 and B = 3, sliding and full, bf16 and fp32) and two-token rows;
 * decode over an empty cache (the new token attends only to itself) and a single row;
+* decode with a window of one or two keys, one row writing the cache's last slot;
 * the one-row, one-word logits head and a three-word vocabulary;
 * position ids of a row that is a single image (no text at all) and of the longest row
   the library accepts (COMPASS_MAX_TOKENS_PER_ROW tokens, images spread over it), bit-exact
@@ -54,6 +55,32 @@ def test_decode_over_empty_cache_and_single_row(dt, kind):
                            H.to_dev(vc, td), H.ints_to_dev(lens))
         torch.cuda.synchronize()
         check_layer_out(sh, out, x, ref, f"decode lens={lens.tolist()}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("win", [1, 2])
+def test_decode_window_of_one_or_two_keys_and_last_cache_slot(dt, win):
+    """A sliding decode layer whose window holds only the new key (or it and one more), with
+    one row writing the cache's last slot (lens = capacity - 1)."""
+    sh = H.small_shape(dt, "sliding", 128, 4, 1, 256, 512, win)
+    bf = dt == "bf16"
+    w, _, _ = layer_case(sh, 1, 8, seed=47 + win)
+    lens = np.array([0, 1, 2, 37, 299], np.int32)
+    Bn, cap = len(lens), 300
+    x = H.rand_np(48, (Bn, sh.hidden), bf16=bf)
+    kc = H.rand_np(49, (Bn, 1, cap, 128), bf16=bf)
+    vc = H.rand_np(50, (Bn, 1, cap, 128), bf16=bf)
+    pos = O.decode_positions(lens, np.array([0, 3, -2, 10, -100], np.int64))
+    ref, knew, vnew = O.layer_decode(sh, w, x, pos, kc, vc, lens)
+    td = H.tdtype(sh)
+    kd, vd = H.to_dev(kc, td), H.to_dev(vc, td)
+    out = H.run_decode(sh, H.weights_to_dev(sh, w), H.to_dev(x, td), H.ints_to_dev(pos), kd, vd,
+                       H.ints_to_dev(lens))
+    torch.cuda.synchronize()
+    check_layer_out(sh, out, x, ref, f"decode window {win}")
+    kg = H.np64(kd)
+    for i, n in enumerate(lens):
+        assert H.rel_err(kg[i, :, n], knew[i]) <= H.tol(sh), f"row {i} new K"
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
